@@ -1,0 +1,254 @@
+"""ctypes wrapper around the plain CPU oracle ``libcsa2ref.so``.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.  Arrays are host
+numpy arrays; bf16 data is passed as its uint16 bit pattern, FP8 / NVFP4 data
+as uint8 codes.  Results in floating point are float64.
+
+The step functions mirror the hot path (NVFP4 article sections 3-3.4):
+compress (2:1 softmax-gated pooling), scan (indexer score of every visible
+latent and the per-block maximum), select (top-k by score, ties to the
+smaller id, an optional forced id), cand (indexer over the latents of the
+chosen blocks), attn (64-head attention over the selected latents plus the
+raw window, with a per-head sink).  ``decode`` chains them per the method.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libcsa2ref.so")
+
+BF16, E4M3, NVFP4, F32 = 1, 2, 3, 4
+D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
+_FMT = {"bf16": BF16, "fp8": E4M3, "nvfp4": NVFP4, "f32": F32}
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from oracle import build as _b
+            _b.build()
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, I64, D_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.csa2ref_bf16.restype = D_
+        L.csa2ref_bf16.argtypes = [ctypes.c_uint16]
+        L.csa2ref_e4m3.restype = D_
+        L.csa2ref_e4m3.argtypes = [ctypes.c_uint8]
+        L.csa2ref_e2m1.restype = D_
+        L.csa2ref_e2m1.argtypes = [ctypes.c_uint8]
+        L.csa2ref_round_bf16.restype = ctypes.c_uint16
+        L.csa2ref_round_bf16.argtypes = [D_]
+        L.csa2ref_n_vis.restype = I64
+        L.csa2ref_n_vis.argtypes = [I64, I64]
+        L.csa2ref_newest_block.restype = I64
+        L.csa2ref_newest_block.argtypes = [I64, I64]
+        L.csa2ref_compress.restype = None
+        L.csa2ref_compress.argtypes = [I, I, P, I64, P, I64, P, I64, P]
+        L.csa2ref_scan.restype = None
+        L.csa2ref_scan.argtypes = [I, I, P, P, P, I, I64, I64, P, P, I64, P, I64]
+        L.csa2ref_select.restype = None
+        L.csa2ref_select.argtypes = [I, I64, P, I64, P, I64, P, I, P, I64]
+        L.csa2ref_cand.restype = None
+        L.csa2ref_cand.argtypes = [I, I, P, P, P, I, I64, I64, P, P, I, P, P, I64]
+        L.csa2ref_attn.restype = None
+        L.csa2ref_attn.argtypes = [I, I, P, I64, P, I, P, I64, I64, P, I, I64, P, I, P,
+                                   I, I, I64, P, P, D_, P, P]
+        L.csa2ref_dequant_fp8.restype = None
+        L.csa2ref_dequant_fp8.argtypes = [P, P, I64, I, P]
+        L.csa2ref_dequant_nvfp4.restype = None
+        L.csa2ref_dequant_nvfp4.argtypes = [P, P, I64, I, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.dtype(dtype), (a.dtype, dtype)
+    return a
+
+
+def _key_fmt(k):
+    return BF16 if k.dtype == np.uint16 else E4M3
+
+
+# ---------------------------------------------------------------- decoders
+def bf16(bits) -> float:
+    return lib().csa2ref_bf16(int(bits))
+
+
+def e4m3(bits) -> float:
+    return lib().csa2ref_e4m3(int(bits))
+
+
+def e2m1(nibble) -> float:
+    return lib().csa2ref_e2m1(int(nibble))
+
+
+def round_bf16(x) -> int:
+    return lib().csa2ref_round_bf16(float(x))
+
+
+def bf16_array(bits: np.ndarray) -> np.ndarray:
+    """Decode a uint16 bf16 array to float64 (via the oracle's decoder)."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16)
+    flat = u.reshape(-1)
+    tab = np.array([bf16(i) for i in range(65536)], dtype=np.float64)
+    return tab[flat].reshape(u.shape)
+
+
+def n_vis(t, n_cache) -> int:
+    return lib().csa2ref_n_vis(int(t), int(n_cache))
+
+
+def newest_block(t, n_cache) -> int:
+    return lib().csa2ref_newest_block(int(t), int(n_cache))
+
+
+# ------------------------------------------------------------------ steps
+def compress(raw: np.ndarray, gate: np.ndarray):
+    """raw, gate: uint16 bf16 [B][T][512] -> (bf16 bits [B][T/2][512], float64)."""
+    raw, gate = _c(raw, np.uint16), _c(gate, np.uint16)
+    B, T, _ = raw.shape
+    out = np.zeros((B, T // 2, D), np.uint16)
+    out64 = np.zeros((B, T // 2, D), np.float64)
+    lib().csa2ref_compress(B, T, _p(raw), T * D, _p(gate), T * D, _p(out), (T // 2) * D, _p(out64))
+    return out, out64
+
+
+def scan(q, w, k, q_pos, want_scores=False):
+    """Indexer scores of every visible latent and per-block maxima.
+
+    q uint16 [B][Tq][32][128]; w f32 [B][Tq][32]; k [B][N][128] (uint16 bf16 or
+    uint8 E4M3); q_pos int64 [B][Tq].  Returns (scores [B*Tq][N] or None,
+    block_max [B*Tq][ceil(N/8)]), float64 with -inf where invisible."""
+    q, w, q_pos = _c(q, np.uint16), _c(w, np.float32), _c(q_pos, np.int64)
+    k = np.ascontiguousarray(k)
+    B, Tq = q.shape[:2]
+    N = k.shape[1]
+    nblk = (N + BLK - 1) // BLK
+    sc = np.zeros((B * Tq, N), np.float64) if want_scores else None
+    bm = np.zeros((B * Tq, nblk), np.float64)
+    lib().csa2ref_scan(B, Tq, _p(q), _p(w), _p(k), _key_fmt(k), N * DI, N, _p(q_pos),
+                       _p(sc), N, _p(bm), nblk)
+    return sc, bm
+
+
+def select(scores, k, ids=None, forced=None):
+    """Top-k per row by (score desc, id asc); ascending ids padded with -1."""
+    scores = _c(scores, np.float64)
+    R, n = scores.shape
+    ids = _c(ids, np.int32)
+    forced = _c(forced, np.int32)
+    out = np.zeros((R, k), np.int32)
+    lib().csa2ref_select(R, n, _p(scores), n, _p(ids), n, _p(forced), k, _p(out), k)
+    return out
+
+
+def cand(q, w, k, q_pos, blocks):
+    """Indexer scores over the latents of the chosen blocks.
+
+    blocks int32 [B*Tq][K_b]; returns (scores float64 [B*Tq][8*K_b],
+    ids int32 [B*Tq][8*K_b]) with id -1 / score -inf for absent latents."""
+    q, w, q_pos, blocks = _c(q, np.uint16), _c(w, np.float32), _c(q_pos, np.int64), _c(blocks, np.int32)
+    k = np.ascontiguousarray(k)
+    B, Tq = q.shape[:2]
+    N = k.shape[1]
+    K_b = blocks.shape[1]
+    sc = np.zeros((B * Tq, K_b * BLK), np.float64)
+    ids = np.zeros((B * Tq, K_b * BLK), np.int32)
+    lib().csa2ref_cand(B, Tq, _p(q), _p(w), _p(k), _key_fmt(k), N * DI, N, _p(q_pos),
+                       _p(blocks), K_b, _p(sc), _p(ids), K_b * BLK)
+    return sc, ids
+
+
+def attn(q, lat, sel, win, q_pos, sink, W, scale, lat_scale=None, win_scale=None):
+    """Sparse attention over Sel + window with sinks.
+
+    q uint16 [B][Tq][64][512]; lat uint16 [B][N][512] (bf16) or uint8
+    [B][N][256] (NVFP4, with lat_scale uint8 [B][N][32]); sel int32
+    [B*Tq][K]; win uint16 [B][W_cap][512] (bf16) or uint8 (E4M3, with
+    win_scale f32 [B][W_cap]); q_pos int64 [B][Tq]; sink f32 [64].
+    Returns (out float64 [B*Tq][64][512], lse float64 [B*Tq][64])."""
+    q, sel, q_pos, sink = _c(q, np.uint16), _c(sel, np.int32), _c(q_pos, np.int64), _c(sink, np.float32)
+    lat, win = np.ascontiguousarray(lat), np.ascontiguousarray(win)
+    B, Tq = q.shape[:2]
+    N = lat.shape[1]
+    W_cap = win.shape[1]
+    K = sel.shape[1]
+    lat_fmt = BF16 if lat.dtype == np.uint16 else NVFP4
+    win_fmt = BF16 if win.dtype == np.uint16 else E4M3
+    lat_scale = _c(lat_scale, np.uint8)
+    win_scale = _c(win_scale, np.float32)
+    out = np.zeros((B * Tq, HQ, D), np.float64)
+    lse = np.zeros((B * Tq, HQ), np.float64)
+    lib().csa2ref_attn(B, Tq, _p(q), Tq * HQ * D, _p(lat), lat_fmt, _p(lat_scale), N, N,
+                       _p(sel), K, K, _p(win), win_fmt, _p(win_scale), W, W_cap, W_cap,
+                       _p(q_pos), _p(sink), float(scale), _p(out), _p(lse))
+    return out, lse
+
+
+def dequant_fp8(src, row_scale=None):
+    src = _c(src, np.uint8)
+    rows, cols = src.shape
+    row_scale = _c(row_scale, np.float32)
+    dst = np.zeros((rows, cols), np.float64)
+    lib().csa2ref_dequant_fp8(_p(src), _p(row_scale), rows, cols, _p(dst))
+    return dst
+
+
+def dequant_nvfp4(packed, scales):
+    packed, scales = _c(packed, np.uint8), _c(scales, np.uint8)
+    rows = packed.shape[0]
+    cols = packed.shape[1] * 2
+    dst = np.zeros((rows, cols), np.float64)
+    lib().csa2ref_dequant_nvfp4(_p(packed), _p(scales), rows, cols, _p(dst))
+    return dst
+
+
+# --------------------------------------------------------------- pipeline
+def decode(inp: dict, K_b: int, K: int, W: int, scale: float, compress_first=False):
+    """Run the whole hot path on host arrays, step by step as the method
+    states it (NVFP4 article section 3 call tree):
+      [compressor] -> candidate-source scan + block max -> block top-K_b with
+      the newest block kept -> current indexer over the candidates ->
+      position top-K -> attention over Sel + window with sinks.
+
+    ``inp`` holds numpy arrays keyed as the input generator names them
+    (q, sink, qs, ws, ks, qi, wi, ki, lat, lat_scale, win, win_scale, q_pos,
+    raw, gate) plus ``comp_pos0`` when ``compress_first``.  Returns a dict
+    of every intermediate."""
+    res = {}
+    lat = inp["lat"]
+    if compress_first:
+        comp_bits, comp64 = compress(inp["raw"], inp["gate"])
+        g0 = inp["comp_pos0"] // 2
+        lat = lat.copy()
+        lat[:, g0:g0 + comp_bits.shape[1]] = comp_bits
+        res["comp"], res["comp64"] = comp_bits, comp64
+    res["lat"] = lat
+    q_pos = inp["q_pos"]
+    B, Tq = q_pos.shape
+    N = lat.shape[1]
+    _, bm = scan(inp["qs"], inp["ws"], inp["ks"], q_pos)
+    forced = np.array([newest_block(t, N) for t in q_pos.reshape(-1)], np.int32)
+    blocks = select(bm, K_b, forced=forced)
+    csc, cid = cand(inp["qi"], inp["wi"], inp["ki"], q_pos, blocks)
+    sel = select(csc, K, ids=cid)
+    out, lse = attn(inp["q"], lat, sel, inp["win"], q_pos, inp["sink"], W, scale,
+                    lat_scale=inp.get("lat_scale"), win_scale=inp.get("win_scale"))
+    res.update(block_max=bm, forced=forced, blocks=blocks, cand_scores=csc,
+               cand_ids=cid, sel=sel, out=out, lse=lse)
+    return res

@@ -1,0 +1,216 @@
+"""Pins for the whole oracle path against the dense brute force and against
+the method's invariants (NVFP4 article sections 3-3.4):
+
+* every query attends to exactly 128 + 512 = 640 rows once the context is
+  long enough; fewer only when fewer exist;
+* the newest block is always among the chosen blocks;
+* with one shared indexer, the two-stage selection equals a flat top-K over
+  all visible latents whenever K <= K_b - 1 (every block holding a flat
+  top-K latent outranks every block holding none);
+* the attention's closed-form special cases (sink limits, one row, equal
+  rows, order of Sel).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from compressed_sparse_attention_03_amd import gen
+from oracle import brute
+from oracle import csa2_ref as ref
+from tests.helpers import np_inputs
+
+
+def _run_both(cfg, compress_first=False, q_pos=None, inp_edit=None):
+    inp = np_inputs(gen.make_inputs(cfg))
+    if q_pos is not None:
+        inp["q_pos"] = np.asarray(q_pos, np.int64).reshape(cfg.B, cfg.Tq)
+    if inp_edit:
+        inp_edit(inp)
+    res = ref.decode(inp, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=compress_first)
+    inp_b = dict(inp, lat=res["lat"])
+    rows = [brute.decode_row(inp_b, r, cfg.K_b, cfg.K, cfg.W, cfg.scale) for r in range(cfg.R)]
+    return inp, res, rows
+
+
+def _compare(cfg, res, rows):
+    for r, br in enumerate(rows):
+        nb = len(br["block_max"])
+        assert np.array_equal(res["block_max"][r, :nb], br["block_max"])
+        assert np.all(res["block_max"][r, nb:] == -np.inf)
+        got_blocks = res["blocks"][r][res["blocks"][r] >= 0]
+        assert np.array_equal(got_blocks, br["blocks"]), r
+        got_sel = res["sel"][r][res["sel"][r] >= 0]
+        assert np.array_equal(got_sel, br["sel"]), r
+        np.testing.assert_allclose(res["out"][r], br["out"], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][r], br["lse"], rtol=1e-12, atol=1e-12)
+
+
+def test_tiny_config_chained_matches_brute():
+    cfg = gen.CONFIGS["tiny"]
+    inp, res, rows = _run_both(cfg, compress_first=True)
+    _compare(cfg, res, rows)
+    # the compressed rows really replaced the cache
+    comp, _ = ref.compress(inp["raw"], inp["gate"])
+    assert np.array_equal(res["lat"][:, :2048], comp)
+    # t = 4092..4095 see 2046, 2047, 2047, 2048 latents; 64 blocks x 8 = 512
+    # candidates at most, so the position stage keeps them all
+    nsel = (res["sel"] >= 0).sum(axis=1)
+    assert list(nsel) == [510, 511, 511, 512]
+    assert [r["n_rows"] for r in rows] == [638, 639, 639, 640]
+
+
+def test_tiny_config_small_k_matches_brute():
+    cfg = gen.shrink(gen.CONFIGS["tiny"], K_b=16, K=64, seed=21)
+    _, res, rows = _run_both(cfg)
+    _compare(cfg, res, rows)
+    assert np.all((res["sel"] >= 0).sum(axis=1) == 64)
+
+
+def test_shared_indexer_equals_flat_topk():
+    cfg = gen.shrink(gen.CONFIGS["tiny"], K_b=16, K=15, shared_indexer=True, seed=22)
+    inp, res, rows = _run_both(cfg)
+    _compare(cfg, res, rows)
+    for r in range(cfg.R):
+        t = int(inp["q_pos"].reshape(-1)[r])
+        nv = ref.n_vis(t, cfg.N)
+        s = brute.index_scores(inp["qs"].reshape(-1, 32, 128)[r], inp["ws"].reshape(-1, 32)[r], inp["ks"][0])[:nv]
+        flat = np.sort(brute.topk_ids(s, np.arange(nv), cfg.K))
+        assert np.array_equal(res["sel"][r], flat)
+
+
+def test_short_contexts():
+    cfg = gen.shrink(gen.CONFIGS["tiny"], Tq=6, K_b=4, K=16, seed=23)
+    q_pos = [0, 1, 2, 15, 40, 300]
+    inp, res, rows = _run_both(cfg, q_pos=q_pos)
+    _compare(cfg, res, rows)
+    # t = 0: no latent exists yet -> window only (one row) + sink
+    assert np.all(res["sel"][0] == -1) and rows[0]["n_rows"] == 1
+    # t = 1: latent 0 exists, block 0 is the newest
+    assert list(res["blocks"][1][:1]) == [0] and rows[1]["n_rows"] == 1 + 2
+    # t = 300: 150 latents, 19 blocks -> 4 blocks chosen incl. newest (18)
+    assert 18 in res["blocks"][5] and (res["blocks"][5] >= 0).sum() == 4
+    assert rows[5]["n_rows"] == 16 + 128
+
+
+def test_low_precision_formats_match_brute():
+    cfg = gen.shrink(gen.CONFIGS["1m_lowp"], B=2, N=1024, t_last=2047, K_b=16, K=64, seed=24)
+    _, res, rows = _run_both(cfg)
+    _compare(cfg, res, rows)
+
+
+def test_prefill_shape_matches_brute():
+    # prefill structure (many queries, causal, one indexer, linear window
+    # ring), scaled down: 256 prior raw tokens + a 64-token chunk
+    cfg = gen.shrink(gen.CONFIGS["prefill"], Tq=64, N=160, t_last=319, K_b=8, K=32,
+                     W_cap=512, comp_T=64, comp_pos0=256, win_pos0=256 - 127, seed=25)
+    _, res, rows = _run_both(cfg, compress_first=True)
+    _compare(cfg, res, rows)
+
+
+def test_newest_block_forced_even_when_worst():
+    cfg = gen.shrink(gen.CONFIGS["tiny"], Tq=1, K_b=8, K=32, seed=26)
+
+    def zero_newest(inp):
+        # block of the newest latent scores 0 on the candidate-source indexer
+        inp["ks"][0, 2040:2048] = 0
+    _, res, rows = _run_both(cfg, inp_edit=zero_newest)
+    _compare(cfg, res, rows)
+    assert res["block_max"][0, 255] == 0.0
+    assert 255 in res["blocks"][0]
+    assert np.sort(res["block_max"][0])[-8] > 0  # it would not have made the cut
+
+
+def test_640_rows_at_long_context():
+    cfg = gen.shrink(gen.CONFIGS["128k"], B=1, N=8192, t_last=16383, K_b=2048, K=512,
+                     comp_T=0, seed=27)
+    inp, res, rows = _run_both(cfg)
+    _compare(cfg, res, rows)
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")))
+    assert rows[0]["n_rows"] == gold["positions_per_query"]["value"] == 640
+    assert (res["sel"][0] >= 0).sum() == gold["index_topk"]["value"]
+
+
+# ---------------------------------------------------------------- attention
+def _attn_case(seed=30, K=4, W=3, t=50):
+    rng = np.random.default_rng(seed)
+    import torch
+
+    def bits(x):
+        return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q = bits(rng.standard_normal((1, 1, 64, 512)))
+    lat = bits(rng.standard_normal((1, 32, 512)))
+    win = bits(rng.standard_normal((1, 64, 512)))
+    sel = np.array([[3, 7, 8, 20][:K] + [-1] * 0], np.int32)
+    return q, lat, win, sel, np.array([[t]], np.int64), bits
+
+
+def test_attention_one_row_and_minus_inf_sink():
+    q, lat, win, sel, q_pos, _ = _attn_case()
+    sel[:] = -1
+    sink = np.full(64, -np.inf, np.float32)
+    out, lse = ref.attn(q, lat, sel, win, q_pos, sink, W=1, scale=512 ** -0.5)
+    row = brute.dec_bf16(win[0, 50 % 64])
+    assert np.array_equal(out[0], np.broadcast_to(row, (64, 512)))
+
+
+def test_attention_huge_sink_gives_zero():
+    q, lat, win, sel, q_pos, _ = _attn_case()
+    sink = np.full(64, 1e30, np.float32)
+    out, lse = ref.attn(q, lat, sel, win, q_pos, sink, W=3, scale=512 ** -0.5)
+    assert np.all(out == 0.0)
+    assert np.allclose(lse, 1e30)
+
+
+def test_attention_equal_rows_closed_form():
+    q, lat, win, sel, q_pos, bits = _attn_case()
+    v = np.random.default_rng(31).standard_normal(512)
+    vb = bits(v)
+    lat[:] = vb
+    win[:] = vb
+    sink = np.random.default_rng(32).standard_normal(64).astype(np.float32)
+    scale = 512 ** -0.5
+    out, lse = ref.attn(q, lat, sel, win, q_pos, sink, W=3, scale=scale)
+    vd = brute.dec_bf16(vb)
+    n = 4 + 3
+    for h in range(64):
+        ell = float(brute.dec_bf16(q[0, 0, h]) @ vd) * scale
+        sh = float(sink[h])
+        p_sink = np.exp(sh) / (np.exp(sh) + n * np.exp(ell))
+        np.testing.assert_allclose(out[0, h], vd * (1 - p_sink), rtol=1e-10, atol=1e-12)
+
+
+def test_attention_order_of_sel_irrelevant():
+    q, lat, win, sel, q_pos, _ = _attn_case()
+    sink = np.zeros(64, np.float32)
+    a, la = ref.attn(q, lat, sel, win, q_pos, sink, W=3, scale=0.05)
+    b, lb = ref.attn(q, lat, sel[:, ::-1].copy(), win, q_pos, sink, W=3, scale=0.05)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(la, lb, rtol=1e-14)
+
+
+def test_minus_inf_sink_is_textbook_softmax():
+    q, lat, win, sel, q_pos, _ = _attn_case()
+    sink = np.full(64, -np.inf, np.float32)
+    out, _ = ref.attn(q, lat, sel, win, q_pos, sink, W=3, scale=0.05)
+    rows = np.concatenate([brute.dec_bf16(lat[0, sel[0]]),
+                           brute.dec_bf16(win[0, [48 % 64, 49 % 64, 50 % 64]])])
+    qd = brute.dec_bf16(q[0, 0])
+    logits = qd @ rows.T * 0.05
+    p = np.exp(logits - logits.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    np.testing.assert_allclose(out[0], p @ rows, rtol=1e-10, atol=1e-12)
+
+
+def test_config_shapes_reproduce_the_pages_figures():
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_constants.json")))
+    c4, c5 = gen.CONFIGS["1m"], gen.CONFIGS["1m_lowp"]
+    assert c4.t_last + 1 == gold["context_tokens"]["value"]
+    assert c4.N == gold["compressed_positions_at_1M_approx"]["exact_reading"]
+    assert c4.N * 512 // 2 == gold["fp4_kv_bytes_per_source_layer"]["exact_bytes"]
+    assert (c4.t_last + 1) * 512 * 2 == gold["dense_bf16_kv_bytes_1M"]["exact_bytes"]
+    assert c5.W * 512 == gold["fp8_window_bytes_per_layer"]["exact_bytes"]
+    assert c4.K_b * 8 == gold["candidate_coverage_positions_approx"]["value"]
+    assert c4.K + c4.W == gold["positions_per_query"]["value"]
+    assert abs(1e6 / (c4.K + c4.W) - gold["dense_ratio_at_1M_approx"]["value"]) < 5
