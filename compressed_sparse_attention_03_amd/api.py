@@ -1,0 +1,180 @@
+"""Python binding of the CSA2 C ABI: torch tensors in, pointers + sizes out.
+
+Argument marshalling only -- every step runs in the HIP kernels of
+``libcsa2.so``; torch only provides device memory and the current stream.
+Names follow include/csa2.h.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import BF16, F32, FP8_E4M3, NVFP4, SCORES_CAND, SCORES_SCAN, check, lib
+
+D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _rows_contig(t: torch.Tensor, inner: int, name: str):
+    """t is [B, rows, inner] (or [B, rows, ...] flattening to inner) with
+    contiguous rows; returns (batch stride, row stride) in elements."""
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: innermost dimension must be contiguous")
+    return t.stride(0)
+
+
+def _key_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported key dtype {t.dtype}")
+
+
+def workspace_bytes(op: int, R: int, n: int, k: int) -> int:
+    return int(lib().csa2_workspace_bytes(op, R, n, k))
+
+
+def compress(raw: torch.Tensor, gate: torch.Tensor, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """a1: raw, gate bf16 [B][T][512] -> out bf16 [B][T/2][512] (may be a cache slice)."""
+    B, T, _ = raw.shape
+    for t, n in ((raw, "raw"), (gate, "gate"), (out, "out")):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1 or t.stride(-2) != D:
+            raise ValueError(f"compress: {n} must be bf16 with contiguous 512-wide rows")
+    check("csa2_compress", lib().csa2_compress(B, T, _p(raw), raw.stride(0), _p(gate), gate.stride(0),
+                                               _p(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def index_scan(q, w, k, q_pos, scores=None, block_max=None, stream=None):
+    """a2: indexer scores of every latent and/or per-block maxima.
+
+    q bf16 [B][Tq][32][128], w f32 [B][Tq][32], k [B][N][128] (bf16 or E4M3
+    bytes), q_pos int64 [B][Tq]; scores f32 [B*Tq][>=N], block_max f32
+    [B*Tq][>=ceil(N/8)]."""
+    B, Tq = q.shape[:2]
+    N = k.shape[1]
+    assert q.is_contiguous() and w.is_contiguous() and q_pos.is_contiguous()
+    check("csa2_index_scores", lib().csa2_index_scores(
+        SCORES_SCAN, B, Tq, _p(q), BF16, _p(w), _p(k), _key_dtype(k), _rows_contig(k, DI, "k"), N,
+        _p(q_pos), None, 0, _p(scores), scores.stride(0) if scores is not None else 0, None,
+        _p(block_max), block_max.stride(0) if block_max is not None else 0, _stream(stream)))
+    return scores, block_max
+
+
+def index_cand(q, w, k, q_pos, blocks, scores, ids, stream=None):
+    """a4: scores of the latents of the chosen blocks (blocks int32 [B*Tq][K_b])."""
+    B, Tq = q.shape[:2]
+    N = k.shape[1]
+    K_b = blocks.shape[1]
+    assert q.is_contiguous() and w.is_contiguous() and q_pos.is_contiguous() and blocks.is_contiguous()
+    assert scores.stride(0) == ids.stride(0)
+    check("csa2_index_scores", lib().csa2_index_scores(
+        SCORES_CAND, B, Tq, _p(q), BF16, _p(w), _p(k), _key_dtype(k), _rows_contig(k, DI, "k"), N,
+        _p(q_pos), _p(blocks), K_b, _p(scores), scores.stride(0), _p(ids), None, 0, _stream(stream)))
+    return scores, ids
+
+
+def select_topk(scores, k: int, out, ids=None, forced=None, force_last=False, stream=None):
+    """a3 / a5: top-k ids per row (ascending, -1 padded)."""
+    R, n = scores.shape
+    check("csa2_select_topk", lib().csa2_select_topk(
+        R, n, _p(scores), scores.stride(0), _p(ids), ids.stride(0) if ids is not None else 0,
+        _p(forced), 1 if force_last else 0, k, _p(out), out.stride(0), None, 0, _stream(stream)))
+    return out
+
+
+def sparse_attn(q, lat, sel, win, q_pos, sink, W: int, scale: float, out, lat_scale=None,
+                win_scale=None, lse=None, ws=None, stream=None):
+    """a6: attention over the selected latents + the raw window with sinks.
+
+    q bf16 [B][Tq][64][512]; lat bf16 [B][N][512] or NVFP4 uint8 [B][N][256]
+    with lat_scale uint8 [B][N][32]; sel int32 [B*Tq][K]; win bf16
+    [B][W_cap][512] or E4M3 uint8 with win_scale f32 [B][W_cap]; out bf16
+    [B*Tq][64][512]; lse f32 [B*Tq][64] or None; ws from workspace_bytes."""
+    B, Tq = q.shape[:2]
+    N = lat.shape[1]
+    W_cap = win.shape[1]
+    K = sel.shape[1]
+    lat_dt = BF16 if lat.dtype == torch.bfloat16 else NVFP4
+    win_dt = BF16 if win.dtype == torch.bfloat16 else FP8_E4M3
+    assert q.stride(-1) == 1 and q.stride(1) == HQ * D
+    check("csa2_sparse_attn", lib().csa2_sparse_attn(
+        B, Tq, _p(q), q.stride(0), _p(lat), lat_dt, _p(lat_scale), lat.stride(0) // lat.stride(1), N,
+        _p(sel), K, sel.stride(0), _p(win), win_dt, _p(win_scale), W, W_cap,
+        win.stride(0) // win.stride(1), _p(q_pos), _p(sink), float(scale), _p(out), out.stride(0),
+        _p(lse), _p(ws), ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
+    return out, lse
+
+
+def dequant_fp8(src, row_scale=None, dtype=torch.bfloat16, out=None, stream=None):
+    rows, cols = src.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=src.device)
+    dt = F32 if out.dtype == torch.float32 else BF16
+    check("csa2_dequant_fp8", lib().csa2_dequant_fp8(_p(src), _p(row_scale), rows, cols, _p(out), dt,
+                                                     _stream(stream)))
+    return out
+
+
+def dequant_nvfp4(packed, scales, dtype=torch.bfloat16, out=None, stream=None):
+    rows, half = packed.shape
+    cols = half * 2
+    if out is None:
+        out = torch.empty((rows, cols), dtype=dtype, device=packed.device)
+    dt = F32 if out.dtype == torch.float32 else BF16
+    check("csa2_dequant_nvfp4", lib().csa2_dequant_nvfp4(_p(packed), _p(scales), rows, cols, _p(out),
+                                                         dt, _stream(stream)))
+    return out
+
+
+class DecodePath:
+    """Buffers and call order of one pass of the CSA2 hot path.
+
+    The call order is the method's (NVFP4 article, section 3 call tree):
+    [compressor] -> candidate-source scan + block max -> block top-K_b with
+    the newest block kept -> current-layer indexer over the candidates ->
+    position top-K -> sparse attention over Sel + window with sinks."""
+
+    def __init__(self, B: int, Tq: int, N: int, K_b: int = 2048, K: int = 512, W: int = 128,
+                 device="cuda"):
+        self.B, self.Tq, self.N, self.K_b, self.K, self.W = B, Tq, N, K_b, K, W
+        R = B * Tq
+        nblk = (N + BLK - 1) // BLK
+        dev = torch.device(device)
+        self.block_max = torch.empty((R, nblk), dtype=torch.float32, device=dev)
+        self.blocks = torch.empty((R, K_b), dtype=torch.int32, device=dev)
+        self.cand_scores = torch.empty((R, K_b * BLK), dtype=torch.float32, device=dev)
+        self.cand_ids = torch.empty((R, K_b * BLK), dtype=torch.int32, device=dev)
+        self.sel = torch.empty((R, K), dtype=torch.int32, device=dev)
+        self.out = torch.empty((R, HQ, D), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((R, HQ), dtype=torch.float32, device=dev)
+        wsb = workspace_bytes(_lib.OP_SPARSE_ATTN, R, K, W)
+        self.ws = torch.empty((max(wsb, 16) // 4 + 4,), dtype=torch.float32, device=dev)
+
+    def run(self, inp: dict, scale: float, compress_first: bool = True, stream=None):
+        if compress_first and inp.get("raw") is not None:
+            g0 = inp["cfg"].comp_pos0 // 2
+            T = inp["raw"].shape[1]
+            compress(inp["raw"], inp["gate"], inp["lat"][:, g0:g0 + T // 2], stream=stream)
+        index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,
+                   stream=stream)
+        select_topk(self.block_max, self.K_b, self.blocks, force_last=True, stream=stream)
+        index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], self.blocks, self.cand_scores,
+                   self.cand_ids, stream=stream)
+        select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids, stream=stream)
+        sparse_attn(inp["q"], inp["lat"], self.sel, inp["win"], inp["q_pos"], inp["sink"], self.W,
+                    scale, self.out, lat_scale=inp.get("lat_scale"), win_scale=inp.get("win_scale"),
+                    lse=self.lse, ws=self.ws, stream=stream)
+        return self.out

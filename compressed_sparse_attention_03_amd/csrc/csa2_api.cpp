@@ -1,0 +1,198 @@
+// csa2_api.cpp -- the extern "C" entry points of libcsa2: host-side argument
+// validation, then the kernel launchers.  Nothing is enqueued unless every
+// check passes; no C++ exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/csa2.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [lo, hi) byte ranges overlap?
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + bbytes && pb < pa + abytes;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ELAUNCH; }
+
+// Clear an error left behind by earlier, unrelated runtime calls so that a
+// failure reported after our launches is our own.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "ok";
+    case CSA2_EINVAL: return "invalid argument (null pointer, size, stride or alignment)";
+    case CSA2_EUNSUPPORTED: return "unsupported dtype or shape";
+    case CSA2_ELAUNCH: return "kernel launch failed";
+    case CSA2_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int csa2_version(void) { return (1 << 16) | 0; }
+
+size_t csa2_workspace_bytes(int op, int64_t R, int64_t n, int64_t k) {
+  if (R <= 0) return 0;
+  if (op == CSA2_OP_SPARSE_ATTN) {
+    if (n < 0 || k < 1) return 0;
+    return csa2::attn_workspace_bytes(R, (int)(n + k));
+  }
+  return 0;  // CSA2_OP_SELECT: one workgroup per row, no scratch
+}
+
+int csa2_compress(int B, int T, const void* kv, int64_t kv_sb, const void* gate, int64_t g_sb,
+                  void* out, int64_t out_sb, hipStream_t stream) {
+  if (B < 0 || T < 0 || (T & 1)) return CSA2_EINVAL;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (B > 65535) return CSA2_EUNSUPPORTED;
+  if (!kv || !gate || !out) return CSA2_EINVAL;
+  if (!aligned(kv, 16) || !aligned(gate, 16) || !aligned(out, 16)) return CSA2_EINVAL;
+  const int64_t rowsz = (int64_t)T * CSA2_D, orow = (int64_t)(T / 2) * CSA2_D;
+  if ((B > 1 && (kv_sb < rowsz || g_sb < rowsz || out_sb < orow)) || kv_sb % 8 || g_sb % 8 ||
+      out_sb % 8 || kv_sb < 0 || g_sb < 0 || out_sb < 0)
+    return CSA2_EINVAL;
+  const int64_t kv_bytes = ((int64_t)(B - 1) * kv_sb + rowsz) * 2;
+  const int64_t g_bytes = ((int64_t)(B - 1) * g_sb + rowsz) * 2;
+  const int64_t o_bytes = ((int64_t)(B - 1) * out_sb + orow) * 2;
+  if (overlap(out, o_bytes, kv, kv_bytes) || overlap(out, o_bytes, gate, g_bytes)) return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_compress(B, T, kv, kv_sb, gate, g_sb, out, out_sb, stream));
+}
+
+int csa2_index_scores(int mode, int B, int Tq, const void* q, csa2_dtype q_dt, const float* w,
+                      const void* k, csa2_dtype k_dt, int64_t k_sb, int64_t n_cache,
+                      const int64_t* q_pos, const int32_t* cand_blocks, int K_b, float* scores,
+                      int64_t s_stride, int32_t* ids_out, float* block_max, int64_t bm_stride,
+                      hipStream_t stream) {
+  if (mode != CSA2_SCORES_SCAN && mode != CSA2_SCORES_CAND) return CSA2_EINVAL;
+  if (B < 0 || Tq < 0 || n_cache < 0) return CSA2_EINVAL;
+  if (q_dt != CSA2_BF16) return CSA2_EUNSUPPORTED;
+  if (k_dt != CSA2_BF16 && k_dt != CSA2_FP8_E4M3) return CSA2_EUNSUPPORTED;
+  if (n_cache > kMaxN * 8) return CSA2_EUNSUPPORTED;
+  const int64_t R = (int64_t)B * Tq;
+  if (R == 0) return CSA2_OK;
+  if (!q || !w || !q_pos) return CSA2_EINVAL;
+  if (!aligned(q, 16) || !aligned(w, 4)) return CSA2_EINVAL;
+  const bool fp8 = k_dt == CSA2_FP8_E4M3;
+  if (n_cache > 0) {
+    if (!k || !aligned(k, 16)) return CSA2_EINVAL;
+    if (k_sb < 0 || (B > 1 && k_sb < n_cache * CSA2_DI) || (k_sb % (fp8 ? 16 : 8))) return CSA2_EINVAL;
+  }
+  if (mode == CSA2_SCORES_SCAN) {
+    if (!scores && !block_max) return CSA2_EINVAL;
+    const int64_t nblk = (n_cache + CSA2_BLOCK - 1) / CSA2_BLOCK;
+    if (scores && s_stride < n_cache) return CSA2_EINVAL;
+    if (block_max && bm_stride < nblk) return CSA2_EINVAL;
+    if (B > 65535 || (Tq + 3) / 4 > 65535) return CSA2_EUNSUPPORTED;
+    if (n_cache == 0) return CSA2_OK;
+    clear_stale_error();
+    return launched(csa2::launch_index_scan(B, Tq, q, w, k, fp8, k_sb, n_cache, q_pos, scores,
+                                            s_stride, block_max, bm_stride, stream));
+  }
+  if (!cand_blocks || !scores || !ids_out || K_b < 1) return CSA2_EINVAL;
+  if (K_b > kMaxN / CSA2_BLOCK) return CSA2_EUNSUPPORTED;
+  if (s_stride < (int64_t)K_b * CSA2_BLOCK) return CSA2_EINVAL;
+  if (R > 65535) return CSA2_EUNSUPPORTED;
+  // n_cache == 0: nothing is visible, the kernel only writes absent entries
+  // and never reads a key
+  clear_stale_error();
+  return launched(csa2::launch_index_cand(B, Tq, q, w, k, fp8, k_sb, n_cache, q_pos, cand_blocks,
+                                          K_b, scores, ids_out, s_stride, stream));
+}
+
+int csa2_select_topk(int R, int64_t n, const float* scores, int64_t s_stride, const int32_t* ids,
+                     int64_t id_stride, const int32_t* forced, int force_last, int k, int32_t* out,
+                     int64_t o_stride, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (R < 0 || n < 1 || k < 1) return CSA2_EINVAL;
+  if (n > kMaxN || k > kMaxN) return CSA2_EUNSUPPORTED;
+  if (R == 0) return CSA2_OK;
+  if (!scores || !out) return CSA2_EINVAL;
+  if (s_stride < n || o_stride < k) return CSA2_EINVAL;
+  if (ids && id_stride < n) return CSA2_EINVAL;
+  if (forced && force_last) return CSA2_EINVAL;
+  if (!aligned(scores, 4) || !aligned(out, 4) || (ids && !aligned(ids, 4))) return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_select_topk(R, n, scores, s_stride, ids, id_stride, forced,
+                                           force_last ? 1 : 0, k, out, o_stride, stream));
+}
+
+int csa2_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
+                     csa2_dtype lat_dt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,
+                     const int32_t* sel, int K, int64_t sel_sb, const void* win, csa2_dtype win_dt,
+                     const float* win_scale, int W, int W_cap, int64_t win_sb,
+                     const int64_t* q_pos, const float* sink, float scale, void* out,
+                     int64_t out_sb, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (B < 0 || Tq < 0 || K < 0 || W < 1 || W_cap < W || n_cache < 0) return CSA2_EINVAL;
+  if (K > 2048) return CSA2_EUNSUPPORTED;
+  if (lat_dt != CSA2_BF16 && lat_dt != CSA2_NVFP4) return CSA2_EUNSUPPORTED;
+  if (win_dt != CSA2_BF16 && win_dt != CSA2_FP8_E4M3) return CSA2_EUNSUPPORTED;
+  if (n_cache >= (int64_t(1) << 31)) return CSA2_EUNSUPPORTED;
+  const int64_t R = (int64_t)B * Tq;
+  if (R == 0) return CSA2_OK;
+  if (R > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  if (!q || !win || !q_pos || !sink || !out) return CSA2_EINVAL;
+  if (K > 0 && !sel) return CSA2_EINVAL;
+  if (n_cache > 0 && !lat) return CSA2_EINVAL;
+  if (lat_dt == CSA2_NVFP4 && n_cache > 0 && !lat_scale) return CSA2_EINVAL;
+  if (win_dt == CSA2_FP8_E4M3 && !win_scale) return CSA2_EINVAL;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(sink, 4) || (lse && !aligned(lse, 4)))
+    return CSA2_EINVAL;
+  if (lat && !aligned(lat, lat_dt == CSA2_BF16 ? 16 : 4)) return CSA2_EINVAL;
+  if (!aligned(win, win_dt == CSA2_BF16 ? 16 : 8)) return CSA2_EINVAL;
+  if (q_sb % 8 || q_sb < 0 || (B > 1 && q_sb < (int64_t)Tq * CSA2_HQ * CSA2_D)) return CSA2_EINVAL;
+  if (out_sb % 8 || out_sb < (int64_t)CSA2_HQ * CSA2_D) return CSA2_EINVAL;
+  if (K > 0 && sel_sb < K) return CSA2_EINVAL;
+  if (lat_sb < 0 || (B > 1 && lat_sb < n_cache)) return CSA2_EINVAL;
+  if (win_sb < 0 || (B > 1 && win_sb < W_cap)) return CSA2_EINVAL;
+  const size_t need = csa2::attn_workspace_bytes(R, K + W);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return CSA2_EWORKSPACE;
+  clear_stale_error();
+  const int lat_fmt = lat_dt == CSA2_NVFP4 ? 3 : 1;
+  const int win_fmt = win_dt == CSA2_FP8_E4M3 ? 2 : 1;
+  return launched(csa2::launch_sparse_attn(B, Tq, q, q_sb, lat, lat_fmt, lat_scale, lat_sb,
+                                           n_cache, sel, K, sel_sb, win, win_fmt, win_scale, W,
+                                           W_cap, win_sb, q_pos, sink, scale, out, out_sb, lse,
+                                           ws, stream));
+}
+
+int csa2_dequant_fp8(const uint8_t* src, const float* row_scale, int64_t rows, int cols,
+                     void* dst, csa2_dtype dst_dt, hipStream_t stream) {
+  if (rows < 0 || cols < 1) return CSA2_EINVAL;
+  if (dst_dt != CSA2_BF16 && dst_dt != CSA2_F32) return CSA2_EUNSUPPORTED;
+  if (rows == 0) return CSA2_OK;
+  if (!src || !dst) return CSA2_EINVAL;
+  if (!aligned(dst, dst_dt == CSA2_F32 ? 4 : 2)) return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_dequant_fp8(src, row_scale, rows, cols, dst, dst_dt == CSA2_F32,
+                                           stream));
+}
+
+int csa2_dequant_nvfp4(const uint8_t* packed, const uint8_t* scale_e4m3, int64_t rows, int cols,
+                       void* dst, csa2_dtype dst_dt, hipStream_t stream) {
+  if (rows < 0 || cols < 16 || cols % 16) return CSA2_EINVAL;
+  if (dst_dt != CSA2_BF16 && dst_dt != CSA2_F32) return CSA2_EUNSUPPORTED;
+  if (rows == 0) return CSA2_OK;
+  if (!packed || !scale_e4m3 || !dst) return CSA2_EINVAL;
+  if (!aligned(dst, 4)) return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_dequant_nvfp4(packed, scale_e4m3, rows, cols, dst,
+                                             dst_dt == CSA2_F32, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,237 @@
+/*
+ * csa2.h -- C ABI of the CSA2 (Compressed Sparse Attention 2) hot path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   [NVFP4]  "DeepSeek-V4.1-Flash-NVFP4" article, lpnh.cn/news/2752702:
+ *            section 3 (two KV sources per query: a 128-token raw window and
+ *            512 selected compressed positions, 640 rows in one sparse
+ *            attention call), 3.1 (sliding-window ring), 3.2 (2:1 Compressor
+ *            with softmax gating; NVFP4 cache, 16-element groups with an E4M3
+ *            scale), 3.3 (block-level top-2048 over blocks of 8 compressed
+ *            positions scored by their in-block maximum, newest block always
+ *            kept; a 32-head indexer with ReLU and per-head weights keeping
+ *            the top 512 positions), 3.4 (one-pass gather + online softmax
+ *            with a learnable attention sink).
+ *   [OQ3E]   "CSA2 sparse attention, 384-expert MoE and 1M context in
+ *            DeepSeek-V4.1-Flash-1017-oQ3e-ngram-mtp", nxmr.cn/news/161930:
+ *            section 1 (64 query heads, one latent KV head), section 2.1
+ *            (index_n_heads 32, index_head_dim 128, index_topk 512,
+ *            candidate_block_size 8, candidate_topk_blocks 2048,
+ *            sliding_window 128).
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
+ *     keeps no pointer after a call returns and allocates no device memory;
+ *     scratch space, where a call needs it, is passed in by the caller.
+ *   - Calls enqueue work on the given HIP stream and return without waiting.
+ *     The library holds no global state and may be called from several
+ *     threads at once on different streams.
+ *   - Strides are in elements of the tensor's own storage type (bytes for
+ *     FP8 / NVFP4 data); the innermost dimension is contiguous.
+ *   - Every call returns a csa2_status.  Arguments are validated on the host
+ *     before anything is enqueued; a call that returns an error has enqueued
+ *     nothing and written nothing.  Conditions only visible on the device
+ *     (contents of index arrays) are documented preconditions; a violation
+ *     gives unspecified results inside the documented output buffers, never
+ *     an access outside the buffers described here.
+ *   - Shapes fixed by the method: latent width D = 512, query heads HQ = 64,
+ *     index heads HI = 32, index width DI = 128, block size 8, compression
+ *     ratio 2.  Anything else is CSA2_EUNSUPPORTED.
+ *   - Positions: latent g pools raw tokens 2g and 2g+1; a query at raw
+ *     position t sees latents g < n_vis(t) = min(n_cache, (t+1)/2).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_D 512
+#define CSA2_HQ 64
+#define CSA2_HI 32
+#define CSA2_DI 128
+#define CSA2_BLOCK 8
+
+typedef enum csa2_dtype {
+  CSA2_BF16 = 1,     /* bfloat16                                           */
+  CSA2_FP8_E4M3 = 2, /* OCP FP8 E4M3FN (bias 7, max 448, S.1111.111 = NaN) */
+  CSA2_NVFP4 = 3,    /* E2M1 codes, 2 per byte (element 2i in the low      */
+                     /* nibble of byte i), one E4M3 scale per 16 elements  */
+  CSA2_F32 = 4
+} csa2_dtype;
+
+typedef enum csa2_status {
+  CSA2_OK = 0,
+  CSA2_EINVAL = -1,       /* null pointer, bad size or stride             */
+  CSA2_EUNSUPPORTED = -2, /* dtype / shape combination not implemented    */
+  CSA2_ELAUNCH = -3,      /* the HIP runtime refused a kernel launch      */
+  CSA2_EWORKSPACE = -4    /* workspace missing or smaller than required   */
+} csa2_status;
+
+/* Static description of a status code (never NULL). */
+const char *csa2_status_string(int status);
+
+/* Library version, (major << 16) | minor. */
+int csa2_version(void);
+
+/* ------------------------------------------------------------------------
+ * a1. Compressor: 2:1 softmax-gated pooling  ([NVFP4] section 3.2).
+ *
+ * For each sequence b, group g < T/2 and channel c:
+ *   out[b][g][c] = sum_{i=0,1} softmax_i(gate[b][2g+i][c]) * kv[b][2g+i][c]
+ * (softmax over the two tokens of the group, independently per channel),
+ * computed in fp32 and rounded to nearest-even bf16.
+ *   kv, gate : bf16 [B][T][512], batch strides kv_sb, g_sb (elements)
+ *   out      : bf16 [B][T/2][512], batch stride out_sb; may point into a
+ *              latent cache.  Must not overlap kv or gate.
+ * T must be even (the token of an unfinished group stays with the caller,
+ * who keeps it as the compressor's state until its partner arrives); the
+ * first token of the input sits at an even raw position.  T = 0 or B = 0 is
+ * a no-op.
+ * ---------------------------------------------------------------------- */
+int csa2_compress(int B, int T, const void *kv, int64_t kv_sb,
+                  const void *gate, int64_t g_sb, void *out, int64_t out_sb,
+                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a2 / a4. Indexer scores  ([NVFP4] section 3.3; [OQ3E] section 2.1).
+ *
+ *   score(p) = sum_{h<32} w[h] * max(0, q[h] . k[p])
+ *
+ * Row r = b*Tq + j is the query (b, j) at raw position q_pos[b][j].
+ *   q     : bf16 [B][Tq][32][128] (q_dt must be CSA2_BF16; with FP8 keys
+ *           the query is rounded to E4M3 inside the kernel, exact for the
+ *           small integers index queries take)
+ *   w     : f32  [B][Tq][32] per-query, per-head weights
+ *   k     : [B][n_cache][128] in k_dt (CSA2_BF16 or CSA2_FP8_E4M3), batch
+ *           stride k_sb elements
+ *   q_pos : int64 [B][Tq]
+ *
+ * mode CSA2_SCORES_SCAN: every latent p < n_cache is scored;
+ *   scores    (optional, may be NULL): f32 [B*Tq][s_stride >= n_cache],
+ *             -inf where p >= n_vis(t)
+ *   block_max (optional): f32 [B*Tq][bm_stride >= ceil(n_cache/8)], the max
+ *             of the block's visible scores, -inf for blocks with none
+ *   cand_blocks, K_b, ids_out are ignored.  At least one output is needed.
+ * mode CSA2_SCORES_CAND: only the latents of the chosen blocks are scored;
+ *   cand_blocks : int32 [B*Tq][K_b] block ids, -1 = none.  Precondition:
+ *             ids are -1 or < ceil(n_cache/8).
+ *   scores    : f32 [B*Tq][s_stride >= 8*K_b]; column 8j+i scores latent
+ *             8*cand_blocks[j]+i;
+ *   ids_out   : int32 [B*Tq][s_stride], that latent's index, or -1 (score
+ *             -inf) when the block id is -1 or the latent is not visible.
+ *   block_max, bm_stride are ignored.
+ * With integer-valued q, k (|q|,|k| <= 3) and weights that are multiples of
+ * 1/16 every score is exact in fp32, whatever the summation order.
+ * ---------------------------------------------------------------------- */
+#define CSA2_SCORES_SCAN 0
+#define CSA2_SCORES_CAND 1
+int csa2_index_scores(int mode, int B, int Tq, const void *q, csa2_dtype q_dt,
+                      const float *w, const void *k, csa2_dtype k_dt,
+                      int64_t k_sb, int64_t n_cache, const int64_t *q_pos,
+                      const int32_t *cand_blocks, int K_b, float *scores,
+                      int64_t s_stride, int32_t *ids_out, float *block_max,
+                      int64_t bm_stride, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a3 / a5. Top-k selection  ([NVFP4] section 3.3).
+ *
+ * Per row r < R over entries j < n: an entry is valid when its id is >= 0
+ * (ids == NULL means id = j) and its score is neither -inf nor NaN.  The
+ * result keeps the k valid entries with the largest scores, ties going to
+ * the smaller id; if fewer than k are valid, all of them.  A forced id is
+ * always kept, taking the place of the weakest pick:
+ *   forced     (optional) int32 [R]: id to keep in row r (-1 = none; an id
+ *              that is not a valid entry of the row is ignored);
+ *   force_last nonzero: additionally keep the valid entry with the largest
+ *              column index (for block scores this is the newest visible
+ *              block).  forced and force_last are mutually exclusive.
+ * out: int32 [R][o_stride >= k]: the kept ids in ascending order, then -1.
+ * Precondition when ids != NULL: the ids of a row's valid entries increase
+ * with the column index (true for the CAND output of csa2_index_scores when
+ * its block list is ascending, as this call produces it).
+ * ws / ws_bytes: scratch, size from csa2_workspace_bytes(CSA2_OP_SELECT..),
+ * may be NULL when that size is 0.  1 <= n <= 2^24, 1 <= k <= 2^24 (k > n
+ * simply keeps every valid entry and pads).
+ * ---------------------------------------------------------------------- */
+int csa2_select_topk(int R, int64_t n, const float *scores, int64_t s_stride,
+                     const int32_t *ids, int64_t id_stride,
+                     const int32_t *forced, int force_last, int k,
+                     int32_t *out, int64_t o_stride, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a6. Sparse attention over the selected latents and the raw window, with a
+ * per-head sink ([NVFP4] sections 3, 3.1, 3.4).
+ *
+ * For query row r = b*Tq + j at raw position t = q_pos[b][j], head h < 64:
+ *   rows    = { lat[b][sel[r][i]] : i < K, sel[r][i] >= 0 }
+ *           + { win[b][p mod W_cap] : max(0, t-W+1) <= p <= t }
+ *   l_i     = scale * (q[b][j][h] . row_i)          (K = V = the row)
+ *   out     = sum_i e^{l_i} row_i / (e^{sink[h]} + sum_i e^{l_i})
+ *   lse     = log(e^{sink[h]} + sum_i e^{l_i})
+ * computed with an online softmax in fp32, bf16 MFMA products, bf16 out.
+ *   q        : bf16 [B][Tq][64][512], batch stride q_sb elements
+ *   lat      : latent cache [B][n_cache][row] in lat_dt (CSA2_BF16: 512
+ *              bf16 per row; CSA2_NVFP4: 256 bytes per row), batch stride
+ *              lat_sb ROWS (>= n_cache)
+ *   lat_scale: CSA2_NVFP4 only, E4M3 bytes [B][n_cache][32] with the same
+ *              batch stride lat_sb rows; NULL otherwise
+ *   sel      : int32 [B*Tq][sel_sb], first K used (-1 = empty).
+ *              Precondition: every id is -1 or < n_cache.
+ *   win      : window source [B][W_cap][512] in win_dt (CSA2_BF16, or
+ *              CSA2_FP8_E4M3 with win_scale f32 [B][W_cap] per slot), batch
+ *              stride win_sb ROWS (>= W_cap) for both win and win_scale.  Precondition: slot p mod W_cap holds
+ *              raw position p for every window position of every query of
+ *              the sequence (W_cap >= W + spread of the row's q_pos).
+ *   sink     : f32 [64];  scale: logit scale (1/sqrt(512) in the configs)
+ *   out      : bf16 [B*Tq][64][512], 16-byte aligned, row stride out_sb
+ *              (elements, a multiple of 8)
+ *   lse      : optional f32 [B*Tq][64]
+ *   ws       : scratch of csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, ...)
+ * 0 <= K <= 2048, 1 <= W <= W_cap.
+ * ---------------------------------------------------------------------- */
+int csa2_sparse_attn(int B, int Tq, const void *q, int64_t q_sb,
+                     const void *lat, csa2_dtype lat_dt, const void *lat_scale,
+                     int64_t lat_sb, int64_t n_cache, const int32_t *sel,
+                     int K, int64_t sel_sb, const void *win,
+                     csa2_dtype win_dt, const float *win_scale, int W,
+                     int W_cap, int64_t win_sb, const int64_t *q_pos,
+                     const float *sink, float scale, void *out,
+                     int64_t out_sb, float *lse, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * a7. Standalone dequantisation ([NVFP4] sections 3.1, 3.2).
+ *   fp8   : src E4M3 [rows][cols], optional f32 row_scale [rows] (NULL = 1)
+ *   nvfp4 : packed [rows][cols/2] (element 2i low nibble of byte i),
+ *           scale_e4m3 [rows][cols/16]; cols % 16 == 0
+ *   dst   : [rows][cols] in dst_dt (CSA2_BF16 or CSA2_F32)
+ * ---------------------------------------------------------------------- */
+int csa2_dequant_fp8(const uint8_t *src, const float *row_scale, int64_t rows,
+                     int cols, void *dst, csa2_dtype dst_dt,
+                     hipStream_t stream);
+int csa2_dequant_nvfp4(const uint8_t *packed, const uint8_t *scale_e4m3,
+                       int64_t rows, int cols, void *dst, csa2_dtype dst_dt,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Scratch sizes.  op = CSA2_OP_SELECT: (R = rows, n = entries per row, k).
+ * op = CSA2_OP_SPARSE_ATTN: (R = B*Tq, n = K, k = W).  Returns bytes (0 when
+ * the call needs no scratch for that shape).
+ * ---------------------------------------------------------------------- */
+#define CSA2_OP_SELECT 1
+#define CSA2_OP_SPARSE_ATTN 2
+size_t csa2_workspace_bytes(int op, int64_t R, int64_t n, int64_t k);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,263 @@
+"""GPU parity: the HIP path (called through the C ABI) against the CPU oracle
+on the same seeded inputs.
+
+Bar: indices (blocks, positions) bit-exact; indexer scores and block maxima
+bit-exact (integer-valued inputs make fp32 scores exact); compressor and
+attention max|err| <= 2e-2 * max|ref| (5e-2 for the NVFP4 / FP8 config).
+Stage tests feed both sides identical inputs; chained tests run each side's
+whole path.  Full-size configs run the whole batch on the GPU and compare
+sampled sequences (or queries) against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_03_amd import api, gen
+from oracle import csa2_ref as ref
+from tests.gpu_util import (BF16_TOL, LOWP_TOL, bf16_to_np, check_close, np_subset,
+                            oracle_path, rows_of, run_gpu_path, say, valid_sorted)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _free_memory():
+    yield
+    torch.cuda.empty_cache()
+
+
+def _inputs(cfg, device="cuda"):
+    say(f"[gen] {cfg.name}: B={cfg.B} Tq={cfg.Tq} N={cfg.N} keys={cfg.key_fmt} lat={cfg.lat_fmt} "
+        f"win={cfg.win_fmt} seed={cfg.seed}")
+    inp = gen.make_inputs(cfg, device=device)
+    torch.cuda.synchronize()
+    return inp
+
+
+# --------------------------------------------------------------- stages
+def test_compress_stage_tiny():
+    cfg = gen.CONFIGS["tiny"]
+    inp = _inputs(cfg)
+    host = np_subset(inp)
+    out = torch.empty((cfg.B, cfg.comp_T // 2, 512), dtype=torch.bfloat16, device="cuda")
+    api.compress(inp["raw"], inp["gate"], out)
+    torch.cuda.synchronize()
+    bits, y64 = ref.compress(host["raw"], host["gate"])
+    got = bf16_to_np(out)
+    check_close("compress", got, y64, BF16_TOL)
+    # stronger than the bar: within one bf16 rounding of the exact value
+    assert np.all(np.abs(got - y64) <= np.abs(y64) * 2 ** -8 + 1e-30)
+    exact = (gen.to_numpy(out) == bits).mean()
+    say(f"  compress: {exact * 100:.3f}% of outputs bit-identical to the oracle's bf16")
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("tiny", dict(N=2051, t_last=4101, seed=31)),            # ragged tiles / blocks
+    ("1m_lowp", dict(B=2, N=4096, t_last=8191, Tq=3, seed=32)),  # FP8 keys, 3 queries
+])
+def test_scan_cand_select_stages(name, kw):
+    cfg = gen.shrink(gen.CONFIGS[name], **kw)
+    inp = _inputs(cfg)
+    host = np_subset(inp)
+    R, nblk = cfg.R, cfg.nblk
+    scores = torch.empty((R, cfg.N), dtype=torch.float32, device="cuda")
+    bm = torch.empty((R, nblk), dtype=torch.float32, device="cuda")
+    api.index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], scores=scores, block_max=bm)
+    torch.cuda.synchronize()
+    sc_ref, bm_ref = ref.scan(host["qs"], host["ws"], host["ks"], host["q_pos"], want_scores=True)
+    got_sc, got_bm = scores.cpu().numpy(), bm.cpu().numpy()
+    assert np.array_equal(got_sc.astype(np.float64), sc_ref), "scan scores"
+    assert np.array_equal(got_bm.astype(np.float64), bm_ref), "block max"
+    say(f"  scan: {R} rows x {cfg.N} scores and {nblk} block maxima bit-exact")
+
+    # block stage on identical block maxima, newest block kept
+    blocks = torch.empty((R, cfg.K_b), dtype=torch.int32, device="cuda")
+    api.select_topk(bm, cfg.K_b, blocks, force_last=True)
+    forced = np.array([ref.newest_block(t, cfg.N) for t in host["q_pos"].reshape(-1)], np.int32)
+    blk_ref = ref.select(bm_ref, cfg.K_b, forced=forced)
+    assert np.array_equal(blocks.cpu().numpy(), blk_ref), "block selection"
+
+    # candidate scoring on identical block lists
+    csc = torch.empty((R, cfg.K_b * 8), dtype=torch.float32, device="cuda")
+    cid = torch.empty((R, cfg.K_b * 8), dtype=torch.int32, device="cuda")
+    api.index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], blocks, csc, cid)
+    torch.cuda.synchronize()
+    csc_ref, cid_ref = ref.cand(host["qi"], host["wi"], host["ki"], host["q_pos"], blk_ref)
+    assert np.array_equal(cid.cpu().numpy(), cid_ref), "candidate ids"
+    assert np.array_equal(csc.cpu().numpy().astype(np.float64), csc_ref), "candidate scores"
+
+    sel = torch.empty((R, cfg.K), dtype=torch.int32, device="cuda")
+    api.select_topk(csc, cfg.K, sel, ids=cid)
+    sel_ref = ref.select(csc_ref, cfg.K, ids=cid_ref)
+    assert np.array_equal(sel.cpu().numpy(), sel_ref), "position selection"
+    say(f"  blocks, candidates and Sel bit-exact ({(sel_ref >= 0).sum(1).tolist()[:4]} selected)")
+
+
+@pytest.mark.parametrize("seed,R,n,k,mode", [
+    (40, 5, 300, 17, "ties"), (41, 3, 65536, 2048, "last"), (42, 7, 16384, 512, "ids"),
+    (43, 4, 1000, 1200, "plain"), (44, 6, 5000, 64, "forced"), (45, 2, 777, 1, "forced"),
+    (46, 3, 4096, 512, "allequal"),
+])
+def test_select_edge_cases(seed, R, n, k, mode):
+    rng = np.random.default_rng(seed)
+    scores = rng.integers(0, 40, (R, n)).astype(np.float32) / 16
+    if mode == "allequal":
+        scores[:] = 1.5
+    scores[rng.random((R, n)) < 0.07] = -np.inf
+    scores[0, :5] = np.nan
+    ids = None
+    if mode == "ids":
+        ids = np.tile((np.arange(n) * 2 + 1).astype(np.int32), (R, 1))
+        ids[rng.random((R, n)) < 0.05] = -1
+    forced = None
+    if mode == "forced":
+        forced = rng.integers(0, n, R).astype(np.int32)
+        forced[0] = -1
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    api.select_topk(torch.from_numpy(scores).cuda(), k, out,
+                    ids=None if ids is None else torch.from_numpy(ids).cuda(),
+                    forced=None if forced is None else torch.from_numpy(forced).cuda(),
+                    force_last=(mode == "last"))
+    torch.cuda.synchronize()
+    if mode == "last":
+        forced = np.array([max([j for j in range(n) if np.isfinite(scores[r, j])], default=-1)
+                           for r in range(R)], np.int32)
+    exp = ref.select(scores.astype(np.float64), k, ids=ids, forced=forced)
+    assert np.array_equal(out.cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("name,kw,tol", [
+    ("tiny", {}, BF16_TOL),
+    ("1m_lowp", dict(B=2, N=4096, t_last=8191, Tq=2, K_b=64, seed=33), LOWP_TOL),
+    ("tiny", dict(Tq=300, K_b=16, K=128, W_cap=512, seed=34), BF16_TOL),  # many queries: no split
+])
+def test_attention_stage(name, kw, tol):
+    cfg = gen.shrink(gen.CONFIGS[name], **kw)
+    inp = _inputs(cfg)
+    host = np_subset(inp)
+    # a selection with ragged fill: some rows keep fewer than K latents
+    rng = np.random.default_rng(cfg.seed)
+    sel = np.full((cfg.R, cfg.K), -1, np.int32)
+    for r in range(cfg.R):
+        t = int(host["q_pos"].reshape(-1)[r])
+        nv = ref.n_vis(t, cfg.N)
+        m = min(cfg.K, nv) - (r % 3) * 7
+        if m > 0:
+            sel[r, :m] = np.sort(rng.choice(nv, m, replace=False))
+    sel_t = torch.from_numpy(sel).cuda()
+    out = torch.empty((cfg.R, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((cfg.R, 64), dtype=torch.float32, device="cuda")
+    wsb = api.workspace_bytes(2, cfg.R, cfg.K, cfg.W)
+    ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device="cuda")
+    api.sparse_attn(inp["q"], inp["lat"], sel_t, inp["win"], inp["q_pos"], inp["sink"], cfg.W,
+                    cfg.scale, out, lat_scale=inp["lat_scale"], win_scale=inp["win_scale"],
+                    lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref.attn(host["q"], host["lat"], sel, host["win"], host["q_pos"], host["sink"],
+                              cfg.W, cfg.scale, lat_scale=host["lat_scale"],
+                              win_scale=host["win_scale"])
+    check_close("attention out", bf16_to_np(out).reshape(o_ref.shape), o_ref, tol)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3
+
+
+# ------------------------------------------------------ chained, small
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("tiny", dict(K_b=16, K=64, seed=35)),
+    ("tiny", dict(Tq=6, seed=36)),
+    ("1m_lowp", dict(B=3, N=8192, t_last=16383, K_b=128, seed=37)),
+    ("prefill", dict(Tq=256, N=4224, t_last=8447, K_b=64, K=128, W_cap=512, comp_T=256,
+                     comp_pos0=8192, win_pos0=8192 - 127, seed=38)),
+])
+def test_chained_small(name, kw):
+    cfg = gen.shrink(gen.CONFIGS[name], **kw)
+    inp = _inputs(cfg)
+    host = np_subset(inp)
+    res = oracle_path(host, cfg, compress_first=cfg.comp_T > 0)
+    path = run_gpu_path(inp, compress_first=cfg.comp_T > 0)
+    _compare_chain(cfg, path, res, list(range(cfg.R)))
+
+
+def _compare_chain(cfg, path, res, rows):
+    tol = LOWP_TOL if cfg.lat_fmt == "nvfp4" else BF16_TOL
+    bm = path.block_max.cpu().numpy()[rows].astype(np.float64)
+    assert np.array_equal(bm, res["block_max"]), "block max"
+    assert np.array_equal(path.blocks.cpu().numpy()[rows], res["blocks"]), "blocks"
+    assert np.array_equal(path.cand_ids.cpu().numpy()[rows], res["cand_ids"]), "candidate ids"
+    assert np.array_equal(path.cand_scores.cpu().numpy()[rows].astype(np.float64),
+                          res["cand_scores"]), "candidate scores"
+    assert np.array_equal(path.sel.cpu().numpy()[rows], res["sel"]), "Sel"
+    check_close("chained out", bf16_to_np(path.out)[rows], res["out"], tol)
+    assert np.abs(path.lse.cpu().numpy()[rows] - res["lse"]).max() < 2e-3
+    n_sel = (res["sel"] >= 0).sum(1)
+    say(f"  chained: indices bit-exact over {len(rows)} rows; Sel sizes {sorted(set(n_sel.tolist()))[:5]}")
+
+
+# ------------------------------------------------- full-size configs
+def _full(name, seqs, queries=None):
+    cfg = gen.CONFIGS[name]
+    inp = _inputs(cfg)
+    comp = cfg.comp_T > 0
+    host = np_subset(inp, seqs=seqs, queries=queries)
+    say(f"[gpu] {name}: full path")
+    path = run_gpu_path(inp, compress_first=comp)
+    say(f"[oracle] {name}: sequences {seqs}, queries {'all' if queries is None else len(queries)}")
+    res = oracle_path(host, cfg, compress_first=comp)
+    rows = rows_of(seqs, cfg.Tq, queries)
+    _compare_chain(cfg, path, res, rows)
+    if comp:
+        # the compressed rows the GPU wrote into the cache
+        g0 = cfg.comp_pos0 // 2
+        got = bf16_to_np(inp["lat"][list(seqs), g0:g0 + cfg.comp_T // 2])
+        _, y64 = ref.compress(host["raw"], host["gate"])
+        check_close("compressor rows", got, y64, BF16_TOL)
+    del inp, path
+    torch.cuda.empty_cache()
+
+
+def test_full_128k():
+    _full("128k", seqs=[0, 13, 31])
+
+
+def test_full_prefill_sampled_queries():
+    Tq = gen.CONFIGS["prefill"].Tq
+    _full("prefill", seqs=[0], queries=[0, 1, 2, 127, 128, 1000, 4095, 4096, 6000, Tq - 2, Tq - 1])
+
+
+def test_full_1m():
+    _full("1m", seqs=[0, 7])
+
+
+def test_full_1m_lowp():
+    _full("1m_lowp", seqs=[0, 31])
+
+
+def test_dequant_all_codes():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(16, 16).cuda()
+    scale = torch.linspace(0.5, 2.0, 16, device="cuda")
+    f = api.dequant_fp8(codes, scale, dtype=torch.float32)
+    torch.cuda.synchronize()
+    exp = ref.dequant_fp8(codes.cpu().numpy(), scale.cpu().numpy())
+    got = f.cpu().numpy().astype(np.float64)
+    nan = np.isnan(exp)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], exp[~nan])
+    rng = np.random.default_rng(50)
+    packed = rng.integers(0, 256, (37, 256), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, (37, 32), dtype=np.uint8)
+    for dt in (torch.float32, torch.bfloat16):
+        d = api.dequant_nvfp4(torch.from_numpy(packed).cuda(), torch.from_numpy(scales).cuda(), dtype=dt)
+        torch.cuda.synchronize()
+        exp = ref.dequant_nvfp4(packed, scales)
+        # every E2M1 x E4M3 product is a bf16 value, so both outputs are exact
+        assert np.array_equal(d.float().cpu().numpy().astype(np.float64), exp)
+
+
+def test_repeat_runs_bitwise_identical():
+    cfg = gen.shrink(gen.CONFIGS["128k"], B=4, N=16384, t_last=32767, comp_T=0, seed=60)
+    inp = _inputs(cfg)
+    a = run_gpu_path(inp, compress_first=False)
+    out_a, sel_a = a.out.clone(), a.sel.clone()
+    b = run_gpu_path(inp, compress_first=False)
+    assert torch.equal(out_a, b.out) and torch.equal(sel_a, b.sel)
