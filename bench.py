@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: compressor (the newest
+pair of raw tokens -> one latent) -> candidate-source indexer scan with the
+fused block max -> block top-2048 (newest block kept) -> current-layer
+indexer over the 16,384 candidates -> position top-512 -> sparse attention
+over the 512 latents + 128-token window with sinks.
+
+The headline workload is 1M-context decode: 8 sequences x 1,048,576 raw
+tokens (524,288 bf16 latents of 512, bf16 index keys), one query each.
+Inputs are seeded synthetic tensors already resident in HBM when the timed
+region starts.  Prints ONE JSON line (see the design doc for every field).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                  [--only-main] [--calib]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA2 decode queries/s (64 heads) at 1M ctx; % HBM peak; prefill indexer MFMA %"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA peak
+D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def n_vis(t, N):
+    return min(N, (t + 1) // 2)
+
+
+def step_bytes(cfg) -> dict:
+    """Algorithmic HBM bytes of one step, per stage: every operand the method
+    must read once and every result it must write once."""
+    R, B, Tq = cfg.R, cfg.B, cfg.Tq
+    kel = 1 if cfg.key_fmt == "fp8" else 2
+    nblk = cfg.nblk
+    lat_row = D // 2 + D // 16 if cfg.lat_fmt == "nvfp4" else 2 * D
+    win_row = D + 4 if cfg.win_fmt == "fp8" else 2 * D
+    t_hi = cfg.t_last
+    keys_per_seq = n_vis(t_hi, cfg.N)  # one pass over the keys serves all queries of a sequence
+    b = {}
+    b["compress"] = B * (cfg.comp_T * D * 2 * 2 + (cfg.comp_T // 2) * D * 2) if cfg.comp_T else 0
+    b["index_scan"] = B * keys_per_seq * DI * kel + R * (HI * DI * 2 + HI * 4 + nblk * 4 + 8)
+    b["select_blocks"] = R * (nblk * 4 + cfg.K_b * 4)
+    b["index_cand"] = R * (cfg.K_b * BLK * DI * kel + HI * DI * 2 + HI * 4 + cfg.K_b * 4 +
+                           cfg.K_b * BLK * 8)
+    b["select_positions"] = R * (cfg.K_b * BLK * 8 + cfg.K * 4)
+    b["sparse_attn"] = R * (cfg.K * lat_row + cfg.W * win_row + HQ * D * 2 * 2 + cfg.K * 4 + HQ * 4)
+    return b
+
+
+def prefill_indexer_flops(cfg) -> float:
+    pairs = sum(n_vis(t, cfg.N) for t in range(cfg.t_last - cfg.Tq + 1, cfg.t_last + 1))
+    return float(pairs) * HI * DI * 2
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel_src: str, workload: str):
+    """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
+    summary, if it was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "index_scan_1m_pmc.md")
+    if not os.path.exists(p):
+        return None
+    vals = {}
+    for line in open(p):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != source_hash(kernel_src) or vals.get("workload") != workload:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_config(name, steps, warmup, torch, gen, api):
+    cfg = gen.CONFIGS[name]
+    log(f"[bench] {name}: generating inputs (B={cfg.B}, N={cfg.N}, seed={cfg.seed})")
+    inp = gen.make_inputs(cfg, device="cuda")
+    path = api.DecodePath(cfg.B, cfg.Tq, cfg.N, cfg.K_b, cfg.K, cfg.W)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        path.run(inp, cfg.scale, compress_first=cfg.comp_T > 0)
+    torch.cuda.synchronize()
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        path.run(inp, cfg.scale, compress_first=cfg.comp_T > 0, marks=marks[i])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    stage_ms = {}
+    for si, sname in enumerate(api.STAGES):
+        stage_ms[sname] = sum(m[si].elapsed_time(m[si + 1]) for m in marks) / steps
+    log(f"[bench] {name}: {ms * 1e3:.1f} us/step  " +
+        "  ".join(f"{k}={v * 1e3:.1f}us" for k, v in stage_ms.items()))
+    return cfg, inp, ms, stage_ms
+
+
+def cpu_baseline(cfg, inp, gen, budget_s=12.0):
+    """The oracle as it stands, on whole sequences of the same workload, until
+    about budget_s of wall time has been spent (at least one sequence)."""
+    import numpy as np  # noqa: F401
+    from oracle import csa2_ref as ref
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    done, t0 = 0, time.perf_counter()
+    for b in range(cfg.B):
+        host = {k: (None if v is None else gen.to_numpy(v if k == "sink" else v[b:b + 1]))
+                for k, v in inp.items() if k != "cfg"}
+        host["comp_pos0"] = cfg.comp_pos0
+        ts = time.perf_counter()
+        ref.decode(host, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=cfg.comp_T > 0)
+        done += 1
+        log(f"[cpu] oracle sequence {b}: {time.perf_counter() - ts:.1f} s")
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    return {"value": done * cfg.Tq / wall, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {cfg.B} sequences of the 1M-context decode workload "
+                      f"(whole path per sequence incl. host copies), {wall:.1f} s wall"}
+
+
+def calib_copy(torch, nbytes=1 << 30):
+    """A plain elementwise copy of known size (reads and writes nbytes), for
+    scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-main", action="store_true", help="skip the low-precision and prefill extras")
+    ap.add_argument("--calib", action="store_true", help="also run a 1 GiB plain copy (counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the CSA2 path here is built and timed on a single "
+              "MI355X (no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from compressed_sparse_attention_03_amd import api, gen
+
+    api.lib()  # fail loudly if the HIP library is not built
+    if args.calib:
+        calib_copy(torch)
+
+    cfg, inp, ms, stage_ms = time_config("1m", args.steps, args.warmup, torch, gen, api)
+    sb = step_bytes(cfg)
+    total_b = sum(sb.values())
+    q_per_s = cfg.R / (ms * 1e-3)
+    scan_s = stage_ms["index_scan"] * 1e-3
+    scan_gbs = sb["index_scan"] / scan_s / 1e9
+    kernel_src = os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", "index_scores.hip")
+    workload = "1m"
+    traffic = stored_traffic(kernel_src, workload)
+    result = {
+        "metric": METRIC,
+        "value": round(q_per_s, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded bf16 N(0,1) latents/queries, integer-valued bf16 index q/k in [-3,3]",
+        "config": {
+            "workload": "1M-context decode: 8 sequences x 1,048,576 raw tokens (524,288 bf16 latents "
+                        "x 512), 1 query each; 64 heads x 512, 1 latent KV head; indexer 32 x 128; "
+                        "top-2048 blocks of 8 -> top-512 positions; window 128",
+            "sequences": cfg.B, "context_tokens": cfg.t_last + 1, "latents": cfg.N,
+            "queries_per_step": cfg.R, "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "index_scan (candidate-source indexer scan + fused block max)",
+            "bound": "hbm",
+            "achieved": round(scan_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": sb["index_scan"],
+            "avg_launch_us": round(scan_s * 1e6, 2),
+        },
+        "step_hbm": {
+            "algorithmic_bytes": total_b,
+            "GB/s": round(total_b / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(total_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+    }
+
+    extra = {}
+    if not args.only_main:
+        del inp
+        torch.cuda.empty_cache()
+        lcfg, linp, lms, lst = time_config("1m_lowp", max(3, args.steps // 2), 2, torch, gen, api)
+        lsb = step_bytes(lcfg)
+        lt = sum(lsb.values())
+        extra["lowp_1m"] = {
+            "workload": "32 sequences x 1M ctx, NVFP4 latents, FP8 E4M3 window + index keys",
+            "queries_per_s": round(lcfg.R / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
+            "step_hbm_frac": round(lt / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "index_scan_GBs": round(lsb["index_scan"] / (lst["index_scan"] * 1e-3) / 1e9, 1),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in lst.items()},
+        }
+        del linp
+        torch.cuda.empty_cache()
+        pcfg, pinp, pms, pst = time_config("prefill", 2, 1, torch, gen, api)
+        flops = prefill_indexer_flops(pcfg)
+        tfs = flops / (pst["index_scan"] * 1e-3) / 1e12
+        extra["prefill"] = {
+            "workload": "8192-token chunk after 65,536 raw tokens (36,864 latents), causal",
+            "indexer_flops": flops, "indexer_TFLOPs": round(tfs, 2),
+            "indexer_mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+            "tokens_per_s": round(pcfg.R / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
+            "stages_us": {k: round(v * 1e3, 2) for k, v in pst.items()},
+        }
+        del pinp
+        torch.cuda.empty_cache()
+        inp = gen.make_inputs(cfg, device="cuda") if not args.no_cpu_baseline else None
+    result["extra"] = extra
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, gen)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

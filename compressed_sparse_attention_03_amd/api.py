@@ -86,12 +86,19 @@ def index_cand(q, w, k, q_pos, blocks, scores, ids, stream=None):
     return scores, ids
 
 
-def select_topk(scores, k: int, out, ids=None, forced=None, force_last=False, stream=None):
-    """a3 / a5: top-k ids per row (ascending, -1 padded)."""
+def select_topk(scores, k: int, out, ids=None, forced=None, force_last=False, ws=None,
+                stream=None):
+    """a3 / a5: top-k ids per row (ascending, -1 padded).  ``ws``: scratch of
+    workspace_bytes(OP_SELECT, R, n, k) bytes (allocated here when None)."""
     R, n = scores.shape
+    if ws is None:
+        need = workspace_bytes(_lib.OP_SELECT, R, n, k)
+        if need:
+            ws = torch.empty((need + 63) // 64 * 8, dtype=torch.float64, device=scores.device)
     check("csa2_select_topk", lib().csa2_select_topk(
         R, n, _p(scores), scores.stride(0), _p(ids), ids.stride(0) if ids is not None else 0,
-        _p(forced), 1 if force_last else 0, k, _p(out), out.stride(0), None, 0, _stream(stream)))
+        _p(forced), 1 if force_last else 0, k, _p(out), out.stride(0), _p(ws),
+        ws.numel() * ws.element_size() if ws is not None else 0, _stream(stream)))
     return out
 
 
@@ -162,19 +169,40 @@ class DecodePath:
         self.lse = torch.empty((R, HQ), dtype=torch.float32, device=dev)
         wsb = workspace_bytes(_lib.OP_SPARSE_ATTN, R, K, W)
         self.ws = torch.empty((max(wsb, 16) // 4 + 4,), dtype=torch.float32, device=dev)
+        sel_b = max(workspace_bytes(_lib.OP_SELECT, R, nblk, K_b),
+                    workspace_bytes(_lib.OP_SELECT, R, K_b * BLK, K))
+        self.sel_ws = torch.empty(((max(sel_b, 64) + 63) // 64 * 8,), dtype=torch.float64, device=dev)
 
-    def run(self, inp: dict, scale: float, compress_first: bool = True, stream=None):
+    def run(self, inp: dict, scale: float, compress_first: bool = True, stream=None, marks=None):
+        """One pass.  ``marks``: optional 7 torch.cuda.Events recorded on the
+        stream before the first step and after each of the six steps."""
+        def mark(i):
+            if marks is not None:
+                marks[i].record(stream if stream is not None else torch.cuda.current_stream())
+        mark(0)
         if compress_first and inp.get("raw") is not None:
             g0 = inp["cfg"].comp_pos0 // 2
             T = inp["raw"].shape[1]
             compress(inp["raw"], inp["gate"], inp["lat"][:, g0:g0 + T // 2], stream=stream)
+        mark(1)
         index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,
                    stream=stream)
-        select_topk(self.block_max, self.K_b, self.blocks, force_last=True, stream=stream)
+        mark(2)
+        select_topk(self.block_max, self.K_b, self.blocks, force_last=True, ws=self.sel_ws,
+                    stream=stream)
+        mark(3)
         index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], self.blocks, self.cand_scores,
                    self.cand_ids, stream=stream)
-        select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids, stream=stream)
+        mark(4)
+        select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids, ws=self.sel_ws,
+                    stream=stream)
+        mark(5)
         sparse_attn(inp["q"], inp["lat"], self.sel, inp["win"], inp["q_pos"], inp["sink"], self.W,
                     scale, self.out, lat_scale=inp.get("lat_scale"), win_scale=inp.get("win_scale"),
                     lse=self.lse, ws=self.ws, stream=stream)
+        mark(6)
         return self.out
+
+
+STAGES = ("compress", "index_scan", "select_blocks", "index_cand", "select_positions",
+          "sparse_attn")

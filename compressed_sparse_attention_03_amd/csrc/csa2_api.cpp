@@ -51,7 +51,11 @@ size_t csa2_workspace_bytes(int op, int64_t R, int64_t n, int64_t k) {
     if (n < 0 || k < 1) return 0;
     return csa2::attn_workspace_bytes(R, (int)(n + k));
   }
-  return 0;  // CSA2_OP_SELECT: one workgroup per row, no scratch
+  if (op == CSA2_OP_SELECT) {
+    if (n < 1 || k < 1) return 0;
+    return csa2::select_workspace_bytes(R, n, k);
+  }
+  return 0;
 }
 
 int csa2_compress(int B, int T, const void* kv, int64_t kv_sb, const void* gate, int64_t g_sb,
@@ -117,8 +121,6 @@ int csa2_index_scores(int mode, int B, int Tq, const void* q, csa2_dtype q_dt, c
 int csa2_select_topk(int R, int64_t n, const float* scores, int64_t s_stride, const int32_t* ids,
                      int64_t id_stride, const int32_t* forced, int force_last, int k, int32_t* out,
                      int64_t o_stride, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (R < 0 || n < 1 || k < 1) return CSA2_EINVAL;
   if (n > kMaxN || k > kMaxN) return CSA2_EUNSUPPORTED;
   if (R == 0) return CSA2_OK;
@@ -127,9 +129,11 @@ int csa2_select_topk(int R, int64_t n, const float* scores, int64_t s_stride, co
   if (ids && id_stride < n) return CSA2_EINVAL;
   if (forced && force_last) return CSA2_EINVAL;
   if (!aligned(scores, 4) || !aligned(out, 4) || (ids && !aligned(ids, 4))) return CSA2_EINVAL;
+  const size_t need = csa2::select_workspace_bytes(R, n, k);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 64))) return CSA2_EWORKSPACE;
   clear_stale_error();
   return launched(csa2::launch_select_topk(R, n, scores, s_stride, ids, id_stride, forced,
-                                           force_last ? 1 : 0, k, out, o_stride, stream));
+                                           force_last ? 1 : 0, k, out, o_stride, ws, stream));
 }
 
 int csa2_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,

@@ -247,12 +247,15 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
   const void* kb = (const void*)((const char*)a.k + b * a.k_sb * key_elem_bytes<KT>());
 
+  // A block owns WAVES * tiles_per_wave consecutive tiles; its waves take
+  // them round-robin, so at any moment the block streams one contiguous
+  // stretch of keys.
   const int64_t n_tiles = (a.n_cache + 15) / 16;
-  int64_t t = ((int64_t)blockIdx.x * WAVES + wave) * a.tiles_per_wave;
-  const int64_t t_end = min(t + (int64_t)a.tiles_per_wave, n_tiles);
+  const int64_t blk0 = (int64_t)blockIdx.x * WAVES * a.tiles_per_wave;
+  int64_t t = blk0 + wave;
+  const int64_t t_end = min(blk0 + (int64_t)WAVES * a.tiles_per_wave, n_tiles);
   if (t >= t_end) return;
 
-  KT cur, nxt;
   auto fetch = [&](int64_t tile, KT& K) {
     const int64_t row = tile * 16 + kl;
     if (tile * 16 < max_nv)
@@ -260,17 +263,15 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     else
       zero_key(K);
   };
-  fetch(t, cur);
-  for (; t < t_end; ++t) {
-    if (t + 1 < t_end) fetch(t + 1, nxt);
-    const int64_t p = t * 16 + kl;
+  auto process = [&](int64_t tile, const KT& K) {
+    const int64_t p = tile * 16 + kl;
 #pragma unroll
     for (int qi = 0; qi < QPB; ++qi) {
       if (qi >= nq) break;
       const int64_t r = (int64_t)b * a.Tq + j0 + qi;
       float s = -INFINITY;
-      if (t * 16 < nv[qi]) {
-        s = tile_score(Q[qi], cur);
+      if (tile * 16 < nv[qi]) {
+        s = tile_score(Q[qi], K);
         if (p >= nv[qi]) s = -INFINITY;
       }
       if (a.scores && g == 0 && p < a.n_cache) a.scores[r * a.s_stride + p] = s;
@@ -283,7 +284,23 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         if (g == 0 && (kl & 7) == 0 && blk < nblk) a.block_max[r * a.bm_stride + blk] = m;
       }
     }
-    cur = nxt;
+  };
+  // DEPTH tiles in flight per wave: the loads of a wave's next-but-one tile
+  // are issued as soon as its current tile has been consumed
+  constexpr int DEPTH = 2;
+  KT buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (t + d * WAVES < t_end) fetch(t + d * WAVES, buf[d]);
+  for (; t < t_end; t += DEPTH * WAVES) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t tt = t + d * WAVES;
+      if (tt < t_end) {
+        process(tt, buf[d]);
+        if (tt + DEPTH * WAVES < t_end) fetch(tt + DEPTH * WAVES, buf[d]);
+      }
+    }
   }
 }
 
@@ -354,12 +371,13 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
   const int qpb = Tq >= 4 ? 4 : (Tq >= 2 ? 2 : 1);
   const int64_t nz = (Tq + qpb - 1) / qpb;
   const int64_t n_tiles = (n_cache + 15) / 16;
-  // aim for ~8 resident waves per CU over 256 CUs, each streaming a
-  // contiguous run of tiles (at most 32 tiles = 128 KiB of bf16 keys)
+  // at most 16 tiles per wave (a block streams 256 KiB of bf16 keys); fewer
+  // when that would leave the chip short of blocks.  Measured on the 1M
+  // decode scan: 16 tiles per wave with interleaved waves beat 8, 32 and 64.
   const int64_t target_waves = 4096;
   int64_t tpw = (n_tiles * B * nz + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
-  if (tpw > 32) tpw = 32;
+  if (tpw > 16) tpw = 16;
   a.tiles_per_wave = (int)tpw;
   const int64_t per_block = tpw * WAVES;
   dim3 grid((unsigned)((n_tiles + per_block - 1) / per_block), (unsigned)B, (unsigned)nz);

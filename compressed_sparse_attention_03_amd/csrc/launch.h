@@ -22,9 +22,10 @@ hipError_t launch_index_cand(int B, int Tq, const void* q, const float* w, const
                              const int32_t* blocks, int K_b, float* scores, int32_t* ids,
                              int64_t s_stride, hipStream_t s);
 
+size_t select_workspace_bytes(int64_t R, int64_t n, int64_t k);
 hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_stride,
                               const int32_t* ids, int64_t id_stride, const int32_t* forced,
-                              int force_last, int k, int32_t* out, int64_t o_stride,
+                              int force_last, int k, int32_t* out, int64_t o_stride, void* ws,
                               hipStream_t s);
 
 int attn_splits(int64_t R, int n_rows);

@@ -140,7 +140,9 @@ __device__ __forceinline__ u32x4 load_piece(const RowSrc& r, int p) {
   return v;
 }
 
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
+// One wave per SIMD: the 64 heads x 512 fp32 accumulators, the query
+// operand and the next tile's rows take more than half of the register file.
+__global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -171,40 +173,58 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
   const int rq = lane & 7;
   const int p0 = (lane >> 3) + 8 * wave;
 
-  for (int i0 = row_beg; i0 < row_end; i0 += TILE) {
-    __syncthreads();  // previous tile fully consumed
-    {
-      RowSrc src[4];
+  // A tile's rows are gathered into registers one tile ahead: the loads of
+  // tile i+1 are in flight while tile i is computed from LDS.
+  struct Staged {
+    u32x4 v[2][4];
+    float rs[4];
+    int ok[4];
+  } nxt;
+  auto gather = [&](int i0, Staged& st) {
+    RowSrc src[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) src[x] = row_source(a, b, t, selrow, i0 + 4 * rq + x, row_end);
+    for (int x = 0; x < 4; ++x) src[x] = row_source(a, b, t, selrow, i0 + 4 * rq + x, row_end);
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const int p = p0 + 32 * pp;
-        u32x4 v[4];
+    for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) v[x] = load_piece(src[x], p);
+      for (int x = 0; x < 4; ++x) st.v[pp][x] = load_piece(src[x], p0 + 32 * pp);
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = v[x];
-        // transpose: dim 8p+d gets the four rows' values side by side
+    for (int x = 0; x < 4; ++x) {
+      st.rs[x] = src[x].rscale;
+      st.ok[x] = src[x].fmt != 0;
+    }
+  };
+  auto stage = [&](const Staged& st) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const int w32 = d >> 1, sh = 16 * (d & 1);
-          u32x2 pr;
-          pr[0] = ((v[0][w32] >> sh) & 0xffffu) | (((v[1][w32] >> sh) & 0xffffu) << 16);
-          pr[1] = ((v[2][w32] >> sh) & 0xffffu) | (((v[3][w32] >> sh) & 0xffffu) << 16);
-          *reinterpret_cast<u32x2*>(&sm.vt[8 * p + d][4 * rq]) = pr;
-        }
-      }
-      if (wave == 0 && (lane >> 3) == 0) {
+    for (int pp = 0; pp < 2; ++pp) {
+      const int p = p0 + 32 * pp;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          sm.rscale[4 * rq + x] = src[x].rscale;
-          sm.rvalid[4 * rq + x] = src[x].fmt != 0;
-        }
+      for (int x = 0; x < 4; ++x) *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = st.v[pp][x];
+      // transpose: dim 8p+d gets the four rows' values side by side
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const int w32 = d >> 1, sh = 16 * (d & 1);
+        u32x2 pr;
+        pr[0] = ((st.v[pp][0][w32] >> sh) & 0xffffu) | (((st.v[pp][1][w32] >> sh) & 0xffffu) << 16);
+        pr[1] = ((st.v[pp][2][w32] >> sh) & 0xffffu) | (((st.v[pp][3][w32] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<u32x2*>(&sm.vt[8 * p + d][4 * rq]) = pr;
       }
     }
+    if (wave == 0 && (lane >> 3) == 0) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        sm.rscale[4 * rq + x] = st.rs[x];
+        sm.rvalid[4 * rq + x] = st.ok[x];
+      }
+    }
+  };
+
+  if (row_beg < row_end) gather(row_beg, nxt);
+  for (int i0 = row_beg; i0 < row_end; i0 += TILE) {
+    __syncthreads();  // previous tile fully consumed
+    stage(nxt);
     __syncthreads();
+    if (i0 + TILE < row_end) gather(i0 + TILE, nxt);
 
     // S^T = KV . Q^T for rows [16st, 16st+16)
     f32x4 s[2];
@@ -301,31 +321,44 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // merge the split partials of one query: grid (R, 16), 256 threads =
-// 4 heads x 64 threads x 8 dims
+// 4 heads x 64 threads x 8 dims.  All of a thread's partial loads are issued
+// before any is used (splits are at most MAX_SPLITS).
+constexpr int MAX_SPLITS = 16;
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t r = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
   const float sk = a.sink[h];
-  float M = sk;
-  for (int s = 0; s < a.splits; ++s) {
-    const float ms = a.part[((r * a.splits + s) * HQ + h) * PART + D];
-    M = fmaxf(M, ms);
+  float ms[MAX_SPLITS], ls[MAX_SPLITS];
+  f32x4 x0[MAX_SPLITS], x1[MAX_SPLITS];
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s) {
+    if (s < a.splits) {
+      const float* pp = a.part + ((r * a.splits + s) * HQ + h) * PART;
+      ms[s] = pp[D];
+      ls[s] = pp[D + 1];
+      x0[s] = *reinterpret_cast<const f32x4*>(pp + d0);
+      x1[s] = *reinterpret_cast<const f32x4*>(pp + d0 + 4);
+    } else {
+      ms[s] = -INFINITY;
+      ls[s] = 0.f;
+      x0[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      x1[s] = x0[s];
+    }
   }
+  float M = sk;
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s) M = fmaxf(M, ms[s]);
   float Z = expf(sk - M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.splits; ++s) {
-    const float* pp = a.part + ((r * a.splits + s) * HQ + h) * PART;
-    const float ms = pp[D];
-    if (ms == -INFINITY) continue;
-    const float e = expf(ms - M);
-    Z += pp[D + 1] * e;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(pp + d0);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(pp + d0 + 4);
+#pragma unroll
+  for (int s = 0; s < MAX_SPLITS; ++s) {
+    const float e = ms[s] == -INFINITY ? 0.f : expf(ms[s] - M);
+    Z += ls[s] * e;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[i] += x0[i] * e;
-      acc[4 + i] += x1[i] * e;
+      acc[i] += x0[s][i] * e;
+      acc[4 + i] += x1[s][i] * e;
     }
   }
   const float inv = 1.0f / Z;
@@ -338,12 +371,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 }  // namespace
 
-int attn_splits(int64_t R, int n_rows) {
-  if (R >= 192) return 1;
+// Tiles of 32 rows handled by one workgroup: many query rows -> one
+// workgroup per query (no merge); few -> split the row list so that roughly
+// 256+ workgroups run, at least 2 tiles each (each split costs a 128 KiB
+// fp32 partial that the merge reads back).
+static int attn_tiles_per_split(int64_t R, int n_rows) {
   const int tiles = (n_rows + TILE - 1) / TILE;
-  int want = (int)((512 + R - 1) / R);  // aim at >= 512 workgroups
-  int s = want < tiles ? want : tiles;
-  if (s > 16) s = 16;
+  if (R >= 192 || tiles <= 2) return tiles > 0 ? tiles : 1;
+  const int64_t want = (256 + R - 1) / R;  // splits wanted per query
+  int tps = (int)((tiles + want - 1) / want);
+  if (tps < 2) tps = 2;
+  if ((tiles + tps - 1) / tps > MAX_SPLITS) tps = (tiles + MAX_SPLITS - 1) / MAX_SPLITS;
+  return tps;
+}
+
+int attn_splits(int64_t R, int n_rows) {
+  const int tiles = (n_rows + TILE - 1) / TILE;
+  const int tps = attn_tiles_per_split(R, n_rows);
+  const int s = (tiles + tps - 1) / tps;
   return s < 1 ? 1 : s;
 }
 
@@ -363,8 +408,7 @@ hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const 
   const int64_t R = (int64_t)B * Tq;
   const int n_rows = K + W;
   const int splits = attn_splits(R, n_rows);
-  const int tiles = (n_rows + TILE - 1) / TILE;
-  const int tiles_per_split = (tiles + splits - 1) / splits;
+  const int tiles_per_split = attn_tiles_per_split(R, n_rows);
   AttnArgs a{(const uint16_t*)q, q_sb, Tq, lat, lat_fmt, (const uint8_t*)lat_scale, lat_sb,
              n_cache, sel, K, sel_sb, win, win_fmt, win_scale, W, W_cap, win_sb, q_pos, sink,
              scale, (uint16_t*)out, out_sb, lse, (float*)ws, splits, tiles_per_split * TILE};

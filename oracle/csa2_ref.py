@@ -122,6 +122,7 @@ def compress(raw: np.ndarray, gate: np.ndarray):
     """raw, gate: uint16 bf16 [B][T][512] -> (bf16 bits [B][T/2][512], float64)."""
     raw, gate = _c(raw, np.uint16), _c(gate, np.uint16)
     B, T, _ = raw.shape
+    assert raw.shape == gate.shape and raw.shape[2] == D and T % 2 == 0
     out = np.zeros((B, T // 2, D), np.uint16)
     out64 = np.zeros((B, T // 2, D), np.float64)
     lib().csa2ref_compress(B, T, _p(raw), T * D, _p(gate), T * D, _p(out), (T // 2) * D, _p(out64))
@@ -138,6 +139,8 @@ def scan(q, w, k, q_pos, want_scores=False):
     k = np.ascontiguousarray(k)
     B, Tq = q.shape[:2]
     N = k.shape[1]
+    assert q.shape == (B, Tq, HI, DI) and w.shape == (B, Tq, HI) and q_pos.shape == (B, Tq)
+    assert k.shape == (B, N, DI)
     nblk = (N + BLK - 1) // BLK
     sc = np.zeros((B * Tq, N), np.float64) if want_scores else None
     bm = np.zeros((B * Tq, nblk), np.float64)
@@ -167,6 +170,8 @@ def cand(q, w, k, q_pos, blocks):
     B, Tq = q.shape[:2]
     N = k.shape[1]
     K_b = blocks.shape[1]
+    assert q.shape == (B, Tq, HI, DI) and w.shape == (B, Tq, HI) and q_pos.shape == (B, Tq)
+    assert k.shape == (B, N, DI) and blocks.shape == (B * Tq, K_b)
     sc = np.zeros((B * Tq, K_b * BLK), np.float64)
     ids = np.zeros((B * Tq, K_b * BLK), np.int32)
     lib().csa2ref_cand(B, Tq, _p(q), _p(w), _p(k), _key_fmt(k), N * DI, N, _p(q_pos),
@@ -185,6 +190,15 @@ def attn(q, lat, sel, win, q_pos, sink, W, scale, lat_scale=None, win_scale=None
     q, sel, q_pos, sink = _c(q, np.uint16), _c(sel, np.int32), _c(q_pos, np.int64), _c(sink, np.float32)
     lat, win = np.ascontiguousarray(lat), np.ascontiguousarray(win)
     B, Tq = q.shape[:2]
+    assert q.shape == (B, Tq, HQ, D) and sink.shape == (HQ,) and q_pos.shape == (B, Tq)
+    assert sel.shape[0] == B * Tq and lat.shape[0] == B and win.shape[0] == B
+    assert win.shape[2] == (D if win.dtype == np.uint16 else D)
+    if lat.dtype != np.uint16:
+        assert lat.shape[2] == D // 2 and lat_scale is not None and lat_scale.shape == (B, lat.shape[1], D // 16)
+    else:
+        assert lat.shape[2] == D
+    if win.dtype != np.uint16:
+        assert win_scale is not None and win_scale.shape == (B, win.shape[1])
     N = lat.shape[1]
     W_cap = win.shape[1]
     K = sel.shape[1]

@@ -24,6 +24,7 @@ def np_subset(inp: dict, seqs=None, queries=None) -> dict:
     queries (dim 1 of the per-query tensors)."""
     out = {}
     per_query = {"q", "qs", "ws", "qi", "wi", "q_pos"}
+    shared = {"sink"}  # per head, not per sequence
     for k, v in inp.items():
         if k == "cfg":
             continue
@@ -31,7 +32,7 @@ def np_subset(inp: dict, seqs=None, queries=None) -> dict:
             out[k] = None
             continue
         t = v
-        if seqs is not None:
+        if seqs is not None and k not in shared:
             t = t[list(seqs)]
         if queries is not None and k in per_query:
             t = t[:, list(queries)]

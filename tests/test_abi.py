@@ -105,6 +105,8 @@ def test_select_validation(L):
     assert _select(L, ids=FAKE, id_stride=8) == _lib.EINVAL
     assert _select(L, forced=FAKE, last=1) == _lib.EINVAL
     assert _select(L, sc=ctypes.c_void_p(0x10001)) == _lib.EINVAL
+    # a long row with few rows needs scratch
+    assert _select(L, n=65536, s_stride=65536, k=2048, o_stride=2048) == _lib.EWORKSPACE
 
 
 def _attn(L, B=1, Tq=1, q=FAKE, q_sb=0, lat=FAKE, lat_dt=_lib.BF16, lat_scale=NULL, lat_sb=0,
@@ -142,7 +144,11 @@ def test_sparse_attn_validation(L):
 def test_workspace_sizes(L):
     # many query rows (prefill): one workgroup per row, no merge, no scratch
     assert L.csa2_workspace_bytes(_lib.OP_SPARSE_ATTN, 8192, 512, 128) == 0
-    assert L.csa2_workspace_bytes(_lib.OP_SELECT, 8, 65536, 2048) == 0
+    # few long rows: the pass over each row is split over many workgroups
+    assert L.csa2_workspace_bytes(_lib.OP_SELECT, 8, 65536, 2048) > 0
+    # many rows, or short rows: one workgroup per row, no scratch
+    assert L.csa2_workspace_bytes(_lib.OP_SELECT, 8192, 16384, 512) == 0
+    assert L.csa2_workspace_bytes(_lib.OP_SELECT, 8, 1000, 512) == 0
     a = L.csa2_workspace_bytes(_lib.OP_SPARSE_ATTN, 8, 512, 128)
     b = L.csa2_workspace_bytes(_lib.OP_SPARSE_ATTN, 32, 512, 128)
     assert a > 0 and b > 0

@@ -98,6 +98,9 @@ def test_scan_cand_select_stages(name, kw):
     (40, 5, 300, 17, "ties"), (41, 3, 65536, 2048, "last"), (42, 7, 16384, 512, "ids"),
     (43, 4, 1000, 1200, "plain"), (44, 6, 5000, 64, "forced"), (45, 2, 777, 1, "forced"),
     (46, 3, 4096, 512, "allequal"),
+    # few long rows take the split path; all-equal keys defeat its bracket
+    (47, 2, 65536, 2048, "allequal"), (48, 3, 65536, 2048, "forced"), (49, 5, 20000, 100, "ids"),
+    (51, 300, 16384, 512, "plain"),   # many rows: one workgroup per row, sampled
 ])
 def test_select_edge_cases(seed, R, n, k, mode):
     rng = np.random.default_rng(seed)
@@ -236,13 +239,21 @@ def test_full_1m_lowp():
 def test_dequant_all_codes():
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(16, 16).cuda()
     scale = torch.linspace(0.5, 2.0, 16, device="cuda")
-    f = api.dequant_fp8(codes, scale, dtype=torch.float32)
+    # unscaled: every E4M3 code decodes exactly
+    f = api.dequant_fp8(codes, None, dtype=torch.float32)
     torch.cuda.synchronize()
-    exp = ref.dequant_fp8(codes.cpu().numpy(), scale.cpu().numpy())
+    exp = ref.dequant_fp8(codes.cpu().numpy(), None)
     got = f.cpu().numpy().astype(np.float64)
     nan = np.isnan(exp)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan], exp[~nan])
+    # with an fp32 row scale the product is one fp32 rounding of the exact value
+    f = api.dequant_fp8(codes, scale, dtype=torch.float32)
+    torch.cuda.synchronize()
+    exp = ref.dequant_fp8(codes.cpu().numpy(), scale.cpu().numpy())
+    got = f.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.all(np.abs(got[~nan] - exp[~nan]) <= np.abs(exp[~nan]) * 2.0 ** -24)
     rng = np.random.default_rng(50)
     packed = rng.integers(0, 256, (37, 256), dtype=np.uint8)
     scales = rng.integers(0, 0x7F, (37, 32), dtype=np.uint8)
