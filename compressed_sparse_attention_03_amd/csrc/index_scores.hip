@@ -305,8 +305,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 }
 
 // ---- candidates: the latents of the chosen blocks ---------------------------
+// A tile is two candidate blocks (16 latents, two contiguous 2 KiB rows runs
+// for bf16 keys).  A wave owns pairs_per_wave consecutive tiles and works on
+// CB of them at a time: block ids first, then every key load of the batch,
+// then the contractions, so the dependent id -> key -> MFMA latencies are paid
+// once per batch instead of once per tile.
 template <typename QT, typename KT>
 __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
+  constexpr int CB = 4;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t r = blockIdx.y;
   const int b = (int)(r / a.Tq);
@@ -317,37 +323,39 @@ __global__ __launch_bounds__(256) void cand_kernel(CandArgs a) {
   const int64_t nv = n_visible(a.q_pos[r], a.n_cache);
   const void* kb = (const void*)((const char*)a.k + b * a.k_sb * key_elem_bytes<KT>());
   const int n_pairs = (a.K_b + 1) / 2;
-  int pr = ((int)blockIdx.x * WAVES + wave) * a.pairs_per_wave;
-  const int pr_end = min(pr + a.pairs_per_wave, n_pairs);
+  const int pr0 = ((int)blockIdx.x * WAVES + wave) * a.pairs_per_wave;
+  const int pr_end = min(pr0 + a.pairs_per_wave, n_pairs);
   const int32_t* brow = a.blocks + r * a.K_b;
 
-  KT cur, nxt;
-  auto fetch = [&](int pair, KT& K, int64_t& key, bool& ok) {
-    const int j = 2 * pair + (kl >> 3);
-    const int32_t blk = j < a.K_b ? brow[j] : -1;
-    key = (int64_t)blk * BLK + (kl & 7);
-    ok = blk >= 0 && key < nv;
-    if (ok)
-      load_key(kb, key, g, K);
-    else
-      zero_key(K);
-  };
-  if (pr >= pr_end) return;
-  int64_t key_cur, key_nxt = -1;
-  bool ok_cur, ok_nxt = false;
-  fetch(pr, cur, key_cur, ok_cur);
-  for (; pr < pr_end; ++pr) {
-    if (pr + 1 < pr_end) fetch(pr + 1, nxt, key_nxt, ok_nxt);
-    float s = tile_score(Q, cur);
-    const int j = 2 * pr + (kl >> 3);
-    if (g == 0 && j < a.K_b) {
-      const int64_t col = r * a.s_stride + (int64_t)j * BLK + (kl & 7);
-      a.scores[col] = ok_cur ? s : -INFINITY;
-      a.ids[col] = ok_cur ? (int32_t)key_cur : -1;
+  for (int pb = pr0; pb < pr_end; pb += CB) {
+    int64_t key[CB];
+    bool ok[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const int j = 2 * (pb + u) + (kl >> 3);
+      const int32_t blk = (pb + u < pr_end && j < a.K_b) ? brow[j] : -1;
+      key[u] = (int64_t)blk * BLK + (kl & 7);
+      ok[u] = blk >= 0 && key[u] < nv;
     }
-    cur = nxt;
-    key_cur = key_nxt;
-    ok_cur = ok_nxt;
+    KT K[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (ok[u])
+        load_key(kb, key[u], g, K[u]);
+      else
+        zero_key(K[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (pb + u >= pr_end) break;  // uniform
+      const float s = tile_score(Q, K[u]);
+      const int j = 2 * (pb + u) + (kl >> 3);
+      if (g == 0 && j < a.K_b) {
+        const int64_t col = r * a.s_stride + (int64_t)j * BLK + (kl & 7);
+        a.scores[col] = ok[u] ? s : -INFINITY;
+        a.ids[col] = ok[u] ? (int32_t)key[u] : -1;
+      }
+    }
   }
 }
 
@@ -394,8 +402,10 @@ hipError_t launch_index_cand(int B, int Tq, const void* q, const float* w, const
              scores, ids, s_stride, 1};
   const int64_t R = (int64_t)B * Tq;
   const int n_pairs = (K_b + 1) / 2;
+  // ~4096 waves over the chip, each taking whole batches of 4 tiles
   int64_t ppw = (n_pairs * R + 4095) / 4096;
-  if (ppw < 1) ppw = 1;
+  ppw = (ppw + 3) / 4 * 4;
+  if (ppw < 4) ppw = 4;
   if (ppw > 16) ppw = 16;
   a.pairs_per_wave = (int)ppw;
   const int64_t per_block = ppw * WAVES;

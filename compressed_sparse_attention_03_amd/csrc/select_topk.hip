@@ -79,9 +79,10 @@ struct Shared {
   uint32_t bcast[8];
 };
 
-// exclusive block scan of one uint32 per thread
+// exclusive block scan of one uint32 per thread (any block size <= 1024)
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = (int)(blockDim.x >> 6);
   uint32_t x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -91,7 +92,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh,
   if (lane == 63) sh.scan[wave] = x;
   __syncthreads();
   uint32_t wpre = 0, tot = 0;
-  for (int i = 0; i < NWAVES; ++i) {
+  for (int i = 0; i < nw; ++i) {
     const uint32_t t = sh.scan[i];
     if (i < wave) wpre += t;
     tot += t;
@@ -275,16 +276,8 @@ constexpr int NBIN = 1024;            // sample histogram bins
 constexpr int CAND_CAP = 8192;        // candidate list capacity per row
 constexpr int CAND_PT = CAND_CAP / THREADS;
 constexpr int KFAST = 2048;           // largest k of the sampled paths
-constexpr int64_t MAX_N_FAST = 1 << 18;  // longest row of the sampled paths (bitmap)
-
-// Per-row state of the split path (lives in the caller's workspace).
-struct RowState {
-  uint32_t A, Bt;          // in: key > A; candidate: Bt <= key <= A
-  int32_t fcol;            // forced column known before the pass (force_last)
-  int32_t fcol_found;      // forced column found during the pass (forced id)
-  uint32_t n_in, n_cand;
-  uint32_t pad[10];
-};
+constexpr int64_t MAX_N_FAST = 1 << 17;  // longest row of the sampled paths (bitmaps)
+constexpr int KBIN = 2048;               // radix digit bins of the candidate select
 
 struct SampleSmem {
   uint32_t hist[NBIN];
@@ -292,8 +285,9 @@ struct SampleSmem {
 };
 
 struct FinishSmem {
-  uint32_t bitmap[MAX_N_FAST / 32];
-  uint32_t hist[256];
+  uint32_t bitmap[MAX_N_FAST / 32];  // chosen columns
+  uint32_t tiemap[MAX_N_FAST / 32];  // columns tied at the threshold key
+  uint32_t hist[KBIN];
   uint32_t bc[4];
 };
 
@@ -316,11 +310,12 @@ __device__ __forceinline__ void wave_append(bool flag, T value, T* list, uint32_
 }
 
 // Column of the last valid entry of the row (-1 if none), scanning back
-// from the end one block-wide chunk at a time.  1024 threads.
+// from the end one block-wide chunk at a time.  Any block size <= 1024.
 __device__ int32_t last_valid_column(const SelArgs& a, int64_t row, Shared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nt = (int)blockDim.x, nw = nt >> 6;
   const int64_t n = a.n;
-  for (int64_t base = ((n - 1) / THREADS) * THREADS; base >= 0; base -= THREADS) {
+  for (int64_t base = ((n - 1) / nt) * nt; base >= 0; base -= nt) {
     const int64_t j = base + tid;
     const bool v = j < n && load_elem(a, row, j).key != 0;
     const uint64_t m = __ballot(v);
@@ -328,12 +323,24 @@ __device__ int32_t last_valid_column(const SelArgs& a, int64_t row, Shared& sh) 
       sh.wred[wave] = m ? (uint32_t)(64 * wave + 63 - __clzll((unsigned long long)m)) : 0xffffffffu;
     __syncthreads();
     int32_t best = -1;
-    for (int i = 0; i < NWAVES; ++i)
+    for (int i = 0; i < nw; ++i)
       if (sh.wred[i] != 0xffffffffu) best = max(best, (int32_t)(base + sh.wred[i]));
     __syncthreads();
     if (best >= 0) return best;
   }
   return -1;
+}
+
+// The SAMPLE sampled entries of a row, SAMPLE / NT per thread (thread t
+// holds samples t, t + NT, ...).
+template <int NT>
+__device__ __forceinline__ void load_sample(const SelArgs& a, int64_t row, Elem (&e)[SAMPLE / NT],
+                                            int64_t (&j)[SAMPLE / NT]) {
+#pragma unroll
+  for (int i = 0; i < SAMPLE / NT; ++i) {
+    j[i] = (int64_t)(threadIdx.x + i * NT) * a.n / SAMPLE;
+    e[i] = load_elem(a, row, j[i]);
+  }
 }
 
 // Bracket [Bt, A] around the k-th key of the row from SAMPLE keys spread
@@ -342,25 +349,27 @@ __device__ int32_t last_valid_column(const SelArgs& a, int64_t row, Shared& sh) 
 // r -/+ delta (r = expected rank of the k-th key, delta = 4 sqrt(r) + 16); the
 // bracket is made of whole bins, so it is approximate by design -- the exact
 // answer comes later and a bracket that misses is detected and handled.
-// 1024 threads.
-__device__ void sample_bracket(const SelArgs& a, int64_t row, int32_t fcol, int32_t fid,
-                               SampleSmem& ss, Shared& sh, uint32_t* A, uint32_t* Bt) {
+// Block of NT threads; the result depends only on the row, not on NT.
+template <int NT>
+__device__ void bracket_from_sample(const SelArgs& a, const Elem (&e)[SAMPLE / NT],
+                                    const int64_t (&js)[SAMPLE / NT], int32_t fcol, int32_t fid,
+                                    SampleSmem& ss, Shared& sh, uint32_t* A, uint32_t* Bt) {
+  constexpr int SPT = SAMPLE / NT;  // samples per thread
+  constexpr int BPT = NBIN / NT;    // histogram bins per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = a.n;
-  uint32_t v[SAMPLE / THREADS];
+  uint32_t v[SPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-  for (int i = 0; i < SAMPLE / THREADS; ++i) {
-    const int64_t j = (int64_t)(tid + i * THREADS) * n / SAMPLE;
-    const Elem e = load_elem(a, row, j);
-    const bool forced = (j == fcol) || (fid >= 0 && e.id == fid);
-    v[i] = forced ? 0u : e.key;
+  for (int i = 0; i < SPT; ++i) {
+    const bool forced = (js[i] == fcol) || (fid >= 0 && e[i].id == fid);
+    v[i] = forced ? 0u : e[i].key;
     if (v[i]) {
       kmin = min(kmin, v[i]);
       kmax = max(kmax, v[i]);
     }
   }
-  for (int i = tid; i < NBIN; i += THREADS) ss.hist[i] = 0;
+  for (int i = tid; i < NBIN; i += NT) ss.hist[i] = 0;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
@@ -373,7 +382,7 @@ __device__ void sample_bracket(const SelArgs& a, int64_t row, int32_t fcol, int3
   __syncthreads();
   kmin = 0xffffffffu;
   kmax = 0u;
-  for (int i = 0; i < NWAVES; ++i) {
+  for (int i = 0; i < NT / 64; ++i) {
     kmin = min(kmin, sh.wred[i * 4 + 1]);
     kmax = max(kmax, sh.wred[i * 4 + 2]);
   }
@@ -391,22 +400,32 @@ __device__ void sample_bracket(const SelArgs& a, int64_t row, int32_t fcol, int3
   const uint32_t range = kmax - kmin;
   const int w = range < (uint32_t)NBIN ? 0 : (32 - __clz(range)) - 10;  // range >> w < NBIN
 #pragma unroll
-  for (int i = 0; i < SAMPLE / THREADS; ++i)
+  for (int i = 0; i < SPT; ++i)
     if (v[i]) atomicAdd(&ss.hist[(v[i] - kmin) >> w], 1u);
   if (tid == 0) {
     ss.b1 = 0xffffffffu;
     ss.b2 = 0xffffffffu;
   }
   __syncthreads();
-  // thread t owns bin NBIN-1-t: an exclusive prefix over t counts the
-  // samples in higher bins
-  const int bin = NBIN - 1 - tid;
-  const uint32_t cnt = tid < NBIN ? ss.hist[bin] : 0u;
+  // thread t owns bins NBIN-1-t*BPT-i (i < BPT), highest first: an exclusive
+  // prefix over t counts the samples in higher bins
+  uint32_t c[BPT];
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    c[i] = ss.hist[NBIN - 1 - tid * BPT - i];
+    cnt += c[i];
+  }
   uint32_t tot;
-  const uint32_t above = block_exclusive_scan(cnt, sh, &tot);
-  if (tid < NBIN && cnt) {
-    if (r_hi >= 0 && above <= (uint32_t)r_hi && (uint32_t)r_hi < above + cnt) ss.b1 = bin;
-    if (above <= (uint32_t)r_lo && (uint32_t)r_lo < above + cnt) ss.b2 = bin;
+  uint32_t above = block_exclusive_scan(cnt, sh, &tot);
+#pragma unroll
+  for (int i = 0; i < BPT; ++i) {
+    const uint32_t bin = NBIN - 1 - tid * BPT - i;
+    if (c[i]) {
+      if (r_hi >= 0 && above <= (uint32_t)r_hi && (uint32_t)r_hi < above + c[i]) ss.b1 = bin;
+      if (above <= (uint32_t)r_lo && (uint32_t)r_lo < above + c[i]) ss.b2 = bin;
+    }
+    above += c[i];
   }
   __syncthreads();
   const uint32_t b1 = ss.b1, b2 = ss.b2;
@@ -419,6 +438,16 @@ __device__ void sample_bracket(const SelArgs& a, int64_t row, int32_t fcol, int3
   }
   *Bt = (b2 == 0xffffffffu) ? 1u : max(1u, kmin + (b2 << w));
   __syncthreads();
+}
+
+// Bracket [Bt, A] around the k-th key of the row (see bracket_from_sample).
+template <int NT>
+__device__ void sample_bracket(const SelArgs& a, int64_t row, int32_t fcol, int32_t fid,
+                               SampleSmem& ss, Shared& sh, uint32_t* A, uint32_t* Bt) {
+  Elem e[SAMPLE / NT];
+  int64_t js[SAMPLE / NT];
+  load_sample<NT>(a, row, e, js);
+  bracket_from_sample<NT>(a, e, js, fcol, fid, ss, sh, A, Bt);
 }
 
 // Classify entries [j0, j1) of a row (stride = blockDim.x) into the in and
@@ -460,134 +489,171 @@ __device__ void classify_range(const SelArgs& a, int64_t row, int64_t j0, int64_
   }
 }
 
-// k-th largest (k >= 1) of the distinct nonzero uint64 values held by the
-// block (CAND_PT per thread): radix select, 8 bits per pass below the bits
-// all values share.  A pass whose chosen digit bin holds exactly the number
-// still wanted ends the search early.  Result: v is among the k largest iff
-// (v >> *lo) >= (*T >> *lo).  1024 threads.
-__device__ void kth_largest_u64(const uint64_t (&v)[CAND_PT], uint32_t k, FinishSmem& fs,
-                                Shared& sh, uint64_t* T, int* lo_out) {
+// Threshold on the candidate KEYS (high half of each composite) such that
+// the m best candidates are: every key above it, plus -- when the threshold
+// key itself is shared by more candidates than still wanted -- the `need`
+// smallest columns among those tied at it.  Bits that every candidate key
+// has in common are skipped (integer-valued scores leave the low mantissa
+// bits constant), then 11-bit radix digits from the top; a digit bin that
+// holds exactly the number still wanted ends the search.  In the result,
+// with u = key >> tz:  chosen  iff (u >> lo) > (U >> lo), or (u >> lo) ==
+// (U >> lo) and (take_all, or among the first `need` such columns).
+// 1024 threads.
+struct KeyThreshold {
+  uint32_t U;
+  int lo, tz;
+  bool take_all;
+  uint32_t need;
+};
+
+__device__ KeyThreshold key_threshold(const uint64_t (&v)[CAND_PT], uint32_t m, FinishSmem& fs,
+                                      Shared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t vmin = ~0ull, vmax = 0ull;
+  uint32_t kand = 0xffffffffu, kor = 0u;
 #pragma unroll
   for (int i = 0; i < CAND_PT; ++i)
     if (v[i]) {
-      vmin = v[i] < vmin ? v[i] : vmin;
-      vmax = v[i] > vmax ? v[i] : vmax;
+      const uint32_t k = (uint32_t)(v[i] >> 32);
+      kand &= k;
+      kor |= k;
     }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t a = __shfl_xor(vmin, o, 64), b = __shfl_xor(vmax, o, 64);
-    vmin = a < vmin ? a : vmin;
-    vmax = b > vmax ? b : vmax;
+    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
+    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
   }
-  __shared__ uint64_t red[2 * NWAVES];
   if (lane == 0) {
-    red[wave] = vmin;
-    red[NWAVES + wave] = vmax;
+    sh.wred[wave * 4 + 0] = kand;
+    sh.wred[wave * 4 + 1] = kor;
   }
   __syncthreads();
-  vmin = ~0ull;
-  vmax = 0ull;
+  kand = 0xffffffffu;
+  kor = 0u;
   for (int i = 0; i < NWAVES; ++i) {
-    vmin = red[i] < vmin ? red[i] : vmin;
-    vmax = red[NWAVES + i] > vmax ? red[NWAVES + i] : vmax;
+    kand &= sh.wred[i * 4 + 0];
+    kor |= sh.wred[i * 4 + 1];
   }
-  int hi = vmin == vmax ? 0 : 64 - __clzll((unsigned long long)(vmin ^ vmax));
-  uint64_t prefix = hi >= 64 ? 0ull : (vmax & ~((1ull << hi) - 1ull));
-  uint32_t remaining = k;
+  __syncthreads();
+  KeyThreshold th;
+  const uint32_t varying = kand ^ kor;  // bits that differ between some keys
+  th.tz = varying ? __ffs(varying) - 1 : 0;
+  int hi = varying ? 32 - __clz(varying >> th.tz) : 0;  // u = key >> tz differ below hi
+  uint32_t prefix = (kor >> th.tz) & ~(hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u));
+  uint32_t remaining = m, cbin = 0;
+  th.take_all = false;
+  th.lo = 0;
+  // count of candidates sharing every key bit (all keys equal)
+  if (hi == 0) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < CAND_PT; ++i) c += v[i] != 0;
+    uint32_t tot;
+    block_exclusive_scan(c, sh, &tot);
+    cbin = tot;
+  }
   while (hi > 0) {
-    const int lo = hi > 8 ? hi - 8 : 0;
+    const int lo = hi > 11 ? hi - 11 : 0;
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    for (int i = tid; i < 256; i += THREADS) fs.hist[i] = 0;
+    for (int i = tid; i < KBIN; i += THREADS) fs.hist[i] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < CAND_PT; ++i) {
-      const bool match = v[i] && (hi >= 64 || (v[i] >> hi) == (prefix >> hi));
-      if (match) atomicAdd(&fs.hist[(uint32_t)(v[i] >> lo) & dmask], 1u);
+      if (!v[i]) continue;
+      const uint32_t u = (uint32_t)(v[i] >> 32) >> th.tz;
+      if (hi >= 32 || (u >> hi) == (prefix >> hi)) atomicAdd(&fs.hist[(u >> lo) & dmask], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      uint32_t c[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = fs.hist[4 * lane + i];
-      const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-      uint32_t suf = tot;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += y;
-      }
-      const uint32_t above = suf - tot;
-      if (above < remaining && remaining <= suf) {
-        uint32_t acc = above;
-        for (int i = 3; i >= 0; --i) {
-          if (acc + c[i] >= remaining) {
-            fs.bc[0] = 4u * lane + i;
-            fs.bc[1] = acc;
-            fs.bc[2] = c[i];
-            break;
-          }
-          acc += c[i];
-        }
-      }
+    // thread t owns bins 2047-2t and 2046-2t (highest first)
+    const uint32_t c0 = fs.hist[KBIN - 1 - 2 * tid], c1 = fs.hist[KBIN - 2 - 2 * tid];
+    uint32_t tot;
+    const uint32_t above = block_exclusive_scan(c0 + c1, sh, &tot);
+    if (above < remaining && remaining <= above + c0) {
+      fs.bc[0] = KBIN - 1 - 2 * tid;
+      fs.bc[1] = above;
+      fs.bc[2] = c0;
+    } else if (above + c0 < remaining && remaining <= above + c0 + c1) {
+      fs.bc[0] = KBIN - 2 - 2 * tid;
+      fs.bc[1] = above + c0;
+      fs.bc[2] = c1;
     }
     __syncthreads();
-    const uint32_t dsel = fs.bc[0], cabove = fs.bc[1], cbin = fs.bc[2];
-    __syncthreads();
-    remaining -= cabove;
-    prefix |= (uint64_t)dsel << lo;
+    const uint32_t dsel = fs.bc[0];
+    remaining -= fs.bc[1];
+    cbin = fs.bc[2];
+    prefix |= dsel << lo;
     hi = lo;
-    if (remaining == cbin) break;  // the whole bin is wanted
+    th.lo = lo;
+    __syncthreads();
+    if (remaining == cbin) break;
   }
-  *T = prefix;
-  *lo_out = hi;
+  th.U = prefix;
+  th.take_all = remaining == cbin;
+  th.need = remaining;
+  return th;
 }
 
-// From the in list and the candidate list to the k ids, ascending.  Returns
-// false (nothing written) when the bracket did not hold.  The chosen
-// columns are marked in an LDS bitmap and read back in column order.
-// 1024 threads.
-__device__ bool finish_from_lists(const SelArgs& a, int64_t row, int32_t fcol, uint32_t n_in,
-                                  uint32_t n_cand, const int32_t* in_list,
-                                  const uint64_t* cand_src, FinishSmem& fs, Shared& sh) {
+// From the "in" columns and the candidate composites (held in registers,
+// CAND_PT per thread, 0 = empty) to the k ids, ascending.  The chosen
+// columns are marked in an LDS bitmap, candidates tied at the threshold key
+// in a second one, and both are read back in column order, keeping the
+// first `need` tied columns.  The caller has checked the bracket
+// (n_in + m == k_rem, n_cand <= CAND_CAP).  1024 threads.
+__device__ void finish_core(const SelArgs& a, int64_t row, int32_t fcol, uint32_t n_in,
+                            const int32_t* in_list, uint32_t m, const uint64_t (&v)[CAND_PT],
+                            FinishSmem& fs, Shared& sh) {
   const int tid = threadIdx.x;
-  const int have_forced = fcol >= 0 ? 1 : 0;
-  const uint32_t k_rem = (uint32_t)(a.k - have_forced);
-  if (n_in > k_rem || n_in + n_cand < k_rem || n_cand > CAND_CAP || a.n > MAX_N_FAST) return false;
-  const uint32_t m = k_rem - n_in;
-  uint64_t v[CAND_PT];
-#pragma unroll
-  for (int i = 0; i < CAND_PT; ++i) {
-    const uint32_t idx = tid + i * THREADS;
-    v[i] = idx < n_cand ? cand_src[idx] : 0ull;
-  }
-  uint64_t T = ~0ull;
-  int lo = 0;
-  if (m > 0) kth_largest_u64(v, m, fs, sh, &T, &lo);
+  KeyThreshold th{0u, 0, 0, true, 0u};
+  if (m > 0) th = key_threshold(v, m, fs, sh);
   const int64_t n = a.n;
   const int words = (int)((n + 31) / 32);
-  for (int i = tid; i < words; i += THREADS) fs.bitmap[i] = 0u;
+  for (int i = tid; i < words; i += THREADS) {
+    fs.bitmap[i] = 0u;
+    fs.tiemap[i] = 0u;
+  }
   __syncthreads();
   for (uint32_t i = tid; i < n_in; i += THREADS) {
     const uint32_t c = (uint32_t)in_list[i];
     atomicOr(&fs.bitmap[c >> 5], 1u << (c & 31));
   }
   if (m > 0) {
+    const uint32_t Ulo = th.U >> th.lo;
 #pragma unroll
-    for (int i = 0; i < CAND_PT; ++i)
-      if (v[i] && (v[i] >> lo) >= (T >> lo)) {
-        const uint32_t c = 0xffffffffu - (uint32_t)(v[i] & 0xffffffffull);
+    for (int i = 0; i < CAND_PT; ++i) {
+      if (!v[i]) continue;
+      const uint32_t u = ((uint32_t)(v[i] >> 32) >> th.tz) >> th.lo;
+      const uint32_t c = 0xffffffffu - (uint32_t)(v[i] & 0xffffffffull);
+      if (u > Ulo || (u == Ulo && th.take_all))
         atomicOr(&fs.bitmap[c >> 5], 1u << (c & 31));
-      }
+      else if (u == Ulo)
+        atomicOr(&fs.tiemap[c >> 5], 1u << (c & 31));
+    }
   }
-  if (tid == 0 && have_forced) atomicOr(&fs.bitmap[fcol >> 5], 1u << (fcol & 31));
+  if (tid == 0 && fcol >= 0) atomicOr(&fs.bitmap[fcol >> 5], 1u << (fcol & 31));
   __syncthreads();
   // ordered read-back: thread t owns a contiguous run of words
   const int wpt = (words + THREADS - 1) / THREADS;
   const int w0 = tid * wpt, w1 = min(words, w0 + wpt);
+  uint32_t nt = 0;
+  if (!th.take_all)
+    for (int wi = w0; wi < w1; ++wi) nt += __popc(fs.tiemap[wi]);
+  uint32_t tot_t = 0;
+  uint32_t tie_rank = th.take_all ? 0u : block_exclusive_scan(nt, sh, &tot_t);
+  // keep the ties with rank < need: fold them into the chosen bitmap words
   uint32_t cnt = 0;
-  for (int wi = w0; wi < w1; ++wi) cnt += __popc(fs.bitmap[wi]);
+  for (int wi = w0; wi < w1; ++wi) {
+    uint32_t word = fs.bitmap[wi];
+    if (!th.take_all) {
+      uint32_t tb = fs.tiemap[wi];
+      while (tb) {
+        const uint32_t bit = tb & (0u - tb);
+        tb &= tb - 1u;
+        if (tie_rank < th.need) word |= bit;
+        ++tie_rank;
+      }
+      fs.bitmap[wi] = word;
+    }
+    cnt += __popc(word);
+  }
   uint32_t total;
   uint32_t pos = block_exclusive_scan(cnt, sh, &total);
   int32_t* orow = a.out + row * a.o_stride;
@@ -602,6 +668,23 @@ __device__ bool finish_from_lists(const SelArgs& a, int64_t row, int32_t fcol, u
     }
   }
   for (int i = (int)total + tid; i < a.k; i += THREADS) orow[i] = -1;
+}
+
+// Lists in one place (LDS): check the bracket, then finish.  Returns false
+// (nothing written) when the bracket did not hold.
+__device__ bool finish_from_lists(const SelArgs& a, int64_t row, int32_t fcol, uint32_t n_in,
+                                  uint32_t n_cand, const int32_t* in_list,
+                                  const uint64_t* cand_src, FinishSmem& fs, Shared& sh) {
+  const int tid = threadIdx.x;
+  const uint32_t k_rem = (uint32_t)(a.k - (fcol >= 0 ? 1 : 0));
+  if (n_in > k_rem || n_in + n_cand < k_rem || n_cand > CAND_CAP || a.n > MAX_N_FAST) return false;
+  uint64_t v[CAND_PT];
+#pragma unroll
+  for (int i = 0; i < CAND_PT; ++i) {
+    const uint32_t idx = tid + i * THREADS;
+    v[i] = idx < n_cand ? cand_src[idx] : 0ull;
+  }
+  finish_core(a, row, fcol, n_in, in_list, k_rem - n_in, v, fs, sh);
   return true;
 }
 
@@ -628,7 +711,7 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(SelArgs a, int try
       sm.n_cand = 0;
       sm.fcol_found = 0x7fffffff;
     }
-    sample_bracket(a, row, fcol, fid, sm.ss, sm.sh, &A, &Bt);
+    sample_bracket<THREADS>(a, row, fcol, fid, sm.ss, sm.sh, &A, &Bt);
     classify_range(a, row, 0, a.n, A, Bt, fcol, fid, sm.in_list, &sm.n_in, KFAST, sm.cand,
                    &sm.n_cand, CAND_CAP, &sm.fcol_found);
     __syncthreads();
@@ -641,82 +724,165 @@ __global__ __launch_bounds__(THREADS) void select_topk_kernel(SelArgs a, int try
 }
 
 // ---- few rows: the pass over the row is split over many workgroups ----------
-// K0: forced column, sample, bracket; resets the row's counters.
-__global__ __launch_bounds__(THREADS) void select_bracket_kernel(SelArgs a, RowState* st) {
-  __shared__ Shared sh;
-  __shared__ SampleSmem ss;
-  const int64_t row = blockIdx.x;
-  const int32_t fid = a.forced ? a.forced[row] : -1;
-  const int32_t fcol = a.force_last ? last_valid_column(a, row, sh) : -1;
-  uint32_t A, Bt;
-  sample_bracket(a, row, fcol, fid, ss, sh, &A, &Bt);
-  if (threadIdx.x == 0) {
-    RowState& s = st[row];
-    s.A = A;
-    s.Bt = Bt;
-    s.fcol = fcol;
-    s.fcol_found = 0x7fffffff;
-    s.n_in = 0;
-    s.n_cand = 0;
-  }
-}
-
-// K1: grid (chunks, rows), 256 threads, CHUNK entries per workgroup.  The
-// workgroup collects its in / candidate entries in LDS, then reserves room
-// in the row's global lists with one atomic per list and copies them out.
+// K1 (grid chunks x rows, 256 threads): every block recomputes the row's
+// forced column and bracket from the same sample -- identical integer work,
+// so all blocks of a row agree -- and classifies its CHUNK entries straight
+// into its own slot (no atomics across blocks).  K2 (one 1024-thread block
+// per row) gathers the slots and finishes.
 constexpr int CLS_THREADS = 256;
 constexpr int CHUNK = 2048;
+constexpr int SLOT = 512;  // per-chunk capacity of each list
+constexpr int MAX_CHUNKS = (int)(MAX_N_FAST / CHUNK);
 
-__global__ __launch_bounds__(CLS_THREADS) void select_classify_kernel(SelArgs a, RowState* st,
-                                                                      int32_t* in_lists,
-                                                                      uint64_t* cand_lists) {
-  __shared__ int32_t l_in[CHUNK];
-  __shared__ uint64_t l_cand[CHUNK];
-  __shared__ uint32_t l_n_in, l_n_cand, g_in, g_cand;
+struct Slot {
+  uint32_t n_in, n_cand;  // may exceed SLOT: the slot then overflowed
+  int32_t fcol;           // forced column known before the pass (force_last)
+  int32_t fcol_found;     // forced column found in this chunk (forced id)
+  uint32_t pad[4];
+  int32_t in[SLOT];
+  uint64_t cand[SLOT];
+};
+
+__global__ __launch_bounds__(CLS_THREADS) void select_classify_kernel(SelArgs a, Slot* slots,
+                                                                      int nchunks) {
+  constexpr int CPT = CHUNK / CLS_THREADS;  // chunk entries per thread
+  __shared__ Shared sh;
+  __shared__ SampleSmem ss;
+  __shared__ uint32_t l_n_in, l_n_cand;
   __shared__ int32_t l_fcol;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.y;
-  const int64_t j0 = (int64_t)blockIdx.x * CHUNK;
-  const int64_t j1 = min(a.n, j0 + CHUNK);
-  RowState& s = st[row];
+  const int chunk = blockIdx.x;
+  const int64_t n = a.n;
+  const int64_t j0 = (int64_t)chunk * CHUNK;
+  const int64_t j1 = min(n, j0 + CHUNK);
   const int32_t fid = a.forced ? a.forced[row] : -1;
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     l_n_in = 0;
     l_n_cand = 0;
     l_fcol = 0x7fffffff;
   }
-  __syncthreads();
-  classify_range(a, row, j0, j1, s.A, s.Bt, s.fcol, fid, l_in, &l_n_in, CHUNK, l_cand, &l_n_cand,
-                 CHUNK, &l_fcol);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    g_in = l_n_in ? atomicAdd(&s.n_in, l_n_in) : 0u;
-    g_cand = l_n_cand ? atomicAdd(&s.n_cand, l_n_cand) : 0u;
-    if (l_fcol != 0x7fffffff) atomicMin(&s.fcol_found, l_fcol);
+  // every load of the block is issued before any of them is used: this
+  // chunk, the row sample and the row's last CLS_THREADS entries
+  Elem ce[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int64_t j = j0 + u * CLS_THREADS + tid;
+    ce[u].key = 0;
+    ce[u].id = -1;
+    if (j < j1) ce[u] = load_elem(a, row, j);
+  }
+  Elem se[SAMPLE / CLS_THREADS];
+  int64_t sj[SAMPLE / CLS_THREADS];
+  load_sample<CLS_THREADS>(a, row, se, sj);
+  const int64_t tail0 = ((n - 1) / CLS_THREADS) * CLS_THREADS;
+  const bool tail_valid = a.force_last && tail0 + tid < n && load_elem(a, row, tail0 + tid).key != 0;
+  int32_t fcol = -1;
+  if (a.force_last) {
+    const uint64_t m = __ballot(tail_valid);
+    if (lane == 0)
+      sh.wred[wave] = m ? (uint32_t)(64 * wave + 63 - __clzll((unsigned long long)m)) : 0xffffffffu;
+    __syncthreads();
+    for (int i = 0; i < CLS_THREADS / 64; ++i)
+      if (sh.wred[i] != 0xffffffffu) fcol = max(fcol, (int32_t)(tail0 + sh.wred[i]));
+    __syncthreads();
+    if (fcol < 0) fcol = last_valid_column(a, row, sh);  // the row ends in invalid entries
+  }
+  uint32_t A, Bt;
+  bracket_from_sample<CLS_THREADS>(a, se, sj, fcol, fid, ss, sh, &A, &Bt);
+  Slot& sl = slots[row * nchunks + chunk];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int64_t j = j0 + u * CLS_THREADS + tid;
+    uint32_t key = ce[u].key;
+    if (j < j1) {
+      if (j == fcol) {
+        key = 0;
+      } else if (fid >= 0 && ce[u].id == fid && key != 0) {
+        atomicMin(&l_fcol, (int32_t)j);
+        key = 0;
+      }
+    }
+    const bool isin = key > A;
+    const bool iscand = !isin && key >= Bt && key != 0;
+    wave_append<int32_t>(isin, (int32_t)j, sl.in, &l_n_in, SLOT);
+    wave_append<uint64_t>(iscand, ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - (uint32_t)j),
+                          sl.cand, &l_n_cand, SLOT);
   }
   __syncthreads();
-  int32_t* gin = in_lists + row * KFAST;
-  uint64_t* gcand = cand_lists + row * CAND_CAP;
-  for (uint32_t i = threadIdx.x; i < l_n_in; i += CLS_THREADS)
-    if (g_in + i < KFAST) gin[g_in + i] = l_in[i];
-  for (uint32_t i = threadIdx.x; i < l_n_cand; i += CLS_THREADS)
-    if (g_cand + i < CAND_CAP) gcand[g_cand + i] = l_cand[i];
+  if (tid == 0) {
+    sl.n_in = l_n_in;
+    sl.n_cand = l_n_cand;
+    sl.fcol = fcol;
+    sl.fcol_found = l_fcol;
+  }
 }
 
-// K2: exact order among the candidates and the ascending id list.
-__global__ __launch_bounds__(THREADS) void select_finish_kernel(SelArgs a, const RowState* st,
-                                                                const int32_t* in_lists,
-                                                                const uint64_t* cand_lists) {
+__global__ __launch_bounds__(THREADS) void select_finish_kernel(SelArgs a, const Slot* slots,
+                                                                int nchunks) {
   __shared__ FinishSmem fs;
   __shared__ Shared sh;
+  __shared__ uint32_t p_in[MAX_CHUNKS + 1], p_cand[MAX_CHUNKS + 1];
+  __shared__ int32_t in_flat[KFAST];
+  __shared__ int32_t s_ff;
+  const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
-  const RowState& s = st[row];
-  int32_t fcol = s.fcol;
-  if (a.forced) fcol = s.fcol_found == 0x7fffffff ? -1 : s.fcol_found;
-  if (finish_from_lists(a, row, fcol, s.n_in, s.n_cand, in_lists + row * KFAST,
-                        cand_lists + row * CAND_CAP, fs, sh))
+  const Slot* sr = slots + row * nchunks;
+  uint32_t ni = 0, nc = 0;
+  int over = 0;
+  if (tid == 0) s_ff = 0x7fffffff;
+  if (tid < nchunks) {
+    ni = sr[tid].n_in;
+    nc = sr[tid].n_cand;
+    over = (ni > SLOT || nc > SLOT) ? 1 : 0;
+  }
+  uint32_t tot_in, tot_cand;
+  const uint32_t b_in = block_exclusive_scan(ni, sh, &tot_in);
+  const uint32_t b_cand = block_exclusive_scan(nc, sh, &tot_cand);
+  if (tid < nchunks) {
+    p_in[tid] = b_in;
+    p_cand[tid] = b_cand;
+    if (a.forced) atomicMin(&s_ff, sr[tid].fcol_found);
+  }
+  if (tid == 0) {
+    p_in[nchunks] = tot_in;
+    p_cand[nchunks] = tot_cand;
+  }
+  const int any_over = __syncthreads_or(over);
+  int32_t fcol = a.force_last ? sr[0].fcol : -1;
+  if (a.forced) fcol = s_ff == 0x7fffffff ? -1 : s_ff;
+  const uint32_t k_rem = (uint32_t)(a.k - (fcol >= 0 ? 1 : 0));
+  if (any_over || tot_in > k_rem || tot_in + tot_cand < k_rem || tot_cand > CAND_CAP) {
+    radix_select_row(a, row, sh);
     return;
+  }
+  // chunk holding flat entry i of a list with prefix array p (last chunk
+  // whose prefix is <= i; chunk counts may be 0)
+  auto chunk_of = [&](const uint32_t* p, uint32_t i) {
+    int lo = 0, hi = nchunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (uint32_t i = tid; i < tot_in; i += THREADS) {
+    const int c = chunk_of(p_in, i);
+    in_flat[i] = sr[c].in[i - p_in[c]];
+  }
+  uint64_t v[CAND_PT];
+#pragma unroll
+  for (int q = 0; q < CAND_PT; ++q) {
+    const uint32_t i = tid + q * THREADS;
+    v[q] = 0ull;
+    if (i < tot_cand) {
+      const int c = chunk_of(p_cand, i);
+      v[q] = sr[c].cand[i - p_cand[c]];
+    }
+  }
   __syncthreads();
-  radix_select_row(a, row, sh);
+  finish_core(a, row, fcol, tot_in, in_flat, k_rem - tot_in, v, fs, sh);
 }
 
 bool sampled_ok(int64_t n, int k) { return n >= 4 * SAMPLE && n <= MAX_N_FAST && k <= KFAST; }
@@ -726,7 +892,8 @@ bool split_path(int64_t R, int64_t n, int k) { return R < 256 && sampled_ok(n, k
 
 size_t select_workspace_bytes(int64_t R, int64_t n, int64_t k) {
   if (!split_path(R, n, (int)k)) return 0;
-  return (size_t)R * (sizeof(RowState) + KFAST * sizeof(int32_t) + CAND_CAP * sizeof(uint64_t));
+  const int64_t nchunks = (n + CHUNK - 1) / CHUNK;
+  return (size_t)(R * nchunks) * sizeof(Slot);
 }
 
 hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_stride,
@@ -735,14 +902,12 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
                               hipStream_t s) {
   SelArgs a{scores, s_stride, ids, id_stride, forced, force_last, n, k, out, o_stride};
   if (split_path(R, n, k)) {
-    RowState* st = static_cast<RowState*>(ws);
-    int32_t* in_lists = reinterpret_cast<int32_t*>(st + R);
-    uint64_t* cand_lists = reinterpret_cast<uint64_t*>(in_lists + (int64_t)R * KFAST);
-    hipLaunchKernelGGL(select_bracket_kernel, dim3((unsigned)R), dim3(THREADS), 0, s, a, st);
-    hipLaunchKernelGGL(select_classify_kernel, dim3((unsigned)((n + CHUNK - 1) / CHUNK), (unsigned)R),
-                       dim3(CLS_THREADS), 0, s, a, st, in_lists, cand_lists);
-    hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)R), dim3(THREADS), 0, s, a, st,
-                       in_lists, cand_lists);
+    const int nchunks = (int)((n + CHUNK - 1) / CHUNK);
+    Slot* slots = static_cast<Slot*>(ws);
+    hipLaunchKernelGGL(select_classify_kernel, dim3((unsigned)nchunks, (unsigned)R),
+                       dim3(CLS_THREADS), 0, s, a, slots, nchunks);
+    hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)R), dim3(THREADS), 0, s, a, slots,
+                       nchunks);
     return hipGetLastError();
   }
   const int try_sampled = sampled_ok(n, k) ? 1 : 0;
