@@ -68,6 +68,8 @@ def prefill_indexer_flops(cfg) -> float:
 
 
 def source_hash(path):
+    if not os.path.exists(path):
+        return None
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
@@ -178,7 +180,7 @@ def main():
     q_per_s = cfg.R / (ms * 1e-3)
     scan_s = stage_ms["index_scan"] * 1e-3
     scan_gbs = sb["index_scan"] / scan_s / 1e9
-    kernel_src = os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", "index_scores.hip")
+    kernel_src = os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", "index_scan.hip")
     workload = "1m"
     traffic = stored_traffic(kernel_src, workload)
     result = {

@@ -15,7 +15,7 @@ BUILD = os.path.join(os.path.dirname(HERE), "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("CSA2_ARCH", "gfx950")
 
-SOURCES = ["compress.hip", "index_scores.hip", "select_topk.hip", "sparse_attn.hip",
+SOURCES = ["compress.hip", "index_scan.hip", "index_cand.hip", "select_topk.hip", "sparse_attn.hip",
            "dequant.hip", "csa2_api.cpp"]
 
 FLAGS = [

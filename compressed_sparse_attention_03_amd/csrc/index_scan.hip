@@ -1,0 +1,272 @@
+// index_scan.hip -- a2, the candidate-source indexer scan (NVFP4 article,
+// section 3.3): every visible latent is scored,
+//     score(p) = sum_{h < 32} w_h * max(0, q_h . k_p),
+// and the maximum over each block of 8 latents is kept (a block is
+// represented by its best in-block score).  Decode (few queries per
+// sequence): keys streamed from HBM once per query group, MFMA operands and
+// epilogue from indexer.h.  Prefill (many queries): see prefill_scan_kernel.
+#include "indexer.h"
+#include "launch.h"
+
+namespace csa2 {
+
+namespace {
+
+using namespace indexer;
+
+struct ScanArgs {
+  const uint16_t* q;
+  const float* w;
+  const void* k;
+  int64_t k_sb;
+  int64_t n_cache;
+  const int64_t* q_pos;
+  int Tq;
+  float* scores;
+  int64_t s_stride;
+  float* block_max;
+  int64_t bm_stride;
+  int tiles_per_wave;
+};
+
+// ---- scan: every latent, block max fused ------------------------------------
+template <int QPB, typename QT, typename KT>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = blockIdx.y;
+  const int j0 = blockIdx.z * QPB;
+  const int nq = min(QPB, a.Tq - j0);
+  const int g = lane >> 4, kl = lane & 15;
+  const int64_t nblk = (a.n_cache + BLK - 1) / BLK;
+
+  __shared__ __align__(16) uint8_t qstage[HI * DI];
+  QT Q[QPB];
+  int64_t nv[QPB];
+  int64_t max_nv = 0;
+#pragma unroll
+  for (int qi = 0; qi < QPB; ++qi) {
+    const int j = j0 + (qi < nq ? qi : 0);
+    const int64_t r = (int64_t)b * a.Tq + j;
+    load_query(a.q + r * (HI * DI), a.w + r * HI, Q[qi], lane, qstage);
+    nv[qi] = qi < nq ? n_visible(a.q_pos[r], a.n_cache) : 0;
+    max_nv = nv[qi] > max_nv ? nv[qi] : max_nv;
+  }
+  const void* kb = (const void*)((const char*)a.k + b * a.k_sb * key_elem_bytes<KT>());
+
+  // A block owns WAVES * tiles_per_wave consecutive tiles; its waves take
+  // them round-robin, so at any moment the block streams one contiguous
+  // stretch of keys.
+  const int64_t n_tiles = (a.n_cache + 15) / 16;
+  const int64_t blk0 = (int64_t)blockIdx.x * WAVES * a.tiles_per_wave;
+  int64_t t = blk0 + wave;
+  const int64_t t_end = min(blk0 + (int64_t)WAVES * a.tiles_per_wave, n_tiles);
+  if (t >= t_end) return;
+
+  auto fetch = [&](int64_t tile, KT& K) {
+    const int64_t row = tile * 16 + kl;
+    if (tile * 16 < max_nv)
+      load_key(kb, row < a.n_cache ? row : a.n_cache - 1, g, K);
+    else
+      zero_key(K);
+  };
+  auto process = [&](int64_t tile, const KT& K) {
+    const int64_t p = tile * 16 + kl;
+#pragma unroll
+    for (int qi = 0; qi < QPB; ++qi) {
+      if (qi >= nq) break;
+      const int64_t r = (int64_t)b * a.Tq + j0 + qi;
+      float s = -INFINITY;
+      if (tile * 16 < nv[qi]) {
+        s = tile_score(Q[qi], K);
+        if (p >= nv[qi]) s = -INFINITY;
+      }
+      if (a.scores && g == 0 && p < a.n_cache) a.scores[r * a.s_stride + p] = s;
+      if (a.block_max) {
+        float m = s;
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        const int64_t blk = p >> 3;
+        if (g == 0 && (kl & 7) == 0 && blk < nblk) a.block_max[r * a.bm_stride + blk] = m;
+      }
+    }
+  };
+  // DEPTH tiles in flight per wave: the loads of a wave's next-but-one tile
+  // are issued as soon as its current tile has been consumed
+  constexpr int DEPTH = 2;
+  KT buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (t + d * WAVES < t_end) fetch(t + d * WAVES, buf[d]);
+  for (; t < t_end; t += DEPTH * WAVES) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t tt = t + d * WAVES;
+      if (tt < t_end) {
+        process(tt, buf[d]);
+        if (tt + DEPTH * WAVES < t_end) fetch(tt + DEPTH * WAVES, buf[d]);
+      }
+    }
+  }
+}
+
+// ---- prefill: many queries per sequence -------------------------------------
+// MFMA-bound.  A block = 8 waves x PF_QW queries = 16 consecutive queries of
+// one sequence, over one of PF_CHUNKS equal key ranges; with 8 ranges and
+// the block id's low bits picking the range, each XCD keeps "its" key range
+// resident in its L2 while every query group streams through it.
+// v_mfma_f32_32x32x16_bf16: A = 32 heads x 16 dims of one query (registers,
+// loaded once), B = 16 dims x 32 keys of the current key tile (LDS, shared by
+// the 16 queries of the block), D = heads x keys; lane l holds key l%32 and
+// heads 8(i/4) + 4(l/32) + i%4 of accumulator element i.  Epilogue per
+// query and 32 keys: ReLU x w_h over the lane's 16 heads, one cross-half
+// shuffle for the other 16, causal mask, max over each 8-key block.
+constexpr int PF_WAVES = 8;
+constexpr int PF_QW = 2;                       // queries per wave
+constexpr int PF_Q = PF_WAVES * PF_QW;         // queries per block
+constexpr int PF_CHUNKS = 8;                   // key ranges (one per XCD)
+constexpr int PF_TILE = 32;                    // keys per tile
+constexpr int PF_LD = DI * 2 + 16;             // LDS bytes per key row (padded)
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
+  __shared__ __align__(16) uint8_t kt[2][PF_TILE * PF_LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, kn = lane & 31;
+  const int chunk = blockIdx.x;
+  const int b = blockIdx.z;
+  const int j0 = blockIdx.y * PF_Q + wave * PF_QW;  // this wave's first query
+  const int64_t k0 = (int64_t)chunk * keys_per_chunk;
+  const int64_t k1 = min(a.n_cache, k0 + keys_per_chunk);
+  const int64_t nblk = (a.n_cache + BLK - 1) / BLK;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.k_sb;
+
+  // query operands and per-lane head weights
+  bf16x8 qa[PF_QW][8];
+  float wl[PF_QW][16];
+  int64_t nv[PF_QW], rows[PF_QW];
+  bool qok[PF_QW];
+  int64_t nv_blk = 0;  // largest visible count of the block's queries
+#pragma unroll
+  for (int qi = 0; qi < PF_QW; ++qi) {
+    const int j = j0 + qi;
+    qok[qi] = j < a.Tq;
+    const int64_t r = (int64_t)b * a.Tq + (qok[qi] ? j : a.Tq - 1);
+    rows[qi] = r;
+    const uint16_t* qr = a.q + r * (HI * DI) + kn * DI + 8 * half;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qa[qi][c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) wl[qi][i] = a.w[r * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
+    nv[qi] = qok[qi] ? n_visible(a.q_pos[r], a.n_cache) : 0;
+  }
+  {
+    // visible range of the whole block (queries are consecutive)
+    const int jl = min(a.Tq - 1, (int)blockIdx.y * PF_Q + PF_Q - 1);
+    nv_blk = n_visible(a.q_pos[(int64_t)b * a.Tq + jl], a.n_cache);
+    const int jf = min(a.Tq - 1, (int)blockIdx.y * PF_Q);
+    nv_blk = max(nv_blk, n_visible(a.q_pos[(int64_t)b * a.Tq + jf], a.n_cache));
+  }
+  // staging: thread -> (row tid/16, 16-byte piece tid%16) of a 32-key tile
+  const int srow = tid >> 4, spiece = tid & 15;
+  auto load_tile = [&](int64_t t0, u32x4& v) {
+    const int64_t row = t0 + srow;
+    v = (u32x4){0u, 0u, 0u, 0u};
+    if (row < k1 && row < nv_blk) v = *reinterpret_cast<const u32x4*>(kb + row * DI + 8 * spiece);
+  };
+  const int64_t kend = min(k1, max(k0, nv_blk));  // keys that need computing
+  u32x4 nxt;
+  int buf = 0;
+  if (k0 < kend) load_tile(k0, nxt);
+  for (int64_t t0 = k0; t0 < k1; t0 += PF_TILE) {
+    const bool compute = t0 < kend;  // block-uniform
+    if (compute) {
+      *reinterpret_cast<u32x4*>(&kt[buf][srow * PF_LD + 16 * spiece]) = nxt;
+      __syncthreads();
+      if (t0 + PF_TILE < kend) load_tile(t0 + PF_TILE, nxt);
+    }
+    const int64_t p = t0 + kn;  // this lane's key
+    bf16x8 kbop[8];
+    if (compute) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        kbop[c] = *reinterpret_cast<const bf16x8*>(&kt[buf][kn * PF_LD + 32 * c + 16 * half]);
+    }
+#pragma unroll
+    for (int qi = 0; qi < PF_QW; ++qi) {
+      if (!qok[qi]) continue;  // wave-uniform
+      float s = -INFINITY;
+      if (compute && t0 < nv[qi]) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qi][c], kbop[c], acc, 0, 0, 0);
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum = fmaf(wl[qi][i], fmaxf(acc[i], 0.f), sum);
+        sum += __shfl_xor(sum, 32, 64);
+        s = p < nv[qi] ? sum : -INFINITY;
+      }
+      if (a.scores && half == 0 && p < k1) a.scores[rows[qi] * a.s_stride + p] = s;
+      if (a.block_max) {
+        float m = s;
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        const int64_t blk = p >> 3;
+        if (half == 0 && (kn & 7) == 0 && blk < nblk && p < k1)
+          a.block_max[rows[qi] * a.bm_stride + blk] = m;
+      }
+    }
+    if (compute) buf ^= 1;
+  }
+}
+
+template <int QPB, bool FP8>
+hipError_t launch_scan_t(const ScanArgs& a, int B, dim3 grid, hipStream_t s) {
+  if (FP8)
+    hipLaunchKernelGGL((scan_kernel<QPB, QFp8, KFp8>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_kernel<QPB, QBf16, KBf16>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const void* k,
+                             bool k_fp8, int64_t k_sb, int64_t n_cache, const int64_t* q_pos,
+                             float* scores, int64_t s_stride, float* block_max,
+                             int64_t bm_stride, hipStream_t s) {
+  ScanArgs a{(const uint16_t*)q, w, k, k_sb, n_cache, q_pos, Tq,
+             scores, s_stride, block_max, bm_stride, 1};
+  if (!k_fp8 && Tq >= 64) {
+    // many queries: the MFMA-bound prefill kernel.  Chunk boundaries are
+    // multiples of the 32-key tile (so of the 8-key block).
+    int64_t kpc = (n_cache + PF_CHUNKS - 1) / PF_CHUNKS;
+    kpc = (kpc + PF_TILE - 1) / PF_TILE * PF_TILE;
+    const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
+    dim3 grid(nchunks, (unsigned)((Tq + PF_Q - 1) / PF_Q), (unsigned)B);
+    hipLaunchKernelGGL(prefill_scan_kernel, grid, dim3(PF_WAVES * 64), 0, s, a, kpc);
+    return hipGetLastError();
+  }
+
+  const int qpb = Tq >= 4 ? 4 : (Tq >= 2 ? 2 : 1);
+  const int64_t nz = (Tq + qpb - 1) / qpb;
+  const int64_t n_tiles = (n_cache + 15) / 16;
+  // at most 16 tiles per wave (a block streams 256 KiB of bf16 keys); fewer
+  // when that would leave the chip short of blocks.  Measured on the 1M
+  // decode scan: 16 tiles per wave with interleaved waves beat 8, 32 and 64.
+  const int64_t target_waves = 4096;
+  int64_t tpw = (n_tiles * B * nz + target_waves - 1) / target_waves;
+  if (tpw < 1) tpw = 1;
+  if (tpw > 16) tpw = 16;
+  a.tiles_per_wave = (int)tpw;
+  const int64_t per_block = tpw * WAVES;
+  dim3 grid((unsigned)((n_tiles + per_block - 1) / per_block), (unsigned)B, (unsigned)nz);
+  if (qpb == 4) return k_fp8 ? launch_scan_t<4, true>(a, B, grid, s) : launch_scan_t<4, false>(a, B, grid, s);
+  if (qpb == 2) return k_fp8 ? launch_scan_t<2, true>(a, B, grid, s) : launch_scan_t<2, false>(a, B, grid, s);
+  return k_fp8 ? launch_scan_t<1, true>(a, B, grid, s) : launch_scan_t<1, false>(a, B, grid, s);
+}
+
+}  // namespace csa2

@@ -55,6 +55,11 @@ def test_compress_stage_tiny():
     ("tiny", {}),
     ("tiny", dict(N=2051, t_last=4101, seed=31)),            # ragged tiles / blocks
     ("1m_lowp", dict(B=2, N=4096, t_last=8191, Tq=3, seed=32)),  # FP8 keys, 3 queries
+    # many queries: the prefill scan kernel; ragged query groups, key chunks
+    # and tiles, visibility changing inside a block of queries
+    ("prefill", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=39)),
+    ("prefill", dict(B=2, Tq=64, N=4096, t_last=8191, K_b=32, K=64, comp_T=0,
+                     shared_indexer=False, seed=41)),
 ])
 def test_scan_cand_select_stages(name, kw):
     cfg = gen.shrink(gen.CONFIGS[name], **kw)
