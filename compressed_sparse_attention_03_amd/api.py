@@ -204,5 +204,16 @@ class DecodePath:
         return self.out
 
 
+    def capture(self, inp: dict, scale: float, compress_first: bool = True):
+        """Record one pass into a HIP graph (torch.cuda.CUDAGraph) for callers
+        that replay work under graph capture; buffers and inputs are the ones
+        given here.  Call run() once before, so that one-time kernel
+        attributes are set outside the capture."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.run(inp, scale, compress_first=compress_first)
+        return graph
+
+
 STAGES = ("compress", "index_scan", "select_blocks", "index_cand", "select_positions",
           "sparse_attn")

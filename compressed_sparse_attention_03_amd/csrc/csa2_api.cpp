@@ -48,8 +48,8 @@ int csa2_version(void) { return (1 << 16) | 0; }
 size_t csa2_workspace_bytes(int op, int64_t R, int64_t n, int64_t k) {
   if (R <= 0) return 0;
   if (op == CSA2_OP_SPARSE_ATTN) {
-    if (n < 0 || k < 1) return 0;
-    return csa2::attn_workspace_bytes(R, (int)(n + k));
+    if (n < 0 || n > 2048 || k < 1 || k > (int64_t(1) << 30)) return 0;
+    return csa2::attn_workspace_bytes(R, (int)n, (int)k);
   }
   if (op == CSA2_OP_SELECT) {
     if (n < 1 || k < 1) return 0;
@@ -164,7 +164,7 @@ int csa2_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat
   if (K > 0 && sel_sb < K) return CSA2_EINVAL;
   if (lat_sb < 0 || (B > 1 && lat_sb < n_cache)) return CSA2_EINVAL;
   if (win_sb < 0 || (B > 1 && win_sb < W_cap)) return CSA2_EINVAL;
-  const size_t need = csa2::attn_workspace_bytes(R, K + W);
+  const size_t need = csa2::attn_workspace_bytes(R, K, W);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return CSA2_EWORKSPACE;
   clear_stale_error();
   const int lat_fmt = lat_dt == CSA2_NVFP4 ? 3 : 1;

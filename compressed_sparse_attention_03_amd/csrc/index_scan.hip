@@ -30,8 +30,67 @@ struct ScanArgs {
 };
 
 // ---- scan: every latent, block max fused ------------------------------------
+// Keys are read fully coalesced: a 16-key tile (4 KiB bf16, 2 KiB FP8) is
+// loaded as 1 KiB contiguous per wave load, lane l taking 16-byte chunk
+// l % C of tile row l / C + (64 / C) c (C = 16-byte chunks per row), the
+// chunk index XOR-swizzled by the row; a per-wave LDS buffer then hands each
+// lane its MFMA operand (key kl = l % 16: bf16 chunks g + 4c, FP8 chunks g
+// and g + 4, g = l / 16).  The swizzle keeps the stores conflict free and the
+// loads at most 2-way.
+template <typename KT>
+struct KRaw;
+template <>
+struct KRaw<KBf16> {
+  static constexpr int ROW = DI * 2, LOADS = 4;
+  u32x4 r[LOADS];
+};
+template <>
+struct KRaw<KFp8> {
+  static constexpr int ROW = DI, LOADS = 2;
+  u32x4 r[LOADS];
+};
+
+template <typename KT>
+__device__ __forceinline__ void load_key_coalesced(const void* kbase, int64_t tile, int64_t n_cache,
+                                                   int lane, KRaw<KT>& R) {
+  constexpr int ROW = KRaw<KT>::ROW, C = ROW / 16, RPL = 64 / C;  // chunks per row, rows per load
+#pragma unroll
+  for (int c = 0; c < KRaw<KT>::LOADS; ++c) {
+    const int rl = lane / C + RPL * c;  // tile row
+    int64_t row = tile * 16 + rl;
+    row = row < n_cache ? row : n_cache - 1;
+    const int chunk = (lane % C) ^ (rl % C);
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kbase) + row * ROW) + chunk;
+    R.r[c] = __builtin_nontemporal_load(p);
+  }
+}
+
+// stage the tile into the wave's LDS buffer and read this lane's operand
+__device__ __forceinline__ void relayout_key(const KRaw<KBf16>& R, uint8_t* kst, int lane, KBf16& K) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(kst + 1024 * c + 16 * lane) = R.r[c];
+  const int kl = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    K.b[c] = *reinterpret_cast<const bf16x8*>(kst + kl * 256 + (((g + 4 * c) ^ kl) << 4));
+}
+
+__device__ __forceinline__ void relayout_key(const KRaw<KFp8>& R, uint8_t* kst, int lane, KFp8& K) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) *reinterpret_cast<u32x4*>(kst + 1024 * c + 16 * lane) = R.r[c];
+  const int kl = lane & 15, g = lane >> 4;
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(kst + kl * 128 + ((g ^ (kl & 7)) << 4));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(kst + kl * 128 + (((g + 4) ^ (kl & 7)) << 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    K.b[i] = (int)lo[i];
+    K.b[4 + i] = (int)hi[i];
+  }
+}
+
 template <int QPB, typename QT, typename KT>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  using KL = KRaw<KT>;  // what a fetch holds
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.y;
   const int j0 = blockIdx.z * QPB;
@@ -40,6 +99,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int64_t nblk = (a.n_cache + BLK - 1) / BLK;
 
   __shared__ __align__(16) uint8_t qstage[HI * DI];
+  __shared__ __align__(16) uint8_t kstage[WAVES][16 * KRaw<KT>::ROW];
   QT Q[QPB];
   int64_t nv[QPB];
   int64_t max_nv = 0;
@@ -62,15 +122,17 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int64_t t_end = min(blk0 + (int64_t)WAVES * a.tiles_per_wave, n_tiles);
   if (t >= t_end) return;
 
-  auto fetch = [&](int64_t tile, KT& K) {
-    const int64_t row = tile * 16 + kl;
-    if (tile * 16 < max_nv)
-      load_key(kb, row < a.n_cache ? row : a.n_cache - 1, g, K);
-    else
-      zero_key(K);
+  // The first DEPTH tiles are fetched without waiting for the queries'
+  // positions (any tile of the cache is readable; invisible keys are masked
+  // when scored); later fetches skip tiles past every query's horizon.
+  auto fetch = [&](int64_t tile, KL& K, int64_t horizon) {
+    if (tile * 16 < horizon) load_key_coalesced<KT>(kb, tile, a.n_cache, lane, K);
   };
-  auto process = [&](int64_t tile, const KT& K) {
+  auto process = [&](int64_t tile, const KL& KLd) {
     const int64_t p = tile * 16 + kl;
+    KT K;
+    // a tile past every query's horizon was not fetched and is not scored
+    if (tile * 16 < max_nv) relayout_key(KLd, kstage[wave], lane, K);
 #pragma unroll
     for (int qi = 0; qi < QPB; ++qi) {
       if (qi >= nq) break;
@@ -91,20 +153,22 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       }
     }
   };
-  // DEPTH tiles in flight per wave: the loads of a wave's next-but-one tile
+  // DEPTH tiles in flight per wave: the loads of a wave's tile DEPTH ahead
   // are issued as soon as its current tile has been consumed
-  constexpr int DEPTH = 2;
-  KT buf[DEPTH];
+  // tiles in flight per wave: 3 for one query; with more queries the
+  // registers of their operands leave room for 2
+  constexpr int DEPTH = QPB == 1 ? 3 : 2;
+  KL buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
-    if (t + d * WAVES < t_end) fetch(t + d * WAVES, buf[d]);
+    if (t + d * WAVES < t_end) fetch(t + d * WAVES, buf[d], a.n_cache);
   for (; t < t_end; t += DEPTH * WAVES) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int64_t tt = t + d * WAVES;
       if (tt < t_end) {
         process(tt, buf[d]);
-        if (tt + DEPTH * WAVES < t_end) fetch(tt + DEPTH * WAVES, buf[d]);
+        if (tt + DEPTH * WAVES < t_end) fetch(tt + DEPTH * WAVES, buf[d], max_nv);
       }
     }
   }
@@ -254,13 +318,14 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
   const int qpb = Tq >= 4 ? 4 : (Tq >= 2 ? 2 : 1);
   const int64_t nz = (Tq + qpb - 1) / qpb;
   const int64_t n_tiles = (n_cache + 15) / 16;
-  // at most 16 tiles per wave (a block streams 256 KiB of bf16 keys); fewer
+  // at most 32 tiles per wave (a block streams 512 KiB of bf16 keys); fewer
   // when that would leave the chip short of blocks.  Measured on the 1M
-  // decode scan: 16 tiles per wave with interleaved waves beat 8, 32 and 64.
-  const int64_t target_waves = 4096;
+  // decode scan (3 tiles in flight per wave): 32 tiles per wave beat 8 to
+  // 24 (per-block start-up) and 64 (2048 blocks balance the XCDs better).
+  const int64_t target_waves = 8192;
   int64_t tpw = (n_tiles * B * nz + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
-  if (tpw > 16) tpw = 16;
+  if (tpw > 32) tpw = 32;
   a.tiles_per_wave = (int)tpw;
   const int64_t per_block = tpw * WAVES;
   dim3 grid((unsigned)((n_tiles + per_block - 1) / per_block), (unsigned)B, (unsigned)nz);

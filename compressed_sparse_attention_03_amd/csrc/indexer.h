@@ -128,16 +128,18 @@ struct KFp8 {
   i32x8 b;
 };
 
+// One key row straight into this lane's operand layout (the candidate
+// gather; cached loads: in prefill the same blocks serve many queries).
 __device__ __forceinline__ void load_key(const void* kbase, int64_t row, int g, KBf16& K) {
-  const uint16_t* p = static_cast<const uint16_t*>(kbase) + row * DI + 8 * g;
+  const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(kbase) + row * DI + 8 * g);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) K.b[c] = *reinterpret_cast<const bf16x8*>(p + 32 * c);
+  for (int c = 0; c < 4; ++c) K.b[c] = __builtin_bit_cast(bf16x8, p[4 * c]);
 }
 
 __device__ __forceinline__ void load_key(const void* kbase, int64_t row, int g, KFp8& K) {
-  const uint8_t* p = static_cast<const uint8_t*>(kbase) + row * DI + 16 * g;
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 64);
+  const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kbase) + row * DI + 16 * g);
+  const u32x4 lo = p[0];
+  const u32x4 hi = p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     K.b[i] = (int)lo[i];

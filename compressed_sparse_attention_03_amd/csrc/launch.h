@@ -28,8 +28,8 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
                               int force_last, int k, int32_t* out, int64_t o_stride, void* ws,
                               hipStream_t s);
 
-int attn_splits(int64_t R, int n_rows);
-size_t attn_workspace_bytes(int64_t R, int n_rows);
+int attn_splits(int64_t R, int K, int W);
+size_t attn_workspace_bytes(int64_t R, int K, int W);
 hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
                               int lat_fmt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,
                               const int32_t* sel, int K, int64_t sel_sb, const void* win,

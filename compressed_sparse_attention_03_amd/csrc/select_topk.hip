@@ -284,11 +284,15 @@ struct SampleSmem {
   uint32_t b1, b2;
 };
 
+struct ThreshSmem {
+  uint32_t hist[KBIN];
+  uint32_t bc[4];
+};
+
 struct FinishSmem {
   uint32_t bitmap[MAX_N_FAST / 32];  // chosen columns
   uint32_t tiemap[MAX_N_FAST / 32];  // columns tied at the threshold key
-  uint32_t hist[KBIN];
-  uint32_t bc[4];
+  ThreshSmem ts;
 };
 
 // Wave-aggregated append of the flagged lanes to a list (LDS or global);
@@ -350,20 +354,16 @@ __device__ __forceinline__ void load_sample(const SelArgs& a, int64_t row, Elem 
 // bracket is made of whole bins, so it is approximate by design -- the exact
 // answer comes later and a bracket that misses is detected and handled.
 // Block of NT threads; the result depends only on the row, not on NT.
-template <int NT>
-__device__ void bracket_from_sample(const SelArgs& a, const Elem (&e)[SAMPLE / NT],
-                                    const int64_t (&js)[SAMPLE / NT], int32_t fcol, int32_t fid,
-                                    SampleSmem& ss, Shared& sh, uint32_t* A, uint32_t* Bt) {
-  constexpr int SPT = SAMPLE / NT;  // samples per thread
-  constexpr int BPT = NBIN / NT;    // histogram bins per thread
+// Core of the bracket: SPT sampled keys per thread (0 = absent) and r, the
+// expected sample rank of the wanted key.
+template <int NT, int SPT>
+__device__ void bracket_core(const uint32_t (&v)[SPT], float r, SampleSmem& ss, Shared& sh,
+                             uint32_t* A, uint32_t* Bt) {
+  constexpr int BPT = NBIN / NT;  // histogram bins per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t n = a.n;
-  uint32_t v[SPT];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
-    const bool forced = (js[i] == fcol) || (fid >= 0 && e[i].id == fid);
-    v[i] = forced ? 0u : e[i].key;
     if (v[i]) {
       kmin = min(kmin, v[i]);
       kmax = max(kmax, v[i]);
@@ -386,8 +386,6 @@ __device__ void bracket_from_sample(const SelArgs& a, const Elem (&e)[SAMPLE / N
     kmin = min(kmin, sh.wred[i * 4 + 1]);
     kmax = max(kmax, sh.wred[i * 4 + 2]);
   }
-  const int have_forced_guess = (fcol >= 0 || fid >= 0) ? 1 : 0;
-  const float r = (float)(a.k - have_forced_guess) * (float)SAMPLE / (float)n;
   const float delta = 4.0f * sqrtf(r) + 16.0f;
   const int r_hi = (int)floorf(r - delta);
   const int r_lo = (int)ceilf(r + delta);
@@ -440,6 +438,24 @@ __device__ void bracket_from_sample(const SelArgs& a, const Elem (&e)[SAMPLE / N
   __syncthreads();
 }
 
+template <int NT>
+__device__ void bracket_from_sample(const SelArgs& a, const Elem (&e)[SAMPLE / NT],
+                                    const int64_t (&js)[SAMPLE / NT], int32_t fcol, int32_t fid,
+                                    SampleSmem& ss, Shared& sh, uint32_t* A, uint32_t* Bt) {
+  constexpr int SPT = SAMPLE / NT;  // samples per thread
+  uint32_t v[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const bool forced = (js[i] == fcol) || (fid >= 0 && e[i].id == fid);
+    v[i] = forced ? 0u : e[i].key;
+  }
+  // each column is sampled with probability SAMPLE / n; invalid entries rank
+  // below every valid one, so the k-th key sits near sample rank k SAMPLE / n
+  const int have_forced_guess = (fcol >= 0 || fid >= 0) ? 1 : 0;
+  const float r = (float)(a.k - have_forced_guess) * (float)SAMPLE / (float)a.n;
+  bracket_core<NT, SPT>(v, r, ss, sh, A, Bt);
+}
+
 // Bracket [Bt, A] around the k-th key of the row (see bracket_from_sample).
 template <int NT>
 __device__ void sample_bracket(const SelArgs& a, int64_t row, int32_t fcol, int32_t fid,
@@ -489,64 +505,91 @@ __device__ void classify_range(const SelArgs& a, int64_t row, int64_t j0, int64_
   }
 }
 
-// Threshold on the candidate KEYS (high half of each composite) such that
-// the m best candidates are: every key above it, plus -- when the threshold
-// key itself is shared by more candidates than still wanted -- the `need`
-// smallest columns among those tied at it.  Bits that every candidate key
-// has in common are skipped (integer-valued scores leave the low mantissa
-// bits constant), then 11-bit radix digits from the top; a digit bin that
-// holds exactly the number still wanted ends the search.  In the result,
-// with u = key >> tz:  chosen  iff (u >> lo) > (U >> lo), or (u >> lo) ==
-// (U >> lo) and (take_all, or among the first `need` such columns).
-// 1024 threads.
+// Threshold on the candidate KEYS such that the m best candidates are: every
+// key above it, plus -- when the threshold key itself is shared by more
+// candidates than still wanted -- the `need` smallest columns among those
+// tied at it.  Low bits that every candidate key has in common are dropped
+// (integer-valued scores leave the low mantissa bits constant) and the
+// smallest key is subtracted, d = (key >> tz) - base, so the digits cover
+// only the spread of the candidates; then 11-bit radix digits of d from the
+// top, a digit bin that holds exactly the number still wanted ending the
+// search.  Candidate order: see th_cmp.  P values per thread; the key of
+// value x is x >> SHIFT, and it is a candidate iff lo_key <= key <= hi_key
+// (lo_key >= 1).  1024 threads.
 struct KeyThreshold {
-  uint32_t U;
+  uint32_t D;     // digits of d chosen so far (bits >= lo)
+  uint32_t base;  // smallest candidate key >> tz
   int lo, tz;
-  bool take_all;
-  uint32_t need;
+  bool take_all;  // every candidate in the threshold bin is taken
+  uint32_t need;  // else: how many of them, in column order
 };
 
-__device__ KeyThreshold key_threshold(const uint64_t (&v)[CAND_PT], uint32_t m, FinishSmem& fs,
-                                      Shared& sh) {
+// +1: candidate above the threshold bin (chosen); 0: in it; -1: below.
+__device__ __forceinline__ int th_cmp(const KeyThreshold& th, uint32_t key) {
+  const uint32_t d = ((key >> th.tz) - th.base) >> th.lo;
+  const uint32_t D = th.D >> th.lo;
+  return d > D ? 1 : (d == D ? 0 : -1);
+}
+
+template <int P, int SHIFT, typename T>
+__device__ KeyThreshold key_threshold(const T (&vals)[P], uint32_t lo_key, uint32_t hi_key,
+                                      uint32_t m, ThreshSmem& fs, Shared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t kand = 0xffffffffu, kor = 0u;
+  auto ck = [&](int i) {
+    const uint32_t k = (uint32_t)(vals[i] >> SHIFT);
+    return (k >= lo_key && k <= hi_key) ? k : 0u;
+  };
+  uint32_t kand = 0xffffffffu, kor = 0u, kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-  for (int i = 0; i < CAND_PT; ++i)
-    if (v[i]) {
-      const uint32_t k = (uint32_t)(v[i] >> 32);
+  for (int i = 0; i < P; ++i) {
+    const uint32_t k = ck(i);
+    if (k) {
       kand &= k;
       kor |= k;
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
     }
+  }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
     kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
   }
   if (lane == 0) {
     sh.wred[wave * 4 + 0] = kand;
     sh.wred[wave * 4 + 1] = kor;
+    sh.wred[wave * 4 + 2] = kmin;
+    sh.wred[wave * 4 + 3] = kmax;
   }
   __syncthreads();
   kand = 0xffffffffu;
   kor = 0u;
+  kmin = 0xffffffffu;
+  kmax = 0u;
   for (int i = 0; i < NWAVES; ++i) {
     kand &= sh.wred[i * 4 + 0];
     kor |= sh.wred[i * 4 + 1];
+    kmin = min(kmin, sh.wred[i * 4 + 2]);
+    kmax = max(kmax, sh.wred[i * 4 + 3]);
   }
   __syncthreads();
   KeyThreshold th;
   const uint32_t varying = kand ^ kor;  // bits that differ between some keys
   th.tz = varying ? __ffs(varying) - 1 : 0;
-  int hi = varying ? 32 - __clz(varying >> th.tz) : 0;  // u = key >> tz differ below hi
-  uint32_t prefix = (kor >> th.tz) & ~(hi >= 32 ? 0xffffffffu : ((1u << hi) - 1u));
+  th.base = kmin >> th.tz;
+  const uint32_t spread = (kmax >> th.tz) - th.base;  // d in [0, spread]
+  int hi = spread ? 32 - __clz(spread) : 0;            // d < 2^hi
+  uint32_t prefix = 0u;
   uint32_t remaining = m, cbin = 0;
   th.take_all = false;
   th.lo = 0;
-  // count of candidates sharing every key bit (all keys equal)
+  // count of candidates sharing one key (spread 0)
   if (hi == 0) {
     uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < CAND_PT; ++i) c += v[i] != 0;
+    for (int i = 0; i < P; ++i) c += ck(i) != 0;
     uint32_t tot;
     block_exclusive_scan(c, sh, &tot);
     cbin = tot;
@@ -557,10 +600,11 @@ __device__ KeyThreshold key_threshold(const uint64_t (&v)[CAND_PT], uint32_t m, 
     for (int i = tid; i < KBIN; i += THREADS) fs.hist[i] = 0;
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < CAND_PT; ++i) {
-      if (!v[i]) continue;
-      const uint32_t u = (uint32_t)(v[i] >> 32) >> th.tz;
-      if (hi >= 32 || (u >> hi) == (prefix >> hi)) atomicAdd(&fs.hist[(u >> lo) & dmask], 1u);
+    for (int i = 0; i < P; ++i) {
+      const uint32_t k = ck(i);
+      if (!k) continue;
+      const uint32_t d = (k >> th.tz) - th.base;
+      if (hi >= 32 || (d >> hi) == (prefix >> hi)) atomicAdd(&fs.hist[(d >> lo) & dmask], 1u);
     }
     __syncthreads();
     // thread t owns bins 2047-2t and 2046-2t (highest first)
@@ -586,10 +630,57 @@ __device__ KeyThreshold key_threshold(const uint64_t (&v)[CAND_PT], uint32_t m, 
     __syncthreads();
     if (remaining == cbin) break;
   }
-  th.U = prefix;
+  th.D = prefix;
   th.take_all = remaining == cbin;
   th.need = remaining;
   return th;
+}
+
+// Ordered read-back of the chosen bitmap (words of 32 columns, column order):
+// unless th.take_all, the first th.need columns of the tie bitmap join the
+// chosen ones; the ids of the chosen columns are written in column order and
+// the row is padded with -1 up to k.  1024 threads.
+__device__ __forceinline__ void read_back(const SelArgs& a, int64_t row, const KeyThreshold& th, int words,
+                          uint32_t* bitmap, const uint32_t* tiemap, Shared& sh) {
+  const int tid = threadIdx.x;
+  // thread t owns a contiguous run of words
+  const int wpt = (words + THREADS - 1) / THREADS;
+  const int w0 = tid * wpt, w1 = min(words, w0 + wpt);
+  uint32_t nt = 0;
+  if (!th.take_all)
+    for (int wi = w0; wi < w1; ++wi) nt += __popc(tiemap[wi]);
+  uint32_t tot_t = 0;
+  uint32_t tie_rank = th.take_all ? 0u : block_exclusive_scan(nt, sh, &tot_t);
+  // keep the ties with rank < need: fold them into the chosen bitmap words
+  uint32_t cnt = 0;
+  for (int wi = w0; wi < w1; ++wi) {
+    uint32_t word = bitmap[wi];
+    if (!th.take_all) {
+      uint32_t tb = tiemap[wi];
+      while (tb) {
+        const uint32_t bit = tb & (0u - tb);
+        tb &= tb - 1u;
+        if (tie_rank < th.need) word |= bit;
+        ++tie_rank;
+      }
+      bitmap[wi] = word;
+    }
+    cnt += __popc(word);
+  }
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan(cnt, sh, &total);
+  int32_t* orow = a.out + row * a.o_stride;
+  for (int wi = w0; wi < w1; ++wi) {
+    uint32_t bits = bitmap[wi];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int64_t c = (int64_t)wi * 32 + b;
+      if (pos < (uint32_t)a.k) orow[pos] = a.ids ? a.ids[row * a.id_stride + c] : (int32_t)c;
+      ++pos;
+    }
+  }
+  for (int i = (int)total + tid; i < a.k; i += THREADS) orow[i] = -1;
 }
 
 // From the "in" columns and the candidate composites (held in registers,
@@ -599,11 +690,12 @@ __device__ KeyThreshold key_threshold(const uint64_t (&v)[CAND_PT], uint32_t m, 
 // first `need` tied columns.  The caller has checked the bracket
 // (n_in + m == k_rem, n_cand <= CAND_CAP).  1024 threads.
 __device__ void finish_core(const SelArgs& a, int64_t row, int32_t fcol, uint32_t n_in,
-                            const int32_t* in_list, uint32_t m, const uint64_t (&v)[CAND_PT],
-                            FinishSmem& fs, Shared& sh) {
+                            const int32_t* in_list, uint32_t m, const uint32_t (&ckey)[CAND_PT],
+                            const uint32_t (&ccol)[CAND_PT], FinishSmem& fs, Shared& sh) {
   const int tid = threadIdx.x;
-  KeyThreshold th{0u, 0, 0, true, 0u};
-  if (m > 0) th = key_threshold(v, m, fs, sh);
+  KeyThreshold th{0u, 0u, 0, 0, true, 0u};
+  if (m > 0)
+    th = key_threshold<CAND_PT, 0>(ckey, 1u, 0xffffffffu, m, fs.ts, sh);
   const int64_t n = a.n;
   const int words = (int)((n + 31) / 32);
   for (int i = tid; i < words; i += THREADS) {
@@ -616,58 +708,20 @@ __device__ void finish_core(const SelArgs& a, int64_t row, int32_t fcol, uint32_
     atomicOr(&fs.bitmap[c >> 5], 1u << (c & 31));
   }
   if (m > 0) {
-    const uint32_t Ulo = th.U >> th.lo;
 #pragma unroll
     for (int i = 0; i < CAND_PT; ++i) {
-      if (!v[i]) continue;
-      const uint32_t u = ((uint32_t)(v[i] >> 32) >> th.tz) >> th.lo;
-      const uint32_t c = 0xffffffffu - (uint32_t)(v[i] & 0xffffffffull);
-      if (u > Ulo || (u == Ulo && th.take_all))
+      if (!ckey[i]) continue;
+      const int cmp = th_cmp(th, ckey[i]);
+      const uint32_t c = ccol[i];
+      if (cmp > 0 || (cmp == 0 && th.take_all))
         atomicOr(&fs.bitmap[c >> 5], 1u << (c & 31));
-      else if (u == Ulo)
+      else if (cmp == 0)
         atomicOr(&fs.tiemap[c >> 5], 1u << (c & 31));
     }
   }
   if (tid == 0 && fcol >= 0) atomicOr(&fs.bitmap[fcol >> 5], 1u << (fcol & 31));
   __syncthreads();
-  // ordered read-back: thread t owns a contiguous run of words
-  const int wpt = (words + THREADS - 1) / THREADS;
-  const int w0 = tid * wpt, w1 = min(words, w0 + wpt);
-  uint32_t nt = 0;
-  if (!th.take_all)
-    for (int wi = w0; wi < w1; ++wi) nt += __popc(fs.tiemap[wi]);
-  uint32_t tot_t = 0;
-  uint32_t tie_rank = th.take_all ? 0u : block_exclusive_scan(nt, sh, &tot_t);
-  // keep the ties with rank < need: fold them into the chosen bitmap words
-  uint32_t cnt = 0;
-  for (int wi = w0; wi < w1; ++wi) {
-    uint32_t word = fs.bitmap[wi];
-    if (!th.take_all) {
-      uint32_t tb = fs.tiemap[wi];
-      while (tb) {
-        const uint32_t bit = tb & (0u - tb);
-        tb &= tb - 1u;
-        if (tie_rank < th.need) word |= bit;
-        ++tie_rank;
-      }
-      fs.bitmap[wi] = word;
-    }
-    cnt += __popc(word);
-  }
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan(cnt, sh, &total);
-  int32_t* orow = a.out + row * a.o_stride;
-  for (int wi = w0; wi < w1; ++wi) {
-    uint32_t bits = fs.bitmap[wi];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      const int64_t c = (int64_t)wi * 32 + b;
-      if (pos < (uint32_t)a.k) orow[pos] = a.ids ? a.ids[row * a.id_stride + c] : (int32_t)c;
-      ++pos;
-    }
-  }
-  for (int i = (int)total + tid; i < a.k; i += THREADS) orow[i] = -1;
+  read_back(a, row, th, words, fs.bitmap, fs.tiemap, sh);
 }
 
 // Lists in one place (LDS): check the bracket, then finish.  Returns false
@@ -678,13 +732,15 @@ __device__ bool finish_from_lists(const SelArgs& a, int64_t row, int32_t fcol, u
   const int tid = threadIdx.x;
   const uint32_t k_rem = (uint32_t)(a.k - (fcol >= 0 ? 1 : 0));
   if (n_in > k_rem || n_in + n_cand < k_rem || n_cand > CAND_CAP || a.n > MAX_N_FAST) return false;
-  uint64_t v[CAND_PT];
+  uint32_t ckey[CAND_PT], ccol[CAND_PT];
 #pragma unroll
   for (int i = 0; i < CAND_PT; ++i) {
     const uint32_t idx = tid + i * THREADS;
-    v[i] = idx < n_cand ? cand_src[idx] : 0ull;
+    const uint64_t v = idx < n_cand ? cand_src[idx] : 0ull;
+    ckey[i] = (uint32_t)(v >> 32);
+    ccol[i] = 0xffffffffu - (uint32_t)v;
   }
-  finish_core(a, row, fcol, n_in, in_list, k_rem - n_in, v, fs, sh);
+  finish_core(a, row, fcol, n_in, in_list, k_rem - n_in, ckey, ccol, fs, sh);
   return true;
 }
 
@@ -871,22 +927,222 @@ __global__ __launch_bounds__(THREADS) void select_finish_kernel(SelArgs a, const
     const int c = chunk_of(p_in, i);
     in_flat[i] = sr[c].in[i - p_in[c]];
   }
-  uint64_t v[CAND_PT];
+  uint32_t ckey[CAND_PT], ccol[CAND_PT];
 #pragma unroll
   for (int q = 0; q < CAND_PT; ++q) {
     const uint32_t i = tid + q * THREADS;
-    v[q] = 0ull;
+    uint64_t v = 0ull;
     if (i < tot_cand) {
       const int c = chunk_of(p_cand, i);
-      v[q] = sr[c].cand[i - p_cand[c]];
+      v = sr[c].cand[i - p_cand[c]];
     }
+    ckey[q] = (uint32_t)(v >> 32);
+    ccol[q] = 0xffffffffu - (uint32_t)v;
   }
   __syncthreads();
-  finish_core(a, row, fcol, tot_in, in_flat, k_rem - tot_in, v, fs, sh);
+  finish_core(a, row, fcol, tot_in, in_flat, k_rem - tot_in, ckey, ccol, fs, sh);
 }
 
+// ---- rows of up to 1024 * E entries, held in registers ----------------------
+// One 1024-thread workgroup per row.  Entry j of the row is element j / 1024
+// of thread j % 1024, so the 32 columns of a bitmap word sit in 32
+// consecutive lanes of one wave and one ballot writes them (no atomics, no
+// clearing).  The row is read from memory once; everything after that works
+// on registers and LDS:
+//  1. keys, valid count and forced column (last valid entry, or the first
+//     valid entry holding the forced id) by block reductions; the forced key
+//     is set aside (0) and k_rem = k - 1 others are wanted;
+//  2. E > 8: a bracket [Bt, A] from 2048 of the register keys, as in the
+//     sampled paths; "in" = key > A, candidates = Bt <= key <= A.  When the
+//     counts show that it missed, every valid entry is a candidate instead, so
+//     the result never depends on the sample.  E = 8: all are candidates;
+//  3. the exact key threshold over the candidates (radix on the registers);
+//  4. ballots into the chosen and tie bitmaps, ordered read-back.
+template <int E>
+struct RowsSmem {
+  Shared sh;
+  SampleSmem ss;
+  ThreshSmem ts;
+  uint64_t bitmap[E * 16];  // 64 columns per entry: the two words of one ballot
+  uint64_t tiemap[E * 16];
+};
+
+template <int E, bool IDS>
+__device__ __forceinline__ void load_row_keys(const SelArgs& a, int64_t row, int32_t fid,
+                                              uint32_t (&key)[E], int32_t* last_valid,
+                                              int32_t* first_fid, uint32_t* n_valid) {
+  const int tid = threadIdx.x;
+  const int n = (int)a.n;
+  const float* srow = a.scores + row * a.s_stride;
+  const int32_t* irow = IDS ? a.ids + row * a.id_stride : nullptr;
+  // with ids, 16 entries at a time so that ids and scores are not all live
+  constexpr int G = (IDS && E > 16) ? 16 : E;
+  int32_t lv = -1, ff = 0x7fffffff;
+  uint32_t nv = 0;
+#pragma unroll
+  for (int g = 0; g < E; g += G) {
+    float sc[G];
+    int32_t id[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = (g + u) * THREADS + tid;
+      sc[u] = j < n ? srow[j] : -INFINITY;
+      id[u] = IDS ? (j < n ? irow[j] : -1) : j;
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = (g + u) * THREADS + tid;
+      const bool ok = id[u] >= 0 && !(sc[u] != sc[u]) && sc[u] != -INFINITY;
+      key[g + u] = ok ? order_key(sc[u]) : 0u;
+      if (ok) {
+        lv = j;  // j grows with g + u
+        ++nv;
+        if (fid >= 0 && id[u] == fid) ff = min(ff, j);
+      }
+    }
+  }
+  *last_valid = lv;
+  *first_fid = ff;
+  *n_valid = nv;
+}
+
+template <int E>
+__global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
+  __shared__ RowsSmem<E> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int32_t fid = a.forced ? a.forced[row] : -1;
+
+  // ---- 1 -------------------------------------------------------------------
+  uint32_t key[E];
+  int32_t lv, ff;
+  uint32_t nv;
+  if (a.ids) load_row_keys<E, true>(a, row, fid, key, &lv, &ff, &nv);
+  else load_row_keys<E, false>(a, row, fid, key, &lv, &ff, &nv);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lv = max(lv, __shfl_xor(lv, o, 64));
+    ff = min(ff, __shfl_xor(ff, o, 64));
+    nv += (uint32_t)__shfl_xor((int)nv, o, 64);
+  }
+  if (lane == 0) {
+    sm.sh.wred[wave * 4 + 0] = (uint32_t)lv;
+    sm.sh.wred[wave * 4 + 1] = (uint32_t)ff;
+    sm.sh.wred[wave * 4 + 2] = nv;
+  }
+  __syncthreads();
+  lv = -1;
+  ff = 0x7fffffff;
+  nv = 0;
+  for (int i = 0; i < NWAVES; ++i) {
+    lv = max(lv, (int32_t)sm.sh.wred[i * 4 + 0]);
+    ff = min(ff, (int32_t)sm.sh.wred[i * 4 + 1]);
+    nv += sm.sh.wred[i * 4 + 2];
+  }
+  __syncthreads();
+  int32_t fcol = -1;
+  if (a.force_last) fcol = lv;
+  else if (fid >= 0 && ff != 0x7fffffff) fcol = ff;
+  if (fcol >= 0) {
+#pragma unroll
+    for (int i = 0; i < E; ++i)
+      if (i * THREADS + tid == fcol) key[i] = 0u;
+  }
+  const uint32_t k_rem = (uint32_t)a.k - (fcol >= 0 ? 1u : 0u);
+  const uint32_t n_rest = nv - (fcol >= 0 ? 1u : 0u);
+
+  // ---- 2 -------------------------------------------------------------------
+  uint32_t A = 0u, Bt = 1u, m = 0u;  // A = 0: every valid key is in
+  if (n_rest > k_rem) {
+    A = 0xffffffffu;  // nothing in, every valid key a candidate
+    m = k_rem;
+    if (E > 8) {
+      // 2048 samples: thread t takes elements (h * 1024 + t) * E / 2048, h = 0, 1
+      uint32_t v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int want = (h * THREADS + tid) * E / (2 * THREADS);
+        v[h] = 0u;
+#pragma unroll
+        for (int i = 0; i < E; ++i)
+          if (i == want) v[h] = key[i];
+      }
+      // every column of [0, 1024 E) is sampled with probability 2 / E
+      uint32_t A2, B2;
+      bracket_core<THREADS, 2>(v, (float)k_rem * 2.0f / (float)E, sm.ss, sm.sh, &A2, &B2);
+      uint32_t c_in = 0, c_cand = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        c_in += key[i] > A2;
+        c_cand += key[i] >= B2 && key[i] <= A2;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        c_in += (uint32_t)__shfl_xor((int)c_in, o, 64);
+        c_cand += (uint32_t)__shfl_xor((int)c_cand, o, 64);
+      }
+      if (lane == 0) {
+        sm.sh.wred[wave * 4 + 0] = c_in;
+        sm.sh.wred[wave * 4 + 1] = c_cand;
+      }
+      __syncthreads();
+      c_in = 0;
+      c_cand = 0;
+      for (int i = 0; i < NWAVES; ++i) {
+        c_in += sm.sh.wred[i * 4 + 0];
+        c_cand += sm.sh.wred[i * 4 + 1];
+      }
+      __syncthreads();
+      if (c_in <= k_rem && k_rem <= c_in + c_cand) {
+        A = A2;
+        Bt = B2;
+        m = k_rem - c_in;
+      }
+    }
+  }
+
+  // ---- 3 -------------------------------------------------------------------
+  KeyThreshold th{0u, 0u, 0, 0, true, 0u};
+  if (m > 0)
+    th = key_threshold<E, 0>(key, Bt, A, m, sm.ts, sm.sh);
+
+  // ---- 4 -------------------------------------------------------------------
+  // lane i of each wave keeps the ballots of element i: one store per lane
+  uint64_t my_cb = 0ull, my_tb = 0ull;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const uint32_t k = key[i];
+    bool chosen = k > A || i * THREADS + tid == fcol;
+    bool tie = false;
+    if (m > 0 && k >= Bt && k <= A) {
+      const int cmp = th_cmp(th, k);
+      chosen = chosen || cmp > 0 || (cmp == 0 && th.take_all);
+      tie = cmp == 0 && !th.take_all;
+    }
+    const uint64_t cb = __ballot(chosen), tb = __ballot(tie);
+    if (lane == i) {
+      my_cb = cb;
+      my_tb = tb;
+    }
+  }
+  if (lane < E) {
+    sm.bitmap[lane * NWAVES + wave] = my_cb;
+    sm.tiemap[lane * NWAVES + wave] = my_tb;
+  }
+  __syncthreads();
+  read_back(a, row, th, (int)((a.n + 31) / 32), reinterpret_cast<uint32_t*>(sm.bitmap),
+            reinterpret_cast<const uint32_t*>(sm.tiemap), sm.sh);
+}
+
+
+// Path choice.  One CU works through a register-held row at a few entries
+// per lane-cycle, so a row of more than 16K entries is faster spread over
+// many workgroups (split path) when there are too few rows to fill the chip.
 bool sampled_ok(int64_t n, int k) { return n >= 4 * SAMPLE && n <= MAX_N_FAST && k <= KFAST; }
-bool split_path(int64_t R, int64_t n, int k) { return R < 256 && sampled_ok(n, k); }
+bool rows_path(int64_t R, int64_t n) { return n <= 16 * THREADS || (R >= 256 && n <= 32 * THREADS); }
+bool split_path(int64_t R, int64_t n, int k) {
+  return !rows_path(R, n) && R < 256 && sampled_ok(n, k);
+}
 
 }  // namespace
 
@@ -901,6 +1157,13 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
                               int force_last, int k, int32_t* out, int64_t o_stride, void* ws,
                               hipStream_t s) {
   SelArgs a{scores, s_stride, ids, id_stride, forced, force_last, n, k, out, o_stride};
+  if (rows_path(R, n)) {
+    const dim3 grid((unsigned)R), block(THREADS);
+    if (n <= 8 * THREADS) hipLaunchKernelGGL(select_rows_kernel<8>, grid, block, 0, s, a);
+    else if (n <= 16 * THREADS) hipLaunchKernelGGL(select_rows_kernel<16>, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(select_rows_kernel<32>, grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if (split_path(R, n, k)) {
     const int nchunks = (int)((n + CHUNK - 1) / CHUNK);
     Slot* slots = static_cast<Slot*>(ws);

@@ -4,11 +4,16 @@
 // latent row, in one pass with an online softmax whose denominator also holds
 // a learnable per-head sink logit.
 //
-// Work decomposition.  A workgroup (4 waves) owns one query and a contiguous
-// range of its row list (i < K: latent sel[i]; K <= i < K+W: window positions
-// t-W+1 .. t).  Few queries (decode) -> the row list is split over several
-// workgroups and a second kernel merges the partial (max, sum, numerator)
-// triples; many queries (prefill) -> one workgroup per query, no merge.
+// Work decomposition.  A query's rows come in tiles of 32: ceil(K/32) latent
+// tiles (rows sel[i]) then ceil(W/32) window tiles (raw positions
+// t-W+1 .. t), so a tile never mixes the two sources and its loads are
+// straight-line code for one format.  A workgroup (4 waves) owns one query
+// and a contiguous range of its tiles.  Few queries (decode) -> the tiles are
+// split over several workgroups and a second kernel merges the partial (max,
+// sum, numerator) triples; many queries (prefill) -> one workgroup per query,
+// no merge.  Rows that do not exist (sel id < 0 or past the cache, a window
+// position before 0, the padding of a partial tile) load row 0 of their
+// source and are zeroed and masked.
 //
 // Per tile of 32 rows:
 //   * every row is gathered from HBM once (1 KiB bf16, or 256 B NVFP4 codes +
@@ -24,6 +29,8 @@
 //     whose B operand is exactly the P values the lane already holds.
 // FP8 window rows keep their per-token scale out of the MFMA: it multiplies
 // the logit of that row and its P weight.
+#include <atomic>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -64,84 +71,59 @@ struct AttnArgs {
   float* lse;
   float* part;       // [R][splits][64][PART] when splits > 1
   int splits;
-  int rows_per_split;
+  int tiles_lat;     // ceil(K / TILE), 0 when the cache is empty
+  int tiles_win;     // ceil(W / TILE)
+  int tiles_per_split;
 };
+
+constexpr int kMaxDevices = 64;
+constexpr float RESCALE_TAU = 8.0f;  // largest log-weight above the reference point
+constexpr int SEL_CAP = 2048;       // largest K: a split's sel entries are cached in LDS
 
 struct Smem {
   uint16_t kv[TILE][KV_LD];
   uint16_t vt[D][VT_LD];
   float rscale[TILE];
   int rvalid[TILE];
+  int32_t selc[SEL_CAP];  // sel[lat_beg ..] of this workgroup's latent rows
 };
 
-struct RowSrc {
-  const void* base;  // row start (codes)
-  const uint8_t* sc; // NVFP4 group scales of the row
-  float rscale;      // FP8 window token scale, else 1
-  int fmt;           // 0 = no row
-};
-
-__device__ __forceinline__ RowSrc row_source(const AttnArgs& a, int b, int64_t t,
-                                             const int32_t* selrow, int i, int row_end) {
-  RowSrc r{nullptr, nullptr, 1.0f, 0};
-  if (i >= row_end) return r;
-  if (i < a.K) {
-    const int32_t gidx = selrow[i];
-    if (gidx < 0 || gidx >= a.n_cache) return r;
-    const int64_t row = (int64_t)b * a.lat_sb + gidx;
-    if (a.lat_fmt == FMT_NVFP4) {
-      r.base = static_cast<const uint8_t*>(a.lat) + row * (D / 2);
-      r.sc = a.lat_scale + row * (D / 16);
-    } else {
-      r.base = static_cast<const uint16_t*>(a.lat) + row * D;
-    }
-    r.fmt = a.lat_fmt;
-    return r;
-  }
-  const int64_t pos = t - (a.W - 1) + (i - a.K);
-  if (pos < 0) return r;
-  const int64_t slot = (int64_t)b * a.win_sb + pos % a.W_cap;
-  if (a.win_fmt == FMT_FP8) {
-    r.base = static_cast<const uint8_t*>(a.win) + slot * D;
-    r.rscale = a.win_scale[slot];
-  } else {
-    r.base = static_cast<const uint16_t*>(a.win) + slot * D;
-  }
-  r.fmt = a.win_fmt;
-  return r;
+// 8 consecutive dims [8p, 8p+8) of a row as bf16 bits, by source format.
+// Every E2M1 x E4M3 product and every E4M3 value is exactly a bf16 value.
+__device__ __forceinline__ u32x4 bf16_piece(const uint16_t* row, int p) {
+  return *reinterpret_cast<const u32x4*>(row + 8 * p);
 }
 
-// 8 consecutive dims [8p, 8p+8) of a row as bf16 bits (scale of FP8 rows not applied)
-__device__ __forceinline__ u32x4 load_piece(const RowSrc& r, int p) {
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (r.fmt == FMT_BF16) {
-    v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(r.base) + 8 * p);
-  } else if (r.fmt == FMT_FP8) {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(r.base) + 8 * p);
+__device__ __forceinline__ u32x4 fp8_codes_to_bf16(uint32_t c0, uint32_t c1) {
+  const u32x2 c = {c0, c1};
+  u32x4 v;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint32_t w = c[h];
-        v[2 * h + i] = e4m3_to_bf16((w >> (16 * i)) & 0xffu) |
-                       (e4m3_to_bf16((w >> (16 * i + 8)) & 0xffu) << 16);
-      }
-  } else if (r.fmt == FMT_NVFP4) {
-    const uint32_t c = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(r.base) + 4 * p);
-    const float s = e4m3_to_f32(r.sc[p >> 1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t byte = (c >> (8 * i)) & 0xffu;
-      // products of an E2M1 value and an E4M3 scale are exact in bf16
-      v[i] = (__float_as_uint(e2m1_to_f32(byte & 15u) * s) >> 16) |
-             (__float_as_uint(e2m1_to_f32(byte >> 4) * s) & 0xffff0000u);
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w = c[h];
+      v[2 * h + i] = e4m3_to_bf16((w >> (16 * i)) & 0xffu) |
+                     (e4m3_to_bf16((w >> (16 * i + 8)) & 0xffu) << 16);
     }
+  return v;
+}
+
+// raw NVFP4 piece: 4 code bytes (8 nibbles) and the group's E4M3 scale byte
+__device__ __forceinline__ u32x4 nvfp4_piece(uint32_t codes, uint32_t scale_byte) {
+  const float s = e4m3_to_f32(scale_byte);
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t byte = (codes >> (8 * i)) & 0xffu;
+    v[i] = (__float_as_uint(e2m1_to_f32(byte & 15u) * s) >> 16) |
+           (__float_as_uint(e2m1_to_f32(byte >> 4) * s) & 0xffff0000u);
   }
   return v;
 }
 
 // One wave per SIMD: the 64 heads x 512 fp32 accumulators, the query
 // operand and the next tile's rows take more than half of the register file.
+template <int LF, int WF>
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
@@ -152,9 +134,20 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   const int b = (int)(r / a.Tq), j = (int)(r % a.Tq);
   const int64_t t = a.q_pos[r];
   const int32_t* selrow = a.sel + r * a.sel_sb;
-  const int n_rows = a.K + a.W;
-  const int row_beg = split * a.rows_per_split;
-  const int row_end = min(n_rows, row_beg + a.rows_per_split);
+  const int n_tiles = a.tiles_lat + a.tiles_win;
+  const int tile_beg = split * a.tiles_per_split;
+  const int tile_end = min(n_tiles, tile_beg + a.tiles_per_split);
+
+  // this workgroup's sel entries, loaded once before anything else: the
+  // row gathers of later tiles then need no dependent global load
+  const int lat_beg = TILE * tile_beg;
+  const int n_lat = max(0, min(TILE * min(tile_end, a.tiles_lat), a.K) - lat_beg);
+  int32_t sv[SEL_CAP / 256];
+#pragma unroll
+  for (int m = 0; m < SEL_CAP / 256; ++m) {
+    const int idx = tid + 256 * m;
+    sv[m] = idx < n_lat ? selrow[lat_beg + idx] : -1;
+  }
 
   // Q^T operand of this wave's 16 heads: lane holds head 16w + l%16,
   // dims 32c + 8g .. +7 for c = 0..15
@@ -162,6 +155,11 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   bf16x8 qop[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+
+#pragma unroll
+  for (int m = 0; m < SEL_CAP / 256; ++m)
+    if (tid + 256 * m < n_lat) sm.selc[tid + 256 * m] = sv[m];
+  __syncthreads();
 
   f32x4 o[32];
 #pragma unroll
@@ -175,68 +173,127 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 
   // A tile's rows are gathered into registers one tile ahead: the loads of
   // tile i+1 are in flight while tile i is computed from LDS.
+  // A tile's raw bytes are gathered into registers one tile ahead: the
+  // loads of tile i+1 are in flight while tile i is computed from LDS.
+  // Nothing reads them before stage() (decode and masking happen there), so
+  // issuing them never waits on memory.
   struct Staged {
-    u32x4 v[2][4];
-    float rs[4];
+    u32x4 v[2][4];  // bf16: 8 values; FP8: .xy = 8 codes; NVFP4: .x = codes, .y = scale byte
+    float rs[4];    // window token scale (FP8)
     int ok[4];
+    bool lat;       // latent tile (else window)
   } nxt;
-  auto gather = [&](int i0, Staged& st) {
-    RowSrc src[4];
+  // tile tt: rows 4rq .. 4rq+3 of this lane, pieces p0 and p0 + 32
+  auto gather = [&](int tt, Staged& st) {
+    st.lat = tt < a.tiles_lat;
+    if (st.lat) {
+      int64_t row[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) src[x] = row_source(a, b, t, selrow, i0 + 4 * rq + x, row_end);
+      for (int x = 0; x < 4; ++x) {
+        const int i = TILE * tt + 4 * rq + x;
+        const int32_t gidx = i < a.K ? sm.selc[i - lat_beg] : -1;
+        st.ok[x] = gidx >= 0 && gidx < a.n_cache;
+        row[x] = (int64_t)b * a.lat_sb + (st.ok[x] ? gidx : 0);
+        st.rs[x] = 1.0f;
+      }
 #pragma unroll
-    for (int pp = 0; pp < 2; ++pp)
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) st.v[pp][x] = load_piece(src[x], p0 + 32 * pp);
+        for (int x = 0; x < 4; ++x) {
+          const int p = p0 + 32 * pp;
+          if (LF == FMT_NVFP4) {
+            const uint8_t* codes = static_cast<const uint8_t*>(a.lat) + row[x] * (D / 2);
+            st.v[pp][x][0] = *reinterpret_cast<const uint32_t*>(codes + 4 * p);
+            st.v[pp][x][1] = a.lat_scale[row[x] * (D / 16) + (p >> 1)];
+          } else {
+            st.v[pp][x] = bf16_piece(static_cast<const uint16_t*>(a.lat) + row[x] * D, p);
+          }
+        }
+    } else {
+      int64_t slot[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      st.rs[x] = src[x].rscale;
-      st.ok[x] = src[x].fmt != 0;
+      for (int x = 0; x < 4; ++x) {
+        const int jw = TILE * (tt - a.tiles_lat) + 4 * rq + x;
+        const int64_t pos = t - (a.W - 1) + jw;
+        st.ok[x] = jw < a.W && pos >= 0;
+        slot[x] = (int64_t)b * a.win_sb + (st.ok[x] ? pos % a.W_cap : 0);
+        st.rs[x] = WF == FMT_FP8 ? a.win_scale[slot[x]] : 1.0f;
+      }
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int p = p0 + 32 * pp;
+          if (WF == FMT_FP8) {
+            const u32x2 c = *reinterpret_cast<const u32x2*>(
+                static_cast<const uint8_t*>(a.win) + slot[x] * D + 8 * p);
+            st.v[pp][x][0] = c[0];
+            st.v[pp][x][1] = c[1];
+          } else {
+            st.v[pp][x] = bf16_piece(static_cast<const uint16_t*>(a.win) + slot[x] * D, p);
+          }
+        }
     }
+  };
+  // decode to bf16, zero the rows that do not exist
+  auto decoded = [&](const Staged& st, int pp, int x) -> u32x4 {
+    u32x4 v = st.v[pp][x];
+    if (st.lat && LF == FMT_NVFP4) v = nvfp4_piece(v[0], v[1]);
+    if (!st.lat && WF == FMT_FP8) v = fp8_codes_to_bf16(v[0], v[1]);
+    return st.ok[x] ? v : (u32x4){0u, 0u, 0u, 0u};
   };
   auto stage = [&](const Staged& st) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int p = p0 + 32 * pp;
+      u32x4 v[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = st.v[pp][x];
+      for (int x = 0; x < 4; ++x) {
+        v[x] = decoded(st, pp, x);
+        *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = v[x];
+      }
       // transpose: dim 8p+d gets the four rows' values side by side
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const int w32 = d >> 1, sh = 16 * (d & 1);
         u32x2 pr;
-        pr[0] = ((st.v[pp][0][w32] >> sh) & 0xffffu) | (((st.v[pp][1][w32] >> sh) & 0xffffu) << 16);
-        pr[1] = ((st.v[pp][2][w32] >> sh) & 0xffffu) | (((st.v[pp][3][w32] >> sh) & 0xffffu) << 16);
+        pr[0] = ((v[0][w32] >> sh) & 0xffffu) | (((v[1][w32] >> sh) & 0xffffu) << 16);
+        pr[1] = ((v[2][w32] >> sh) & 0xffffu) | (((v[3][w32] >> sh) & 0xffffu) << 16);
         *reinterpret_cast<u32x2*>(&sm.vt[8 * p + d][4 * rq]) = pr;
       }
     }
     if (wave == 0 && (lane >> 3) == 0) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        sm.rscale[4 * rq + x] = st.rs[x];
+        sm.rscale[4 * rq + x] = st.ok[x] ? st.rs[x] : 1.0f;
         sm.rvalid[4 * rq + x] = st.ok[x];
       }
     }
   };
 
-  if (row_beg < row_end) gather(row_beg, nxt);
-  for (int i0 = row_beg; i0 < row_end; i0 += TILE) {
+  if (tile_beg < tile_end) gather(tile_beg, nxt);
+  for (int tt = tile_beg; tt < tile_end; ++tt) {
     __syncthreads();  // previous tile fully consumed
     stage(nxt);
     __syncthreads();
-    if (i0 + TILE < row_end) gather(i0 + TILE, nxt);
+    if (tt + 1 < tile_end) gather(tt + 1, nxt);
 
-    // S^T = KV . Q^T for rows [16st, 16st+16)
-    f32x4 s[2];
+    // S^T = KV . Q^T for rows [16st, 16st+16): the two row halves are
+    // independent accumulation chains; their K operands are read in pairs
+    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 16; c += 2) {
+      bf16x8 kop[2][2];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&sm.kv[16 * st + hl][32 * c + 8 * g]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], acc, 0, 0, 0);
-      }
-      s[st] = acc;
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          kop[st][u] = *reinterpret_cast<const bf16x8*>(&sm.kv[16 * st + hl][32 * (c + u) + 8 * g]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st][u], qop[c + u], s[st], 0, 0, 0);
     }
     // logits of rows 16st + 4g + i for head l%16
     float lg[2][4], rs[2][4];
@@ -261,32 +318,48 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int i = 0; i < 4; ++i) mine |= sm.rvalid[16 * st + 4 * g + i] != 0;
     seen |= __ballot(mine) != 0;
     if (!seen) continue;
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
-    m_run = m_new;
+    // Lazy rescaling: m_run is a reference point, not necessarily the
+    // running max; it moves only when a logit exceeds it by more than
+    // RESCALE_TAU, so the weights stay below e^RESCALE_TAU and the
+    // accumulators are rescaled rarely (never when the head had no row yet,
+    // its accumulators being zero).  The sums are the same, each term
+    // relative to the final reference.
+    const bool grow = mt > m_run + RESCALE_TAU;
+    const bool scale_acc = grow && m_run != -INFINITY;
+    if (__ballot(scale_acc) != 0) {
+      const float alpha = scale_acc ? expf(m_run - mt) : 1.0f;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) o[i] *= alpha;
+    }
+    if (grow) m_run = mt;
     float psum = 0.f;
     bf16x8 pop;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = expf(lg[st][i] - m_new);
+        const float p = expf(lg[st][i] - m_run);
         psum += p;
         pop[4 * st + i] = (__bf16)(p * rs[st][i]);
       }
-    l_run = l_run * alpha + psum;
-    if (alpha != 1.0f) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] *= alpha;
-    }
+    l_run += psum;
     // O^T += V^T . P^T ; A lane: dim 16T + l%16, k-slots = rows 4g..4g+3, 16+4g..16+4g+3
+    // operands read 4 MFMAs ahead so that LDS latency overlaps the MFMAs
 #pragma unroll
-    for (int T = 0; T < 32; ++T) {
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[16 * T + hl][4 * g]);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[16 * T + hl][16 + 4 * g]);
-      const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, vv);
-      o[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, o[T], 0, 0, 0);
+    for (int T0 = 0; T0 < 32; T0 += 4) {
+      bf16x8 vop[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int T = T0 + u;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[16 * T + hl][4 * g]);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[16 * T + hl][16 + 4 * g]);
+        const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
+        vop[u] = __builtin_bit_cast(bf16x8, vv);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        o[T0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[u], pop, o[T0 + u], 0, 0, 0);
     }
   }
 
@@ -371,12 +444,15 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 }  // namespace
 
-// Tiles of 32 rows handled by one workgroup: many query rows -> one
-// workgroup per query (no merge); few -> split the row list so that roughly
-// 256+ workgroups run, at least 2 tiles each (each split costs a 128 KiB
-// fp32 partial that the merge reads back).
-static int attn_tiles_per_split(int64_t R, int n_rows) {
-  const int tiles = (n_rows + TILE - 1) / TILE;
+// Tiles of one query: latent tiles then window tiles (never mixed).
+static int attn_tiles(int K, int W) { return (K + TILE - 1) / TILE + (W + TILE - 1) / TILE; }
+
+// Tiles handled by one workgroup: many query rows -> one workgroup per
+// query (no merge); few -> split the tiles so that roughly 256+ workgroups
+// run, at least 2 tiles each (each split costs a 128 KiB fp32 partial that
+// the merge reads back).
+static int attn_tiles_per_split(int64_t R, int K, int W) {
+  const int tiles = attn_tiles(K, W);
   if (R >= 192 || tiles <= 2) return tiles > 0 ? tiles : 1;
   const int64_t want = (256 + R - 1) / R;  // splits wanted per query
   int tps = (int)((tiles + want - 1) / want);
@@ -385,15 +461,15 @@ static int attn_tiles_per_split(int64_t R, int n_rows) {
   return tps;
 }
 
-int attn_splits(int64_t R, int n_rows) {
-  const int tiles = (n_rows + TILE - 1) / TILE;
-  const int tps = attn_tiles_per_split(R, n_rows);
+int attn_splits(int64_t R, int K, int W) {
+  const int tiles = attn_tiles(K, W);
+  const int tps = attn_tiles_per_split(R, K, W);
   const int s = (tiles + tps - 1) / tps;
   return s < 1 ? 1 : s;
 }
 
-size_t attn_workspace_bytes(int64_t R, int n_rows) {
-  const int s = attn_splits(R, n_rows);
+size_t attn_workspace_bytes(int64_t R, int K, int W) {
+  const int s = attn_splits(R, K, W);
   if (s <= 1) return 0;
   return (size_t)R * s * HQ * PART * sizeof(float);
 }
@@ -406,17 +482,43 @@ hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const 
                               float scale, void* out, int64_t out_sb, float* lse, void* ws,
                               hipStream_t s) {
   const int64_t R = (int64_t)B * Tq;
-  const int n_rows = K + W;
-  const int splits = attn_splits(R, n_rows);
-  const int tiles_per_split = attn_tiles_per_split(R, n_rows);
+  const int splits = attn_splits(R, K, W);
+  const int tiles_per_split = attn_tiles_per_split(R, K, W);
+  // with an empty cache no latent row exists: its tiles are dropped (they
+  // would only be masked rows, and the cache pointer may be null)
+  const int tiles_lat = n_cache > 0 ? (K + TILE - 1) / TILE : 0;
+  const int tiles_win = (W + TILE - 1) / TILE;
   AttnArgs a{(const uint16_t*)q, q_sb, Tq, lat, lat_fmt, (const uint8_t*)lat_scale, lat_sb,
              n_cache, sel, K, sel_sb, win, win_fmt, win_scale, W, W_cap, win_sb, q_pos, sink,
-             scale, (uint16_t*)out, out_sb, lse, (float*)ws, splits, tiles_per_split * TILE};
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)sparse_attn_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(sparse_attn_kernel, dim3((unsigned)R, (unsigned)splits), dim3(256),
-                     sizeof(Smem), s, a);
+             scale, (uint16_t*)out, out_sb, lse, (float*)ws, splits, tiles_lat, tiles_win,
+             tiles_per_split};
+  // the dynamic LDS limit is raised once per device and kernel
+  static std::atomic<int> attr_set[kMaxDevices];
+  int dev = 0;
+  hipError_t e0 = hipGetDevice(&dev);
+  if (e0 != hipSuccess) return e0;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  const void* kernels[4] = {(const void*)sparse_attn_kernel<FMT_BF16, FMT_BF16>,
+                            (const void*)sparse_attn_kernel<FMT_BF16, FMT_FP8>,
+                            (const void*)sparse_attn_kernel<FMT_NVFP4, FMT_BF16>,
+                            (const void*)sparse_attn_kernel<FMT_NVFP4, FMT_FP8>};
+  if (!attr_set[dev].load(std::memory_order_acquire)) {
+    for (const void* k : kernels) {
+      e0 = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
+      if (e0 != hipSuccess) return e0;
+    }
+    attr_set[dev].store(1, std::memory_order_release);
+  }
+  const dim3 grid((unsigned)R, (unsigned)splits), block(256);
+  const bool lat4 = lat_fmt == FMT_NVFP4, win8 = win_fmt == FMT_FP8;
+  if (!lat4 && !win8)
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_BF16>), grid, block, sizeof(Smem), s, a);
+  else if (!lat4)
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_FP8>), grid, block, sizeof(Smem), s, a);
+  else if (!win8)
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_NVFP4, FMT_BF16>), grid, block, sizeof(Smem), s, a);
+  else
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_NVFP4, FMT_FP8>), grid, block, sizeof(Smem), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)R, HQ / 4), dim3(256), 0, s, a);

@@ -103,9 +103,14 @@ def test_scan_cand_select_stages(name, kw):
     (40, 5, 300, 17, "ties"), (41, 3, 65536, 2048, "last"), (42, 7, 16384, 512, "ids"),
     (43, 4, 1000, 1200, "plain"), (44, 6, 5000, 64, "forced"), (45, 2, 777, 1, "forced"),
     (46, 3, 4096, 512, "allequal"),
-    # few long rows take the split path; all-equal keys defeat its bracket
+    # rows of up to 65,536 entries are held in registers (8, 16, 32 or 64 per
+    # thread); all-equal keys defeat the sampled bracket
     (47, 2, 65536, 2048, "allequal"), (48, 3, 65536, 2048, "forced"), (49, 5, 20000, 100, "ids"),
-    (51, 300, 16384, 512, "plain"),   # many rows: one workgroup per row, sampled
+    (51, 300, 16384, 512, "plain"), (55, 4, 65536, 2048, "ids"), (56, 3, 1, 1, "plain"),
+    (57, 3, 8193, 700, "last"), (58, 2, 32769, 2048, "ties"), (59, 3, 40000, 39000, "plain"),
+    # longer rows: few rows take the split path, else one workgroup per row from memory
+    (60, 2, 100000, 2048, "allequal"), (61, 3, 131072, 2048, "forced"),
+    (62, 2, 140000, 300, "last"), (63, 2, 100000, 1500, "ids"),
 ])
 def test_select_edge_cases(seed, R, n, k, mode):
     rng = np.random.default_rng(seed)
