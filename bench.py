@@ -67,13 +67,20 @@ def prefill_indexer_flops(cfg) -> float:
     return float(pairs) * HI * DI * 2
 
 
-def source_hash(path):
-    if not os.path.exists(path):
-        return None
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+SCAN_SOURCES = ("index_scan.hip", "indexer.h", "device_common.h")
 
 
-def stored_traffic(kernel_src: str, workload: str):
+def source_hash(paths):
+    """Hash of the sources that define a kernel (None if one is missing)."""
+    h = hashlib.sha256()
+    for p in paths:
+        if not os.path.exists(p):
+            return None
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_src, workload: str):
     """HBM traffic of the dominant kernel from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source; else None."""
     p = os.path.join(ROOT, "profiles", "index_scan_1m_pmc.md")
@@ -206,7 +213,7 @@ def main():
     scan_gbs = sb["index_scan"] / scan_s / 1e9
     log(f"[bench] 1m: scan kernel {scan_us:.1f} us/launch = {scan_gbs:.0f} GB/s")
     del path
-    kernel_src = os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", "index_scan.hip")
+    kernel_src = [os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", f) for f in SCAN_SOURCES]
     workload = "1m"
     traffic = stored_traffic(kernel_src, workload)
     result = {
