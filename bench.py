@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the CSA2 hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: compressor (the newest
-pair of raw tokens -> one latent) -> candidate-source indexer scan with the
-fused block max -> block top-2048 (newest block kept) -> current-layer
-indexer over the 16,384 candidates -> position top-512 -> sparse attention
-over the 512 latents + 128-token window with sinks.
+A step is one pass of the whole path over one batch: candidate-source
+indexer scan with the fused block max -> block top-2048 (newest block kept)
+-> current-layer indexer over the 16,384 candidates -> position top-512 ->
+sparse attention over the 512 latents + 128-token window with sinks.  The 1M
+workloads have no compressor step (their cache is given); the compressor is
+timed inside the prefill pass, which pools its 8192-token chunk.
 
 The headline workload is 1M-context decode: 8 sequences x 1,048,576 raw
 tokens (524,288 bf16 latents of 512, bf16 index keys), one query each.

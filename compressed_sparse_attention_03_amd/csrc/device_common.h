@@ -98,3 +98,80 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 }  // namespace csa2
+
+namespace csa2 {
+
+// ---- wave-level reductions and scans over 64 lanes ------------------------
+// Within a row of 16 lanes the data moves by DPP (register-to-register):
+// quad permutes, half-row and row mirrors; across rows by ds_bpermute (two
+// steps) or, for the scan, by the row broadcasts of the GFX9 DPP set.  Every
+// lane gets the result (reductions) or its inclusive prefix (scan).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+template <typename F>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, F op) {
+  v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp_mov<0x141>(v));  // row_half_mirror: lane i <- 7-i of its 8
+  v = op(v, dpp_mov<0x140>(v));  // row_mirror: lane i <- 15-i of its 16
+  v = op(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  v = op(v, (uint32_t)__shfl_xor((int)v, 32, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a & b; });
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a | b; });
+}
+__device__ __forceinline__ int32_t wave_max_i(int32_t v) {
+  return (int32_t)wave_allreduce((uint32_t)v, [](uint32_t a, uint32_t b) {
+    return (int32_t)a > (int32_t)b ? a : b;
+  });
+}
+__device__ __forceinline__ int32_t wave_min_i(int32_t v) {
+  return (int32_t)wave_allreduce((uint32_t)v, [](uint32_t a, uint32_t b) {
+    return (int32_t)a < (int32_t)b ? a : b;
+  });
+}
+
+// Combination over the waves of a block of per-wave values stored at
+// vals[0 .. nw) (nw <= 16): lane l reads vals[l % 16] (or the identity), and
+// the 16 lanes of each row reduce by DPP; every lane gets the result.
+template <typename F>
+__device__ __forceinline__ uint32_t waves_combine(const uint32_t* vals, int nw, uint32_t identity,
+                                                  F op) {
+  const int i = threadIdx.x & 15;
+  uint32_t v = i < nw ? vals[i] : identity;
+  v = op(v, dpp_mov<0xB1>(v));
+  v = op(v, dpp_mov<0x4E>(v));
+  v = op(v, dpp_mov<0x141>(v));
+  v = op(v, dpp_mov<0x140>(v));
+  return v;
+}
+
+// inclusive prefix sum in lane order
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_mov<0x111>(v);        // row_shr:1 (lanes shifted in from outside the row add 0)
+  v += dpp_mov<0x112>(v);        // row_shr:2
+  v += dpp_mov<0x114>(v);        // row_shr:4
+  v += dpp_mov<0x118>(v);        // row_shr:8
+  v += dpp_mov<0x142, 0xA>(v);   // row_bcast:15 -> rows 1 and 3
+  v += dpp_mov<0x143, 0xC>(v);   // row_bcast:31 -> rows 2 and 3
+  return v;
+}
+
+}  // namespace csa2

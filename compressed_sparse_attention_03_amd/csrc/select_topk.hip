@@ -76,6 +76,7 @@ struct Shared {
   uint32_t hist[256];
   uint32_t wred[NWAVES * 4];
   uint32_t scan[NWAVES];
+  uint32_t wred_x[NWAVES];
   uint32_t bcast[8];
 };
 
@@ -83,12 +84,7 @@ struct Shared {
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = (int)(blockDim.x >> 6);
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh.scan[wave] = x;
   __syncthreads();
   uint32_t wpre = 0, tot = 0;
@@ -281,13 +277,56 @@ constexpr int KBIN = 2048;               // radix digit bins of the candidate se
 
 struct SampleSmem {
   uint32_t hist[NBIN];
-  uint32_t b1, b2;
+  uint32_t o1[4], o2[4];  // bins of the two bracket ranks (wave_find_bin)
 };
 
 struct ThreshSmem {
-  uint32_t hist[KBIN];
+  uint32_t hist[2][KBIN];  // radix digit bins, one buffer per pass parity
   uint32_t bc[4];
 };
+
+// Statistics of a candidate set: AND and OR of the keys (their common bits),
+// smallest and largest key, count; and the count of keys above the set.
+struct CandStats {
+  uint32_t kand, kor, kmin, kmax, count, above;
+};
+
+// Wave 0 scans NB bins from the top (bin NB-1 first), NB / 64 per lane:
+// finds the bin holding the `want`-th entry (want >= 1) and returns, through
+// out[0..2], the bin, the count in higher bins and the bin's count.  Only
+// wave 0 may call this; nothing is written if want exceeds the total.  Kept
+// out of line: inlined into the 1024-thread kernels it made the register
+// allocator spill.
+template <int NB>
+__device__ __noinline__ void wave_find_bin(const uint32_t* hist, uint32_t want, uint32_t* out) {
+  constexpr int PL = NB / 64;
+  const int lane = threadIdx.x & 63;
+  const uint32_t* mine = hist + NB - PL * (lane + 1);  // this lane's bins, ascending
+  uint32_t c[PL];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < PL; i += 4) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(mine + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      c[i + j] = x[j];
+      tot += x[j];
+    }
+  }
+  const uint32_t incl = wave_incl_scan(tot);  // over lanes (lane 0 = highest bins)
+  uint32_t above = incl - tot;
+  if (above < want && want <= incl) {  // one lane: walk its bins from the top
+#pragma unroll
+    for (int i = PL - 1; i >= 0; --i) {
+      if (above < want && want <= above + c[i]) {
+        out[0] = (uint32_t)(NB - PL * (lane + 1) + i);
+        out[1] = above;
+        out[2] = c[i];
+      }
+      above += c[i];
+    }
+  }
+}
 
 struct FinishSmem {
   uint32_t bitmap[MAX_N_FAST / 32];  // chosen columns
@@ -359,7 +398,6 @@ __device__ __forceinline__ void load_sample(const SelArgs& a, int64_t row, Elem 
 template <int NT, int SPT>
 __device__ void bracket_core(const uint32_t (&v)[SPT], float r, SampleSmem& ss, Shared& sh,
                              uint32_t* A, uint32_t* Bt) {
-  constexpr int BPT = NBIN / NT;  // histogram bins per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -370,22 +408,15 @@ __device__ void bracket_core(const uint32_t (&v)[SPT], float r, SampleSmem& ss, 
     }
   }
   for (int i = tid; i < NBIN; i += NT) ss.hist[i] = 0;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
   if (lane == 0) {
-    sh.wred[wave * 4 + 1] = kmin;
-    sh.wred[wave * 4 + 2] = kmax;
+    sh.wred[1 * NWAVES + wave] = kmin;
+    sh.wred[2 * NWAVES + wave] = kmax;
   }
   __syncthreads();
-  kmin = 0xffffffffu;
-  kmax = 0u;
-  for (int i = 0; i < NT / 64; ++i) {
-    kmin = min(kmin, sh.wred[i * 4 + 1]);
-    kmax = max(kmax, sh.wred[i * 4 + 2]);
-  }
+  kmin = waves_combine(sh.wred + 1 * NWAVES, NT / 64, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  kmax = waves_combine(sh.wred + 2 * NWAVES, NT / 64, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
   const float delta = 4.0f * sqrtf(r) + 16.0f;
   const int r_hi = (int)floorf(r - delta);
   const int r_lo = (int)ceilf(r + delta);
@@ -401,32 +432,18 @@ __device__ void bracket_core(const uint32_t (&v)[SPT], float r, SampleSmem& ss, 
   for (int i = 0; i < SPT; ++i)
     if (v[i]) atomicAdd(&ss.hist[(v[i] - kmin) >> w], 1u);
   if (tid == 0) {
-    ss.b1 = 0xffffffffu;
-    ss.b2 = 0xffffffffu;
+    ss.o1[0] = 0xffffffffu;
+    ss.o2[0] = 0xffffffffu;
   }
   __syncthreads();
-  // thread t owns bins NBIN-1-t*BPT-i (i < BPT), highest first: an exclusive
-  // prefix over t counts the samples in higher bins
-  uint32_t c[BPT];
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    c[i] = ss.hist[NBIN - 1 - tid * BPT - i];
-    cnt += c[i];
-  }
-  uint32_t tot;
-  uint32_t above = block_exclusive_scan(cnt, sh, &tot);
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    const uint32_t bin = NBIN - 1 - tid * BPT - i;
-    if (c[i]) {
-      if (r_hi >= 0 && above <= (uint32_t)r_hi && (uint32_t)r_hi < above + c[i]) ss.b1 = bin;
-      if (above <= (uint32_t)r_lo && (uint32_t)r_lo < above + c[i]) ss.b2 = bin;
-    }
-    above += c[i];
+  // wave 0 locates the bins of sample ranks r_hi and r_lo (0-based, from the
+  // top); a rank beyond the sample leaves its bin unset
+  if (wave == 0) {
+    if (r_hi >= 0) wave_find_bin<NBIN>(ss.hist, (uint32_t)r_hi + 1u, ss.o1);
+    wave_find_bin<NBIN>(ss.hist, (uint32_t)r_lo + 1u, ss.o2);
   }
   __syncthreads();
-  const uint32_t b1 = ss.b1, b2 = ss.b2;
+  const uint32_t b1 = ss.o1[0], b2 = ss.o2[0];
   // in: whole bins above b1; candidates: bins b2 .. b1
   if (r_hi < 0 || b1 == 0xffffffffu) {
     *A = 0xffffffffu;
@@ -531,94 +548,91 @@ __device__ __forceinline__ int th_cmp(const KeyThreshold& th, uint32_t key) {
   return d > D ? 1 : (d == D ? 0 : -1);
 }
 
+// Candidate statistics over P values per thread (key = value >> SHIFT,
+// candidate iff lo_key <= key <= hi_key), reduced over the block.
 template <int P, int SHIFT, typename T>
-__device__ KeyThreshold key_threshold(const T (&vals)[P], uint32_t lo_key, uint32_t hi_key,
-                                      uint32_t m, ThreshSmem& fs, Shared& sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto ck = [&](int i) {
-    const uint32_t k = (uint32_t)(vals[i] >> SHIFT);
-    return (k >= lo_key && k <= hi_key) ? k : 0u;
-  };
-  uint32_t kand = 0xffffffffu, kor = 0u, kmin = 0xffffffffu, kmax = 0u;
+__device__ CandStats cand_stats(const T (&vals)[P], uint32_t lo_key, uint32_t hi_key, Shared& sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  CandStats st{0xffffffffu, 0u, 0xffffffffu, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < P; ++i) {
-    const uint32_t k = ck(i);
-    if (k) {
-      kand &= k;
-      kor |= k;
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
+    const uint32_t k = (uint32_t)(vals[i] >> SHIFT);
+    if (k >= lo_key && k <= hi_key) {
+      st.kand &= k;
+      st.kor |= k;
+      st.kmin = min(st.kmin, k);
+      st.kmax = max(st.kmax, k);
+      ++st.count;
     }
+    st.above += k > hi_key;
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kand &= (uint32_t)__shfl_xor((int)kand, o, 64);
-    kor |= (uint32_t)__shfl_xor((int)kor, o, 64);
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  st.kand = wave_and(st.kand);
+  st.kor = wave_or(st.kor);
+  st.kmin = wave_min(st.kmin);
+  st.kmax = wave_max(st.kmax);
+  st.count = wave_sum(st.count);
+  st.above = wave_sum(st.above);
+  __syncthreads();  // earlier readers of sh.wred are done
   if (lane == 0) {
-    sh.wred[wave * 4 + 0] = kand;
-    sh.wred[wave * 4 + 1] = kor;
-    sh.wred[wave * 4 + 2] = kmin;
-    sh.wred[wave * 4 + 3] = kmax;
+    sh.wred[0 * NWAVES + wave] = st.kand;
+    sh.wred[1 * NWAVES + wave] = st.kor;
+    sh.wred[2 * NWAVES + wave] = st.kmin;
+    sh.wred[3 * NWAVES + wave] = st.kmax;
+    sh.scan[wave] = st.count;
+    sh.wred_x[wave] = st.above;
   }
   __syncthreads();
-  kand = 0xffffffffu;
-  kor = 0u;
-  kmin = 0xffffffffu;
-  kmax = 0u;
-  for (int i = 0; i < NWAVES; ++i) {
-    kand &= sh.wred[i * 4 + 0];
-    kor |= sh.wred[i * 4 + 1];
-    kmin = min(kmin, sh.wred[i * 4 + 2]);
-    kmax = max(kmax, sh.wred[i * 4 + 3]);
-  }
-  __syncthreads();
+  const int nw = (int)(blockDim.x >> 6);
+  CandStats t;
+  t.kand = waves_combine(sh.wred + 0 * NWAVES, nw, 0xffffffffu, [](uint32_t a, uint32_t b) { return a & b; });
+  t.kor = waves_combine(sh.wred + 1 * NWAVES, nw, 0u, [](uint32_t a, uint32_t b) { return a | b; });
+  t.kmin = waves_combine(sh.wred + 2 * NWAVES, nw, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+  t.kmax = waves_combine(sh.wred + 3 * NWAVES, nw, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  t.count = waves_combine(sh.scan, nw, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+  t.above = waves_combine(sh.wred_x, nw, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+  return t;
+}
+
+// Threshold over the candidates (see above).  `st` are their statistics
+// (cand_stats).  Per radix pass: the block adds its digits into one
+// histogram buffer, wave 0 scans it while the other waves clear the other
+// buffer, two barriers in all.  1024 threads.
+template <int P, int SHIFT, typename T>
+__device__ KeyThreshold key_threshold(const T (&vals)[P], uint32_t lo_key, uint32_t hi_key,
+                                      uint32_t m, const CandStats& st, ThreshSmem& fs) {
+  const int tid = threadIdx.x, wave = tid >> 6;
   KeyThreshold th;
-  const uint32_t varying = kand ^ kor;  // bits that differ between some keys
+  const uint32_t varying = st.kand ^ st.kor;  // bits that differ between some keys
   th.tz = varying ? __ffs(varying) - 1 : 0;
-  th.base = kmin >> th.tz;
-  const uint32_t spread = (kmax >> th.tz) - th.base;  // d in [0, spread]
-  int hi = spread ? 32 - __clz(spread) : 0;            // d < 2^hi
+  th.base = st.kmin >> th.tz;
+  const uint32_t spread = (st.kmax >> th.tz) - th.base;  // d in [0, spread]
+  int hi = spread ? 32 - __clz(spread) : 0;              // d < 2^hi
   uint32_t prefix = 0u;
-  uint32_t remaining = m, cbin = 0;
+  uint32_t remaining = m, cbin = st.count;  // spread 0: one key shared by all
   th.take_all = false;
   th.lo = 0;
-  // count of candidates sharing one key (spread 0)
-  if (hi == 0) {
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < P; ++i) c += ck(i) != 0;
-    uint32_t tot;
-    block_exclusive_scan(c, sh, &tot);
-    cbin = tot;
+  int cur = 0;
+  if (hi > 0) {
+    for (int i = tid; i < KBIN; i += THREADS) fs.hist[0][i] = 0;
+    __syncthreads();
   }
   while (hi > 0) {
     const int lo = hi > 11 ? hi - 11 : 0;
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
-    for (int i = tid; i < KBIN; i += THREADS) fs.hist[i] = 0;
-    __syncthreads();
+    uint32_t* h = fs.hist[cur];
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const uint32_t k = ck(i);
-      if (!k) continue;
+      const uint32_t k = (uint32_t)(vals[i] >> SHIFT);
+      if (k < lo_key || k > hi_key) continue;
       const uint32_t d = (k >> th.tz) - th.base;
-      if (hi >= 32 || (d >> hi) == (prefix >> hi)) atomicAdd(&fs.hist[(d >> lo) & dmask], 1u);
+      if (hi >= 32 || (d >> hi) == (prefix >> hi)) atomicAdd(&h[(d >> lo) & dmask], 1u);
     }
     __syncthreads();
-    // thread t owns bins 2047-2t and 2046-2t (highest first)
-    const uint32_t c0 = fs.hist[KBIN - 1 - 2 * tid], c1 = fs.hist[KBIN - 2 - 2 * tid];
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(c0 + c1, sh, &tot);
-    if (above < remaining && remaining <= above + c0) {
-      fs.bc[0] = KBIN - 1 - 2 * tid;
-      fs.bc[1] = above;
-      fs.bc[2] = c0;
-    } else if (above + c0 < remaining && remaining <= above + c0 + c1) {
-      fs.bc[0] = KBIN - 2 - 2 * tid;
-      fs.bc[1] = above + c0;
-      fs.bc[2] = c1;
+    if (wave == 0) {
+      wave_find_bin<KBIN>(h, remaining, fs.bc);
+    } else {
+      uint32_t* other = fs.hist[cur ^ 1];
+      for (int i = tid - 64; i < KBIN; i += THREADS - 64) other[i] = 0;
     }
     __syncthreads();
     const uint32_t dsel = fs.bc[0];
@@ -627,12 +641,14 @@ __device__ KeyThreshold key_threshold(const T (&vals)[P], uint32_t lo_key, uint3
     prefix |= dsel << lo;
     hi = lo;
     th.lo = lo;
-    __syncthreads();
+    cur ^= 1;
     if (remaining == cbin) break;
   }
   th.D = prefix;
   th.take_all = remaining == cbin;
   th.need = remaining;
+  // the next use of fs.bc (another pass, another row) comes after a barrier
+  // of the caller or of the next key_threshold's first pass
   return th;
 }
 
@@ -694,8 +710,10 @@ __device__ void finish_core(const SelArgs& a, int64_t row, int32_t fcol, uint32_
                             const uint32_t (&ccol)[CAND_PT], FinishSmem& fs, Shared& sh) {
   const int tid = threadIdx.x;
   KeyThreshold th{0u, 0u, 0, 0, true, 0u};
-  if (m > 0)
-    th = key_threshold<CAND_PT, 0>(ckey, 1u, 0xffffffffu, m, fs.ts, sh);
+  if (m > 0) {
+    const CandStats st = cand_stats<CAND_PT, 0>(ckey, 1u, 0xffffffffu, sh);
+    th = key_threshold<CAND_PT, 0>(ckey, 1u, 0xffffffffu, m, st, fs.ts);
+  }
   const int64_t n = a.n;
   const int words = (int)((n + 31) / 32);
   for (int i = tid; i < words; i += THREADS) {
@@ -1019,26 +1037,22 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
   uint32_t nv;
   if (a.ids) load_row_keys<E, true>(a, row, fid, key, &lv, &ff, &nv);
   else load_row_keys<E, false>(a, row, fid, key, &lv, &ff, &nv);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lv = max(lv, __shfl_xor(lv, o, 64));
-    ff = min(ff, __shfl_xor(ff, o, 64));
-    nv += (uint32_t)__shfl_xor((int)nv, o, 64);
-  }
+  lv = wave_max_i(lv);
+  ff = wave_min_i(ff);
+  nv = wave_sum(nv);
   if (lane == 0) {
-    sm.sh.wred[wave * 4 + 0] = (uint32_t)lv;
-    sm.sh.wred[wave * 4 + 1] = (uint32_t)ff;
-    sm.sh.wred[wave * 4 + 2] = nv;
+    sm.sh.wred[0 * NWAVES + wave] = (uint32_t)lv;
+    sm.sh.wred[1 * NWAVES + wave] = (uint32_t)ff;
+    sm.sh.wred[2 * NWAVES + wave] = nv;
   }
   __syncthreads();
-  lv = -1;
-  ff = 0x7fffffff;
-  nv = 0;
-  for (int i = 0; i < NWAVES; ++i) {
-    lv = max(lv, (int32_t)sm.sh.wred[i * 4 + 0]);
-    ff = min(ff, (int32_t)sm.sh.wred[i * 4 + 1]);
-    nv += sm.sh.wred[i * 4 + 2];
-  }
+  lv = (int32_t)waves_combine(sm.sh.wred + 0 * NWAVES, NWAVES, 0xffffffffu, [](uint32_t a, uint32_t b) {
+    return (int32_t)a > (int32_t)b ? a : b;
+  });
+  ff = (int32_t)waves_combine(sm.sh.wred + 1 * NWAVES, NWAVES, 0x7fffffffu, [](uint32_t a, uint32_t b) {
+    return (int32_t)a < (int32_t)b ? a : b;
+  });
+  nv = waves_combine(sm.sh.wred + 2 * NWAVES, NWAVES, 0u, [](uint32_t a, uint32_t b) { return a + b; });
   __syncthreads();
   int32_t fcol = -1;
   if (a.force_last) fcol = lv;
@@ -1053,6 +1067,8 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
 
   // ---- 2 -------------------------------------------------------------------
   uint32_t A = 0u, Bt = 1u, m = 0u;  // A = 0: every valid key is in
+  CandStats st{0u, 0u, 0u, 0u, 0u, 0u};
+  bool have_st = false;
   if (n_rest > k_rem) {
     A = 0xffffffffu;  // nothing in, every valid key a candidate
     m = k_rem;
@@ -1070,41 +1086,23 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
       // every column of [0, 1024 E) is sampled with probability 2 / E
       uint32_t A2, B2;
       bracket_core<THREADS, 2>(v, (float)k_rem * 2.0f / (float)E, sm.ss, sm.sh, &A2, &B2);
-      uint32_t c_in = 0, c_cand = 0;
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        c_in += key[i] > A2;
-        c_cand += key[i] >= B2 && key[i] <= A2;
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        c_in += (uint32_t)__shfl_xor((int)c_in, o, 64);
-        c_cand += (uint32_t)__shfl_xor((int)c_cand, o, 64);
-      }
-      if (lane == 0) {
-        sm.sh.wred[wave * 4 + 0] = c_in;
-        sm.sh.wred[wave * 4 + 1] = c_cand;
-      }
-      __syncthreads();
-      c_in = 0;
-      c_cand = 0;
-      for (int i = 0; i < NWAVES; ++i) {
-        c_in += sm.sh.wred[i * 4 + 0];
-        c_cand += sm.sh.wred[i * 4 + 1];
-      }
-      __syncthreads();
-      if (c_in <= k_rem && k_rem <= c_in + c_cand) {
+      // one reduction: the counts that check the bracket and the statistics
+      // of its candidates
+      const CandStats s2 = cand_stats<E, 0>(key, B2, A2, sm.sh);
+      if (s2.above <= k_rem && k_rem <= s2.above + s2.count) {
         A = A2;
         Bt = B2;
-        m = k_rem - c_in;
+        m = k_rem - s2.above;
+        st = s2;
+        have_st = true;
       }
     }
+    if (!have_st && m > 0) st = cand_stats<E, 0>(key, Bt, A, sm.sh);
   }
 
   // ---- 3 -------------------------------------------------------------------
   KeyThreshold th{0u, 0u, 0, 0, true, 0u};
-  if (m > 0)
-    th = key_threshold<E, 0>(key, Bt, A, m, sm.ts, sm.sh);
+  if (m > 0) th = key_threshold<E, 0>(key, Bt, A, m, st, sm.ts);
 
   // ---- 4 -------------------------------------------------------------------
   // lane i of each wave keeps the ballots of element i: one store per lane

@@ -394,29 +394,25 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 }
 
 // merge the split partials of one query: grid (R, 16), 256 threads =
-// 4 heads x 64 threads x 8 dims.  All of a thread's partial loads are issued
-// before any is used (splits are at most MAX_SPLITS).
-constexpr int MAX_SPLITS = 16;
+// 4 heads x 64 threads x 8 dims.  The (reference, sum) pairs of all splits
+// are read first, then the numerators in batches of MERGE_BATCH splits whose
+// loads are all issued before any is used.
+constexpr int MAX_SPLITS = 32;
+constexpr int MERGE_BATCH = 8;
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t r = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
   const float sk = a.sink[h];
+  const float* part = a.part + (r * a.splits * HQ + h) * PART;  // split s at + s * HQ * PART
   float ms[MAX_SPLITS], ls[MAX_SPLITS];
-  f32x4 x0[MAX_SPLITS], x1[MAX_SPLITS];
 #pragma unroll
   for (int s = 0; s < MAX_SPLITS; ++s) {
+    ms[s] = -INFINITY;
+    ls[s] = 0.f;
     if (s < a.splits) {
-      const float* pp = a.part + ((r * a.splits + s) * HQ + h) * PART;
-      ms[s] = pp[D];
-      ls[s] = pp[D + 1];
-      x0[s] = *reinterpret_cast<const f32x4*>(pp + d0);
-      x1[s] = *reinterpret_cast<const f32x4*>(pp + d0 + 4);
-    } else {
-      ms[s] = -INFINITY;
-      ls[s] = 0.f;
-      x0[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      x1[s] = x0[s];
+      ms[s] = part[(int64_t)s * HQ * PART + D];
+      ls[s] = part[(int64_t)s * HQ * PART + D + 1];
     }
   }
   float M = sk;
@@ -425,13 +421,29 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   float Z = expf(sk - M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < MAX_SPLITS; ++s) {
-    const float e = ms[s] == -INFINITY ? 0.f : expf(ms[s] - M);
-    Z += ls[s] * e;
+  for (int s0 = 0; s0 < MAX_SPLITS; s0 += MERGE_BATCH) {
+    if (s0 >= a.splits) break;
+    f32x4 x0[MERGE_BATCH], x1[MERGE_BATCH];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] += x0[s][i] * e;
-      acc[4 + i] += x1[s][i] * e;
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      x0[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      x1[u] = x0[u];
+      if (s0 + u < a.splits) {
+        const float* pp = part + (int64_t)(s0 + u) * HQ * PART + d0;
+        x0[u] = *reinterpret_cast<const f32x4*>(pp);
+        x1[u] = *reinterpret_cast<const f32x4*>(pp + 4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MERGE_BATCH; ++u) {
+      const int s = s0 + u;
+      const float e = ms[s] == -INFINITY ? 0.f : expf(ms[s] - M);
+      Z += ls[s] * e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += x0[u][i] * e;
+        acc[4 + i] += x1[u][i] * e;
+      }
     }
   }
   const float inv = 1.0f / Z;
@@ -449,14 +461,15 @@ static int attn_tiles(int K, int W) { return (K + TILE - 1) / TILE + (W + TILE -
 
 // Tiles handled by one workgroup: many query rows -> one workgroup per
 // query (no merge); few -> split the tiles so that roughly 256+ workgroups
-// run, at least 2 tiles each (each split costs a 128 KiB fp32 partial that
-// the merge reads back).
+// run, down to one tile each (each split costs a 128 KiB fp32 partial that
+// the merge reads back, but a workgroup's gathers all start at once, and
+// one gather round is 2-4 us of latency on random latent rows).
 static int attn_tiles_per_split(int64_t R, int K, int W) {
   const int tiles = attn_tiles(K, W);
-  if (R >= 192 || tiles <= 2) return tiles > 0 ? tiles : 1;
+  if (R >= 192 || tiles <= 1) return tiles > 0 ? tiles : 1;
   const int64_t want = (256 + R - 1) / R;  // splits wanted per query
   int tps = (int)((tiles + want - 1) / want);
-  if (tps < 2) tps = 2;
+  if (tps < 1) tps = 1;
   if ((tiles + tps - 1) / tps > MAX_SPLITS) tps = (tiles + MAX_SPLITS - 1) / MAX_SPLITS;
   return tps;
 }

@@ -85,9 +85,8 @@ def _configs():
         win_pos0=65536 - 127, seed=2,
         desc="8192-token chunk after 65536 raw tokens, causal, one indexer")
     c4 = Config(
-        "1m", B=8, Tq=1, N=524288, t_last=1048575, W_cap=128,
-        comp_T=2, comp_pos0=1048574, comp_from_win=True, win_pos0=1048575 - 127,
-        seed=3, desc="8 sequences x 1,048,576 raw tokens, bf16 caches")
+        "1m", B=8, Tq=1, N=524288, t_last=1048575, W_cap=128, win_pos0=1048575 - 127,
+        seed=3, desc="8 sequences x 1,048,576 raw tokens, bf16 caches (no compressor step)")
     c5 = Config(
         "1m_lowp", B=32, Tq=1, N=524288, t_last=1048575, W_cap=128,
         key_fmt="fp8", lat_fmt="nvfp4", win_fmt="fp8", win_pos0=1048575 - 127,
