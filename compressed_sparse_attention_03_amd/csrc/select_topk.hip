@@ -80,22 +80,26 @@ struct Shared {
   uint32_t bcast[8];
 };
 
-// exclusive block scan of one uint32 per thread (any block size <= 1024)
+// exclusive block scan of one uint32 per thread (any block size <= 1024):
+// DPP scan inside each wave, then the 16 lanes of a row scan the wave totals
+// and each wave picks its prefix with readlane.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, Shared& sh, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = (int)(blockDim.x >> 6);
   const uint32_t x = wave_incl_scan(v);
   if (lane == 63) sh.scan[wave] = x;
   __syncthreads();
-  uint32_t wpre = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    const uint32_t t = sh.scan[i];
-    if (i < wave) wpre += t;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return wpre + x - v;
+  const int i = lane & 15;
+  uint32_t t = i < nw ? sh.scan[i] : 0u;
+  t += dpp_mov<0x111>(t);  // row_shr:1
+  t += dpp_mov<0x112>(t);  // row_shr:2
+  t += dpp_mov<0x114>(t);  // row_shr:4
+  t += dpp_mov<0x118>(t);  // row_shr:8
+  const uint32_t through_me = (uint32_t)__builtin_amdgcn_readlane((int)t, wave);
+  const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)t, nw - 1);
+  __syncthreads();  // sh.scan may be rewritten by the next scan
+  return through_me - mine + x - v;
 }
 
 // Exact radix select of one row straight from global memory (any n, any k).
@@ -375,13 +379,16 @@ __device__ int32_t last_valid_column(const SelArgs& a, int64_t row, Shared& sh) 
 }
 
 // The SAMPLE sampled entries of a row, SAMPLE / NT per thread (thread t
-// holds samples t, t + NT, ...).
+// holds samples t, t + NT, ...): 64 runs of 32 consecutive entries, run s
+// starting at entry floor(s n / 64), so that a wave's loads touch two cache
+// lines and every column is sampled with probability SAMPLE / n (n >= 2048).
 template <int NT>
 __device__ __forceinline__ void load_sample(const SelArgs& a, int64_t row, Elem (&e)[SAMPLE / NT],
                                             int64_t (&j)[SAMPLE / NT]) {
 #pragma unroll
   for (int i = 0; i < SAMPLE / NT; ++i) {
-    j[i] = (int64_t)(threadIdx.x + i * NT) * a.n / SAMPLE;
+    const int s = threadIdx.x + i * NT;
+    j[i] = (int64_t)(s >> 5) * a.n / 64 + (s & 31);
     e[i] = load_elem(a, row, j[i]);
   }
 }
