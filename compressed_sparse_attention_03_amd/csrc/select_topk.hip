@@ -277,7 +277,7 @@ constexpr int CAND_CAP = 8192;        // candidate list capacity per row
 constexpr int CAND_PT = CAND_CAP / THREADS;
 constexpr int KFAST = 2048;           // largest k of the sampled paths
 constexpr int64_t MAX_N_FAST = 1 << 17;  // longest row of the sampled paths (bitmaps)
-constexpr int KBIN = 2048;               // radix digit bins of the candidate select
+constexpr int KBIN = 4096;               // radix digit bins of the candidate select (12 bits)
 
 struct SampleSmem {
   uint32_t hist[NBIN];
@@ -303,31 +303,40 @@ struct CandStats {
 // allocator spill.
 template <int NB>
 __device__ __noinline__ void wave_find_bin(const uint32_t* hist, uint32_t want, uint32_t* out) {
-  constexpr int PL = NB / 64;
+  constexpr int PL = NB / 64, NG = PL / 4;  // bins per lane, groups of 4 per lane
   const int lane = threadIdx.x & 63;
   const uint32_t* mine = hist + NB - PL * (lane + 1);  // this lane's bins, ascending
-  uint32_t c[PL];
+  uint32_t gsum[NG];
   uint32_t tot = 0;
 #pragma unroll
-  for (int i = 0; i < PL; i += 4) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(mine + i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      c[i + j] = x[j];
-      tot += x[j];
-    }
+  for (int gi = 0; gi < NG; ++gi) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(mine + 4 * gi);
+    gsum[gi] = x[0] + x[1] + x[2] + x[3];
+    tot += gsum[gi];
   }
   const uint32_t incl = wave_incl_scan(tot);  // over lanes (lane 0 = highest bins)
   uint32_t above = incl - tot;
-  if (above < want && want <= incl) {  // one lane: walk its bins from the top
+  if (above < want && want <= incl) {  // one lane: its group, then the bin
+    int gsel = 0;
+    uint32_t gabove = above;
 #pragma unroll
-    for (int i = PL - 1; i >= 0; --i) {
-      if (above < want && want <= above + c[i]) {
-        out[0] = (uint32_t)(NB - PL * (lane + 1) + i);
-        out[1] = above;
-        out[2] = c[i];
+    for (int gi = NG - 1; gi >= 0; --gi) {
+      if (above < want && want <= above + gsum[gi]) {
+        gsel = gi;
+        gabove = above;
       }
-      above += c[i];
+      above += gsum[gi];
+    }
+    const u32x4 x = *reinterpret_cast<const u32x4*>(mine + 4 * gsel);
+    above = gabove;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (above < want && want <= above + x[j]) {
+        out[0] = (uint32_t)(NB - PL * (lane + 1) + 4 * gsel + j);
+        out[1] = above;
+        out[2] = x[j];
+      }
+      above += x[j];
     }
   }
 }
@@ -535,7 +544,7 @@ __device__ void classify_range(const SelArgs& a, int64_t row, int64_t j0, int64_
 // tied at it.  Low bits that every candidate key has in common are dropped
 // (integer-valued scores leave the low mantissa bits constant) and the
 // smallest key is subtracted, d = (key >> tz) - base, so the digits cover
-// only the spread of the candidates; then 11-bit radix digits of d from the
+// only the spread of the candidates; then 12-bit radix digits of d from the
 // top, a digit bin that holds exactly the number still wanted ending the
 // search.  Candidate order: see th_cmp.  P values per thread; the key of
 // value x is x >> SHIFT, and it is a candidate iff lo_key <= key <= hi_key
@@ -624,7 +633,7 @@ __device__ KeyThreshold key_threshold(const T (&vals)[P], uint32_t lo_key, uint3
     __syncthreads();
   }
   while (hi > 0) {
-    const int lo = hi > 11 ? hi - 11 : 0;
+    const int lo = hi > 12 ? hi - 12 : 0;
     const uint32_t dmask = (1u << (hi - lo)) - 1u;
     uint32_t* h = fs.hist[cur];
 #pragma unroll
