@@ -149,28 +149,32 @@ def scan_launch_us(torch, api, path, inp, launches):
     return start.elapsed_time(end) / launches * 1e3
 
 
-def cpu_baseline(cfg, inp, gen, budget_s=12.0):
-    """The oracle as it stands, on whole sequences of the same workload, until
-    about budget_s of wall time has been spent (at least one sequence)."""
-    import numpy as np  # noqa: F401
+def cpu_baseline(cfg, inp, gen, budget_s=10.0):
+    """The oracle as it stands, on the sequences of the same workload: each
+    sequence's inputs are copied to the host once, then whole-sequence oracle
+    decodes run round-robin until about budget_s of oracle time (the host
+    copies are not counted)."""
     from oracle import csa2_ref as ref
 
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    done, t0 = 0, time.perf_counter()
+    hosts = []
     for b in range(cfg.B):
         host = {k: (None if v is None else gen.to_numpy(v if k == "sink" else v[b:b + 1]))
                 for k, v in inp.items() if k != "cfg"}
         host["comp_pos0"] = cfg.comp_pos0
+        hosts.append(host)
+    done, spent = 0, 0.0
+    while spent < budget_s:
+        host = hosts[done % cfg.B]
         ts = time.perf_counter()
         ref.decode(host, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=cfg.comp_T > 0)
+        spent += time.perf_counter() - ts
         done += 1
-        log(f"[cpu] oracle sequence {b}: {time.perf_counter() - ts:.1f} s")
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    wall = time.perf_counter() - t0
-    return {"value": done * cfg.Tq / wall, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {cfg.B} sequences of the 1M-context decode workload "
-                      f"(whole path per sequence incl. host copies), {wall:.1f} s wall"}
+    log(f"[cpu] oracle: {done} sequence decodes in {spent:.1f} s")
+    return {"value": done * cfg.Tq / spent, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} whole-sequence decodes (round-robin over the {cfg.B} sequences of the "
+                      f"1M-context decode workload, one query each), {spent:.1f} s of oracle time; "
+                      f"host copies of the inputs excluded"}
 
 
 def calib_copy(torch, nbytes=1 << 30):
