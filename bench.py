@@ -278,6 +278,20 @@ def main():
         }
         del linp
         torch.cuda.empty_cache()
+        vcfg, vinp, vpath, vms, vst = time_config("1m_verify", max(3, args.steps // 2), 2, torch, gen,
+                                                  api)
+        del vpath
+        vsb = step_bytes(vcfg)
+        vt = sum(vsb.values())
+        extra["verify_1m"] = {
+            "workload": "speculative verification: 8 sequences x 5 draft tokens at 1M ctx, bf16 caches",
+            "queries_per_s": round(vcfg.R / (vms * 1e-3), 1), "ms_per_step": round(vms, 4),
+            "step_hbm_frac": round(vt / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "index_scan_GBs_eager_stage": round(vsb["index_scan"] / (vst["index_scan"] * 1e-3) / 1e9, 1),
+            "stages_us_eager": {k: round(v * 1e3, 2) for k, v in vst.items()},
+        }
+        del vinp
+        torch.cuda.empty_cache()
         pcfg, pinp, ppath, pms, pst = time_config("prefill", 2, 1, torch, gen, api)
         del ppath
         flops = prefill_indexer_flops(pcfg)

@@ -4,7 +4,8 @@
 // and the maximum over each block of 8 latents is kept (a block is
 // represented by its best in-block score).  Decode (few queries per
 // sequence): keys streamed from HBM once per query group, MFMA operands and
-// epilogue from indexer.h.  Prefill (many queries): see prefill_scan_kernel.
+// epilogue from indexer.h.  Several queries per sequence (speculative
+// verification, prefill): see tile_scan_kernel.
 #include "indexer.h"
 #include "launch.h"
 
@@ -174,46 +175,51 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
 }
 
-// ---- prefill: many queries per sequence -------------------------------------
-// MFMA-bound.  A block = 8 waves x PF_QW queries = 16 consecutive queries of
-// one sequence, over one of PF_CHUNKS equal key ranges; with 8 ranges and
-// the block id's low bits picking the range, each XCD keeps "its" key range
-// resident in its L2 while every query group streams through it.
-// v_mfma_f32_32x32x16_bf16: A = 32 heads x 16 dims of one query (registers,
-// loaded once), B = 16 dims x 32 keys of the current key tile (LDS, shared by
-// the 16 queries of the block), D = heads x keys; lane l holds key l%32 and
-// heads 8(i/4) + 4(l/32) + i%4 of accumulator element i.  Epilogue per
-// query and 32 keys: ReLU x w_h over the lane's 16 heads, one cross-half
-// shuffle for the other 16, causal mask, max over each 8-key block.
-constexpr int PF_WAVES = 8;
-constexpr int PF_QW = 2;                       // queries per wave
-constexpr int PF_Q = PF_WAVES * PF_QW;         // queries per block
-constexpr int PF_CHUNKS = 8;                   // key ranges (one per XCD)
-constexpr int PF_TILE = 32;                    // keys per tile
-constexpr int PF_LD = DI * 2 + 16;             // LDS bytes per key row (padded)
+// ---- several queries per sequence: key tiles shared through LDS -------------
+// A block = NW waves x QW queries = NW*QW consecutive queries of one
+// sequence, over one key range.  32-key tiles (8 KiB of bf16 keys) are read
+// coalesced by the whole block, DEPTH tiles ahead, into a double-buffered LDS
+// tile that every wave uses for all of its queries: the keys cross HBM once
+// per NW*QW queries.  v_mfma_f32_32x32x16_bf16: A = 32 heads x 16 dims of a
+// query (registers, loaded once), B = 16 dims x 32 keys of the LDS tile,
+// D = heads x keys; lane l holds key l%32 and heads 8(i/4) + 4(l/32) + i%4 of
+// accumulator element i.  Epilogue per query and 32 keys: ReLU x w_h over the
+// lane's 16 heads, one cross-half shuffle for the other 16, causal mask, max
+// over each 8-key block.
+// Prefill (thousands of queries, MFMA-bound): 8 waves x 2 queries, 8 key
+// ranges with the range as the block id's low index, so that each XCD keeps
+// "its" range resident in L2 while all query groups stream through it.
+// Verification decode (a few queries per sequence, HBM-bound): 4 waves x 2
+// queries, 3 tiles in flight, enough key ranges to fill the chip.
+constexpr int TS_TILE = 32;              // keys per tile
+constexpr int TS_LD = DI * 2 + 16;       // LDS bytes per key row (padded)
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-__global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
-  __shared__ __align__(16) uint8_t kt[2][PF_TILE * PF_LD];
+template <int NW, int QW, int DEPTH>
+__global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
+  constexpr int NT = NW * 64;
+  constexpr int NQ = NW * QW;                     // queries per block
+  constexpr int LPT = TS_TILE * DI * 2 / 16 / NT;  // 16-byte loads per thread per tile
+  static_assert(LPT >= 1 && LPT * NT * 16 == TS_TILE * DI * 2, "tile split");
+  __shared__ __align__(16) uint8_t kt[2][TS_TILE * TS_LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, kn = lane & 31;
   const int chunk = blockIdx.x;
   const int b = blockIdx.z;
-  const int j0 = blockIdx.y * PF_Q + wave * PF_QW;  // this wave's first query
+  const int j0 = blockIdx.y * NQ + wave * QW;  // this wave's first query
   const int64_t k0 = (int64_t)chunk * keys_per_chunk;
   const int64_t k1 = min(a.n_cache, k0 + keys_per_chunk);
   const int64_t nblk = (a.n_cache + BLK - 1) / BLK;
   const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.k_sb;
 
   // query operands and per-lane head weights
-  bf16x8 qa[PF_QW][8];
-  float wl[PF_QW][16];
-  int64_t nv[PF_QW], rows[PF_QW];
-  bool qok[PF_QW];
-  int64_t nv_blk = 0;  // largest visible count of the block's queries
+  bf16x8 qa[QW][8];
+  float wl[QW][16];
+  int64_t nv[QW], rows[QW];
+  bool qok[QW];
 #pragma unroll
-  for (int qi = 0; qi < PF_QW; ++qi) {
+  for (int qi = 0; qi < QW; ++qi) {
     const int j = j0 + qi;
     qok[qi] = j < a.Tq;
     const int64_t r = (int64_t)b * a.Tq + (qok[qi] ? j : a.Tq - 1);
@@ -225,43 +231,36 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_scan_kernel(ScanArgs
     for (int i = 0; i < 16; ++i) wl[qi][i] = a.w[r * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
     nv[qi] = qok[qi] ? n_visible(a.q_pos[r], a.n_cache) : 0;
   }
+  // visible range of the whole block (queries are consecutive)
+  int64_t nv_blk;
   {
-    // visible range of the whole block (queries are consecutive)
-    const int jl = min(a.Tq - 1, (int)blockIdx.y * PF_Q + PF_Q - 1);
-    nv_blk = n_visible(a.q_pos[(int64_t)b * a.Tq + jl], a.n_cache);
-    const int jf = min(a.Tq - 1, (int)blockIdx.y * PF_Q);
-    nv_blk = max(nv_blk, n_visible(a.q_pos[(int64_t)b * a.Tq + jf], a.n_cache));
+    const int jl = min(a.Tq - 1, (int)blockIdx.y * NQ + NQ - 1);
+    const int jf = min(a.Tq - 1, (int)blockIdx.y * NQ);
+    nv_blk = max(n_visible(a.q_pos[(int64_t)b * a.Tq + jl], a.n_cache),
+                 n_visible(a.q_pos[(int64_t)b * a.Tq + jf], a.n_cache));
   }
-  // staging: thread -> (row tid/16, 16-byte piece tid%16) of a 32-key tile
-  const int srow = tid >> 4, spiece = tid & 15;
-  auto load_tile = [&](int64_t t0, u32x4& v) {
-    const int64_t row = t0 + srow;
-    v = (u32x4){0u, 0u, 0u, 0u};
-    if (row < k1 && row < nv_blk) v = *reinterpret_cast<const u32x4*>(kb + row * DI + 8 * spiece);
-  };
+  // staging: load u of a tile -> (row (u NT + tid) / 16, 16-byte piece tid % 16)
+  const int spiece = tid & 15;
   const int64_t kend = min(k1, max(k0, nv_blk));  // keys that need computing
-  u32x4 nxt;
-  int buf = 0;
-  if (k0 < kend) load_tile(k0, nxt);
-  for (int64_t t0 = k0; t0 < k1; t0 += PF_TILE) {
-    const bool compute = t0 < kend;  // block-uniform
-    if (compute) {
-      *reinterpret_cast<u32x4*>(&kt[buf][srow * PF_LD + 16 * spiece]) = nxt;
-      __syncthreads();
-      if (t0 + PF_TILE < kend) load_tile(t0 + PF_TILE, nxt);
+  auto load_tile = [&](int64_t t0, u32x4 (&v)[LPT]) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int64_t row = t0 + (u * NT + tid) / 16;
+      v[u] = (u32x4){0u, 0u, 0u, 0u};
+      if (row < kend) v[u] = *reinterpret_cast<const u32x4*>(kb + row * DI + 8 * spiece);
     }
+  };
+  auto compute = [&](int64_t t0, const uint8_t* tile) {
     const int64_t p = t0 + kn;  // this lane's key
     bf16x8 kbop[8];
-    if (compute) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        kbop[c] = *reinterpret_cast<const bf16x8*>(&kt[buf][kn * PF_LD + 32 * c + 16 * half]);
-    }
+    for (int c = 0; c < 8; ++c)
+      kbop[c] = *reinterpret_cast<const bf16x8*>(tile + kn * TS_LD + 32 * c + 16 * half);
 #pragma unroll
-    for (int qi = 0; qi < PF_QW; ++qi) {
+    for (int qi = 0; qi < QW; ++qi) {
       if (!qok[qi]) continue;  // wave-uniform
       float s = -INFINITY;
-      if (compute && t0 < nv[qi]) {
+      if (t0 < nv[qi]) {
         f32x16 acc = {};
 #pragma unroll
         for (int c = 0; c < 8; ++c)
@@ -283,8 +282,46 @@ __global__ __launch_bounds__(PF_WAVES * 64, 1) void prefill_scan_kernel(ScanArgs
           a.block_max[rows[qi] * a.bm_stride + blk] = m;
       }
     }
-    if (compute) buf ^= 1;
+  };
+  // keys past every query's horizon: masked scores and block maxima only
+  auto masked = [&](int64_t t0) {
+    const int64_t p = t0 + kn;
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi) {
+      if (!qok[qi]) continue;
+      if (a.scores && half == 0 && p < k1) a.scores[rows[qi] * a.s_stride + p] = -INFINITY;
+      const int64_t blk = p >> 3;
+      if (a.block_max && half == 0 && (kn & 7) == 0 && blk < nblk && p < k1)
+        a.block_max[rows[qi] * a.bm_stride + blk] = -INFINITY;
+    }
+  };
+
+  u32x4 stage[DEPTH][LPT];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (k0 + d * TS_TILE < kend) load_tile(k0 + d * TS_TILE, stage[d]);
+  int buf = 0;
+  int64_t t0 = k0;
+  for (; t0 < kend; t0 += DEPTH * TS_TILE) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int64_t tt = t0 + d * TS_TILE;
+      if (tt < kend) {  // block-uniform
+#pragma unroll
+        for (int u = 0; u < LPT; ++u) {
+          const int row = (u * NT + tid) / 16;
+          *reinterpret_cast<u32x4*>(&kt[buf][row * TS_LD + 16 * spiece]) = stage[d][u];
+        }
+        __syncthreads();
+        if (tt + DEPTH * TS_TILE < kend) load_tile(tt + DEPTH * TS_TILE, stage[d]);
+        compute(tt, kt[buf]);
+        buf ^= 1;
+      }
+    }
   }
+  // the tiles of the range that no query sees
+  for (int64_t tt = max(k0, (kend + TS_TILE - 1) / TS_TILE * TS_TILE); tt < k1; tt += TS_TILE)
+    masked(tt);
 }
 
 template <int QPB, bool FP8>
@@ -305,13 +342,27 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
   ScanArgs a{(const uint16_t*)q, w, k, k_sb, n_cache, q_pos, Tq,
              scores, s_stride, block_max, bm_stride, 1};
   if (!k_fp8 && Tq >= 64) {
-    // many queries: the MFMA-bound prefill kernel.  Chunk boundaries are
-    // multiples of the 32-key tile (so of the 8-key block).
-    int64_t kpc = (n_cache + PF_CHUNKS - 1) / PF_CHUNKS;
-    kpc = (kpc + PF_TILE - 1) / PF_TILE * PF_TILE;
+    // many queries: MFMA-bound.  8 key ranges, tile-aligned (so block-aligned).
+    constexpr int CH = 8;
+    int64_t kpc = (n_cache + CH - 1) / CH;
+    kpc = (kpc + TS_TILE - 1) / TS_TILE * TS_TILE;
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
-    dim3 grid(nchunks, (unsigned)((Tq + PF_Q - 1) / PF_Q), (unsigned)B);
-    hipLaunchKernelGGL(prefill_scan_kernel, grid, dim3(PF_WAVES * 64), 0, s, a, kpc);
+    dim3 grid(nchunks, (unsigned)((Tq + 15) / 16), (unsigned)B);
+    hipLaunchKernelGGL((tile_scan_kernel<8, 2, 1>), grid, dim3(512), 0, s, a, kpc);
+    return hipGetLastError();
+  }
+  if (!k_fp8 && Tq >= 2) {
+    // a few queries per sequence (speculative verification): HBM-bound, the
+    // keys are read once per 8 queries; ranges of whole tiles, ~1024 blocks
+    const int64_t groups = (Tq + 7) / 8;
+    const int64_t n_tiles32 = (n_cache + TS_TILE - 1) / TS_TILE;
+    int64_t ch = (1024 + B * groups - 1) / (B * groups);
+    if (ch > n_tiles32) ch = n_tiles32;
+    if (ch < 1) ch = 1;
+    const int64_t kpc = (n_tiles32 + ch - 1) / ch * TS_TILE;
+    const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
+    dim3 grid(nchunks, (unsigned)groups, (unsigned)B);
+    hipLaunchKernelGGL((tile_scan_kernel<8, 1, 6>), grid, dim3(512), 0, s, a, kpc);
     return hipGetLastError();
   }
 

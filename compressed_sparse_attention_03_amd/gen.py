@@ -91,7 +91,12 @@ def _configs():
         "1m_lowp", B=32, Tq=1, N=524288, t_last=1048575, W_cap=128,
         key_fmt="fp8", lat_fmt="nvfp4", win_fmt="fp8", win_pos0=1048575 - 127,
         seed=4, desc="32 sequences x 1,048,576 raw tokens, NVFP4 latents, FP8 window/keys")
-    return {c.name: c for c in (c1, c2, c3, c4, c5)}
+    c6 = Config(
+        "1m_verify", B=8, Tq=5, N=524288, t_last=1048575, W_cap=256,
+        win_pos0=1048575 - 4 - 127, seed=5,
+        desc="speculative verification at 1M: 8 sequences x 5 draft tokens at the end of "
+             "1,048,576 raw tokens, bf16 caches")
+    return {c.name: c for c in (c1, c2, c3, c4, c5, c6)}
 
 
 CONFIGS = _configs()

@@ -58,6 +58,10 @@ def test_compress_stage_tiny():
     # many queries: the prefill scan kernel; ragged query groups, key chunks
     # and tiles, visibility changing inside a block of queries
     ("prefill", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=39)),
+    # a few queries per sequence: key tiles shared through LDS by up to 8 queries
+    ("1m_verify", dict(B=3, N=20000, t_last=39999, K_b=256, win_pos0=39999 - 131, seed=64)),
+    ("1m_verify", dict(B=2, Tq=9, N=9000, t_last=18003, K_b=128, win_pos0=18003 - 135, seed=65)),
+    ("1m_verify", dict(B=2, Tq=2, N=4103, t_last=8205, K_b=64, win_pos0=8205 - 128, seed=66)),
     ("prefill", dict(B=2, Tq=64, N=4096, t_last=8191, K_b=32, K=64, comp_T=0,
                      shared_indexer=False, seed=41)),
 ])
@@ -240,6 +244,10 @@ def test_full_prefill_sampled_queries():
 
 def test_full_1m():
     _full("1m", seqs=[0, 7])
+
+
+def test_full_1m_verify():
+    _full("1m_verify", seqs=[0, 7])
 
 
 def test_full_1m_lowp():
