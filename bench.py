@@ -134,6 +134,44 @@ def time_config(name, steps, warmup, torch, gen, api):
     return cfg, inp, path, ms, stage_ms
 
 
+def time_layer_stack(steps, torch, gen, api):
+    """One decode step through the pages' 40-layer stack on the 1M workload:
+    the block stage once, the candidate indexer + position top-512 at each of
+    the 8 index source layers, attention at every layer (window only at
+    layers 0-1), 4 shared compressed caches.  Steps launched back to back."""
+    cfg = gen.CONFIGS["1m"]
+    log(f"[bench] layer stack: generating inputs ({gen.STACK_LAYERS} layers, B={cfg.B}, N={cfg.N})")
+    inp = gen.make_stack_inputs(cfg, device="cuda")
+    path = api.LayerStackPath(inp, cfg.K_b, cfg.K, cfg.W)
+    for _ in range(2):
+        path.run(inp, cfg.scale)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        path.run(inp, cfg.scale)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    L, R = gen.STACK_LAYERS, cfg.R
+    n_idx, n_win = len(gen.STACK_INDEX_SOURCES), len(gen.STACK_WINDOW_ONLY)
+    sb = step_bytes(cfg)
+    win_row = 2 * D
+    attn_win_only = R * (cfg.W * win_row + HQ * D * 2 * 2 + HQ * 4)
+    total = (sb["index_scan"] + sb["select_blocks"] + n_idx * (sb["index_cand"] + sb["select_positions"])
+             + (L - n_win) * sb["sparse_attn"] + n_win * attn_win_only)
+    log(f"[bench] layer stack: {ms * 1e3:.1f} us/step ({ms * 1e3 / L:.1f} us per layer)")
+    del path, inp
+    return {
+        "workload": f"{L}-layer decode step at 1M ctx (8 sequences x 1 query): block stage once, "
+                    f"{n_idx} index source layers, 4 shared compressed caches, {n_win} window-only layers",
+        "ms_per_step": round(ms, 4), "us_per_layer": round(ms * 1e3 / L, 2),
+        "queries_per_s": round(R / (ms * 1e-3), 1),
+        "step_hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": total,
+    }
+
+
 def scan_launch_us(torch, api, path, inp, launches):
     """Average duration of the candidate-source scan kernel: `launches`
     back-to-back launches on the current stream between two events (each
@@ -291,6 +329,8 @@ def main():
             "stages_us_eager": {k: round(v * 1e3, 2) for k, v in vst.items()},
         }
         del vinp
+        torch.cuda.empty_cache()
+        extra["layer_stack_1m"] = time_layer_stack(max(3, args.steps // 4), torch, gen, api)
         torch.cuda.empty_cache()
         pcfg, pinp, ppath, pms, pst = time_config("prefill", 2, 1, torch, gen, api)
         del ppath

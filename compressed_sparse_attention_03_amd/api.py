@@ -215,5 +215,70 @@ class DecodePath:
         return graph
 
 
+class LayerStackPath:
+    """One decode step through a stack of layers that share index results and
+    compressed caches (NVFP4 article, sections 3.3 and 4): the block stage
+    once; the candidate indexer and the position top-K once per index source
+    layer; sparse attention for every layer, reading the Sel of its index
+    source layer and the latent cache of its KV source layer (window only for
+    the window-only layers).  Layers run in order, one attention launch each,
+    as a model's forward pass would.  Inputs from gen.make_stack_inputs."""
+
+    def __init__(self, inp: dict, K_b: int = 2048, K: int = 512, W: int = 128):
+        cfg = inp["cfg"]
+        self.B, self.Tq, self.N, self.K_b, self.K, self.W = cfg.B, cfg.Tq, cfg.N, K_b, K, W
+        self.layers = inp["layers"]
+        self.window_only = inp["window_only"]
+        self.index_sources = inp["index_sources"]
+        self.kv_sources = inp["kv_sources"]
+        R = cfg.B * cfg.Tq
+        nblk = (cfg.N + BLK - 1) // BLK
+        dev = inp["q_pos"].device
+        self.block_max = torch.empty((R, nblk), dtype=torch.float32, device=dev)
+        self.blocks = torch.empty((R, K_b), dtype=torch.int32, device=dev)
+        self.cand_scores = torch.empty((R, K_b * BLK), dtype=torch.float32, device=dev)
+        self.cand_ids = torch.empty((R, K_b * BLK), dtype=torch.int32, device=dev)
+        self.sel = {s: torch.empty((R, K), dtype=torch.int32, device=dev) for s in self.index_sources}
+        self.no_sel = torch.empty((R, 0), dtype=torch.int32, device=dev)
+        self.out = [torch.empty((R, HQ, D), dtype=torch.bfloat16, device=dev)
+                    for _ in range(self.layers)]
+        self.lse = [torch.empty((R, HQ), dtype=torch.float32, device=dev) for _ in range(self.layers)]
+        wsb = max(workspace_bytes(_lib.OP_SPARSE_ATTN, R, K, W),
+                  workspace_bytes(_lib.OP_SPARSE_ATTN, R, 0, W))
+        self.ws = torch.empty((max(wsb, 16) // 4 + 4,), dtype=torch.float32, device=dev)
+        sel_b = max(workspace_bytes(_lib.OP_SELECT, R, nblk, K_b),
+                    workspace_bytes(_lib.OP_SELECT, R, K_b * BLK, K))
+        self.sel_ws = torch.empty(((max(sel_b, 64) + 63) // 64 * 8,), dtype=torch.float64, device=dev)
+
+    def source_of(self, layer: int):
+        """(index source, KV source) read by ``layer``; None for window-only layers."""
+        if layer in self.window_only:
+            return None
+        from .gen import stack_source
+        return stack_source(layer, self.index_sources), stack_source(layer, self.kv_sources)
+
+    def run(self, inp: dict, scale: float, stream=None):
+        index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,
+                   stream=stream)
+        select_topk(self.block_max, self.K_b, self.blocks, force_last=True, ws=self.sel_ws,
+                    stream=stream)
+        any_lat = inp["lat"][self.kv_sources[0]]
+        for layer in range(self.layers):
+            if layer in self.index_sources:
+                index_cand(inp["qi"][layer], inp["wi"][layer], inp["ki"][layer], inp["q_pos"],
+                           self.blocks, self.cand_scores, self.cand_ids, stream=stream)
+                select_topk(self.cand_scores, self.K, self.sel[layer], ids=self.cand_ids,
+                            ws=self.sel_ws, stream=stream)
+            src = self.source_of(layer)
+            if src is None:
+                lat, sel = any_lat, self.no_sel
+            else:
+                lat, sel = inp["lat"][src[1]], self.sel[src[0]]
+            sparse_attn(inp["q"][layer], lat, sel, inp["win"][layer], inp["q_pos"],
+                        inp["sink"][layer], self.W, scale, self.out[layer], lse=self.lse[layer],
+                        ws=self.ws, stream=stream)
+        return self.out
+
+
 STAGES = ("compress", "index_scan", "select_blocks", "index_cand", "select_positions",
           "sparse_attn")

@@ -191,3 +191,55 @@ def to_numpy(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view("uint16")
     return t.numpy()
+
+
+# ---- a stack of layers sharing index results and compressed caches ----------
+# Layout of the NVFP4 article (sections 3.3 and 4): 40 layers; layers 0 and 1
+# attend to their sliding window only; 8 index source layers compute and
+# publish their position top-K, every later layer reads the one of the most
+# recent index source layer; 4 KV source layers store a compressed cache that
+# the layers up to the next source read through a shared handle; the block
+# stage runs once per token (at the candidate-source layer).
+STACK_LAYERS = 40
+STACK_WINDOW_ONLY = (0, 1)
+STACK_INDEX_SOURCES = (2, 8, 14, 20, 24, 28, 32, 36)
+STACK_KV_SOURCES = (2, 8, 14, 20)
+
+
+def stack_source(layer: int, sources) -> int:
+    """The most recent source layer at or before ``layer`` (-1 if none)."""
+    best = -1
+    for s in sources:
+        if s <= layer:
+            best = max(best, s)
+    return best
+
+
+def make_stack_inputs(cfg: Config, layers: int = STACK_LAYERS, window_only=STACK_WINDOW_ONLY,
+                      index_sources=STACK_INDEX_SOURCES, kv_sources=STACK_KV_SOURCES,
+                      device="cpu", seed: Optional[int] = None) -> dict:
+    """Inputs of a layer stack: the candidate-source indexer (qs, ws, ks), per
+    index source layer s an indexer (qi[s], wi[s], ki[s]), per KV source
+    layer a latent cache lat[s], per layer an attention query q[l], window
+    source win[l] and sink[l]; one set of query positions.  bf16 caches."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed if seed is None else seed)
+    B, Tq, N = cfg.B, cfg.Tq, cfg.N
+    out = {"cfg": cfg, "layers": layers, "window_only": tuple(window_only),
+           "index_sources": tuple(index_sources), "kv_sources": tuple(kv_sources)}
+    out["q_pos"] = q_positions(cfg).to(dev)
+    out["qs"] = _int_bf16((B, Tq, HI, DI), g, dev)
+    out["ws"] = _head_weights((B, Tq, HI), g, dev)
+    out["ks"] = _int_bf16((B, N, DI), g, dev)
+    out["qi"], out["wi"], out["ki"] = {}, {}, {}
+    for s in index_sources:
+        out["qi"][s] = _int_bf16((B, Tq, HI, DI), g, dev)
+        out["wi"][s] = _head_weights((B, Tq, HI), g, dev)
+        out["ki"][s] = _int_bf16((B, N, DI), g, dev)
+    out["lat"] = {s: _normal_bf16((B, N, D), g, dev) for s in kv_sources}
+    out["q"] = [_normal_bf16((B, Tq, HQ, D), g, dev) for _ in range(layers)]
+    out["win"] = [_normal_bf16((B, cfg.W_cap, D), g, dev) for _ in range(layers)]
+    out["sink"] = [torch.randn((HQ,), generator=g, device=dev, dtype=torch.float32)
+                   for _ in range(layers)]
+    return out
