@@ -418,3 +418,71 @@ void csa2ref_dequant_nvfp4(const uint8_t *packed, const uint8_t *scales,
       dst[r * cols + c] = csa2ref_e2m1(nib) * csa2ref_e4m3(scales[r * (cols / 16) + c / 16]);
     }
 }
+
+/* ===================================================================== */
+/* f1: NVFP4 quantisation of compressed latents (NVFP4 article, section   */
+/* 3.2: the cache holds E2M1 values in groups of 16 sharing one E4M3      */
+/* scale).  The article names the format, not the encoder; the reading    */
+/* taken here is the plain one:                                           */
+/*   scale  = the E4M3 value nearest to amax/6 (6 = largest E2M1          */
+/*            magnitude), ties to the even code, saturating at 448;       */
+/*   code_i = the E2M1 value nearest to x_i / scale, ties to the even     */
+/*            code, saturating at +-6, sign taken from x_i;               */
+/*   a group whose scale rounds to 0 stores scale 0 and all-zero codes.   */
+/* "Nearest" is decided on the exact real quotients: both quotients are   */
+/* formed in double, whose rounding cannot move a quotient of an fp32     */
+/* numerator by an E4M3 / E2M1 value onto or across a rounding midpoint   */
+/* (a midpoint has at most 5 significant bits, the exact quotient either  */
+/* equals it or differs from it by far more than 2^-53 relative).  The    */
+/* search is a brute-force scan over every finite code.                   */
+/* ===================================================================== */
+uint8_t csa2ref_quant_scale_e4m3(float amax) {
+  double target = (double)amax / 6.0;
+  uint8_t best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) { /* every finite non-negative code */
+    double d = fabs(csa2ref_e4m3((uint8_t)c) - target);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = (uint8_t)c;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
+uint8_t csa2ref_quant_e2m1(float x, uint8_t scale_code) {
+  double s = csa2ref_e4m3(scale_code);
+  double target, best_d = INFINITY;
+  uint8_t best = 0;
+  if (s == 0.0) return 0;
+  target = fabs((double)x) / s;
+  for (int c = 0; c < 8; ++c) { /* the eight magnitudes */
+    double d = fabs(csa2ref_e2m1((uint8_t)c) - target);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = (uint8_t)c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(best | (x < 0.0f ? 8 : 0));
+}
+
+void csa2ref_quant_nvfp4(const float *src, int64_t rows, int cols,
+                         uint8_t *packed, uint8_t *scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int g = 0; g < cols / 16; ++g) {
+      const float *x = src + r * cols + 16 * g;
+      float amax = 0.0f;
+      uint8_t sc;
+      for (int i = 0; i < 16; ++i)
+        if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+      sc = csa2ref_quant_scale_e4m3(amax);
+      scales[r * (cols / 16) + g] = sc;
+      for (int i = 0; i < 16; i += 2) {
+        uint8_t lo = csa2ref_quant_e2m1(x[i], sc);
+        uint8_t hi = csa2ref_quant_e2m1(x[i + 1], sc);
+        packed[r * (cols / 2) + (16 * g + i) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}

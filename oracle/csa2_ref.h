@@ -131,6 +131,18 @@ void csa2ref_dequant_fp8(const uint8_t *src, const float *row_scale,
 void csa2ref_dequant_nvfp4(const uint8_t *packed, const uint8_t *scales,
                            int64_t rows, int cols, double *dst);
 
+
+/* ---- f1: NVFP4 quantisation (the inverse of csa2ref_dequant_nvfp4) ---- */
+/* scale code: nearest E4M3 to amax/6, ties to even, saturating at 448.
+ * element code: nearest E2M1 to x/scale (sign from x), ties to even,
+ * saturating at 6; scale 0 gives code 0.  src f32 [rows][cols], cols % 16
+ * == 0; packed [rows][cols/2] (element 2i in the low nibble of byte i),
+ * scales [rows][cols/16].                                                */
+uint8_t csa2ref_quant_scale_e4m3(float amax);
+uint8_t csa2ref_quant_e2m1(float x, uint8_t scale_code);
+void csa2ref_quant_nvfp4(const float *src, int64_t rows, int cols,
+                         uint8_t *packed, uint8_t *scales);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,6 +64,12 @@ def lib():
         L.csa2ref_dequant_fp8.argtypes = [P, P, I64, I, P]
         L.csa2ref_dequant_nvfp4.restype = None
         L.csa2ref_dequant_nvfp4.argtypes = [P, P, I64, I, P]
+        L.csa2ref_quant_scale_e4m3.restype = ctypes.c_uint8
+        L.csa2ref_quant_scale_e4m3.argtypes = [ctypes.c_float]
+        L.csa2ref_quant_e2m1.restype = ctypes.c_uint8
+        L.csa2ref_quant_e2m1.argtypes = [ctypes.c_float, ctypes.c_uint8]
+        L.csa2ref_quant_nvfp4.restype = None
+        L.csa2ref_quant_nvfp4.argtypes = [P, I64, I, P, P]
         _lib = L
     return _lib
 
@@ -230,6 +236,74 @@ def dequant_nvfp4(packed, scales):
     dst = np.zeros((rows, cols), np.float64)
     lib().csa2ref_dequant_nvfp4(_p(packed), _p(scales), rows, cols, _p(dst))
     return dst
+
+
+# ------------------------------------------------- f1: NVFP4 cache writes
+def quant_scale_e4m3(amax) -> int:
+    return lib().csa2ref_quant_scale_e4m3(float(amax))
+
+
+def quant_e2m1(x, scale_code) -> int:
+    return lib().csa2ref_quant_e2m1(float(x), int(scale_code))
+
+
+def quant_nvfp4(x):
+    """x: float32 [rows][cols] (cols % 16 == 0) -> (packed uint8 [rows][cols/2],
+    scales uint8 [rows][cols/16]): nearest E4M3 scale to amax/6 per group of
+    16, nearest E2M1 code to x/scale, ties to even (NVFP4 article 3.2)."""
+    x = _c(x, np.float32)
+    rows, cols = x.shape
+    assert cols % 16 == 0
+    packed = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    lib().csa2ref_quant_nvfp4(_p(x), rows, cols, _p(packed), _p(scales))
+    return packed, scales
+
+
+def compress_nvfp4(raw: np.ndarray, gate: np.ndarray):
+    """The compressor writing the NVFP4 cache: the pooled value (exact up to
+    double rounding) rounded once to fp32, then quantised as quant_nvfp4.
+    Returns (packed [B][T/2][256], scales [B][T/2][32], pooled float64)."""
+    _, out64 = compress(raw, gate)
+    B, G, _ = out64.shape
+    packed, scales = quant_nvfp4(out64.astype(np.float32).reshape(B * G, D))
+    return packed.reshape(B, G, D // 2), scales.reshape(B, G, D // 16), out64
+
+
+def compress_decode(state, kv_tok, gate_tok, pos, cache, n_cache, fmt="bf16"):
+    """One decode step of the compressor with its carried state (NVFP4
+    article 3.2: the unfinished half of a group waits in state; a latent is
+    emitted once both tokens of its group are there).
+
+    state : uint16 [B][2][512], the pending (kv, gate) token of each sequence,
+            updated in place;  kv_tok, gate_tok : uint16 [B][512], the new
+            token at raw position pos[b] (negative = no token).
+    An even position only stores the token.  An odd position t pools the
+    stored token with the new one into latent t//2 of ``cache``, if that row
+    is below n_cache.  cache: fmt "bf16" -> uint16 [B][rows][512];
+    fmt "nvfp4" -> (packed uint8 [B][rows][256], scales uint8 [B][rows][32]).
+    """
+    B = kv_tok.shape[0]
+    for b in range(B):
+        t = int(pos[b])
+        if t < 0:
+            continue
+        if t % 2 == 0:
+            state[b, 0] = kv_tok[b]
+            state[b, 1] = gate_tok[b]
+            continue
+        g = t // 2
+        if g >= n_cache:
+            continue
+        raw = np.stack([state[b, 0], kv_tok[b]])[None]
+        gate = np.stack([state[b, 1], gate_tok[b]])[None]
+        if fmt == "bf16":
+            out, _ = compress(raw, gate)
+            cache[b, g] = out[0, 0]
+        else:
+            packed, scales, _ = compress_nvfp4(raw, gate)
+            cache[0][b, g] = packed[0, 0]
+            cache[1][b, g] = scales[0, 0]
 
 
 # --------------------------------------------------------------- pipeline
