@@ -21,7 +21,7 @@ OP_SELECT, OP_SPARSE_ATTN = 1, 2
 EXPORTS = (
     "csa2_status_string", "csa2_version", "csa2_compress", "csa2_index_scores",
     "csa2_select_topk", "csa2_sparse_attn", "csa2_dequant_fp8", "csa2_dequant_nvfp4",
-    "csa2_workspace_bytes",
+    "csa2_workspace_bytes", "csa2_compress_nvfp4", "csa2_compress_step", "csa2_quant_nvfp4",
 )
 
 _lib = None
@@ -56,6 +56,9 @@ def lib():
         "csa2_dequant_fp8": (I, [P, P, I64, I, P, I, P]),
         "csa2_dequant_nvfp4": (I, [P, P, I64, I, P, I, P]),
         "csa2_workspace_bytes": (SZ, [I, I64, I64, I64]),
+        "csa2_compress_nvfp4": (I, [I, I, P, I64, P, I64, P, P, I64, P]),
+        "csa2_compress_step": (I, [I, P, I64, P, I64, P, P, I, P, P, I64, I64, P]),
+        "csa2_quant_nvfp4": (I, [P, I, I64, I, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -57,6 +57,72 @@ def compress(raw: torch.Tensor, gate: torch.Tensor, out: torch.Tensor, stream=No
     return out
 
 
+def compress_nvfp4(raw: torch.Tensor, gate: torch.Tensor, codes: torch.Tensor,
+                   scales: torch.Tensor, stream=None):
+    """a1 with the NVFP4 epilogue: raw, gate bf16 [B][T][512] -> codes uint8
+    [B][rows][256] and E4M3 scales uint8 [B][rows][32] for rows 0..T/2-1 (the
+    tensors may be views of a larger cache with the same row stride)."""
+    B, T, _ = raw.shape
+    for t, n in ((raw, "raw"), (gate, "gate")):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1 or t.stride(-2) != D:
+            raise ValueError(f"compress_nvfp4: {n} must be bf16 with contiguous 512-wide rows")
+    sb = _fp4_rows(codes, scales, "compress_nvfp4")
+    check("csa2_compress_nvfp4", lib().csa2_compress_nvfp4(
+        B, T, _p(raw), raw.stride(0), _p(gate), gate.stride(0), _p(codes), _p(scales), sb,
+        _stream(stream)))
+    return codes, scales
+
+
+def _fp4_rows(codes, scales, fn):
+    if codes.dtype != torch.uint8 or scales.dtype != torch.uint8:
+        raise ValueError(f"{fn}: codes and scales must be uint8")
+    if codes.stride(-1) != 1 or codes.stride(-2) != D // 2 or scales.stride(-1) != 1 or \
+            scales.stride(-2) != D // 16 or codes.stride(0) // (D // 2) != scales.stride(0) // (D // 16):
+        raise ValueError(f"{fn}: codes [B][rows][256] / scales [B][rows][32] need one row stride")
+    return codes.stride(0) // (D // 2)
+
+
+def compress_step(kv: torch.Tensor, gate: torch.Tensor, pos: torch.Tensor, state: torch.Tensor,
+                  cache, n_cache: int = None, stream=None):
+    """One decode step of the compressor: kv, gate bf16 [B][512] at raw
+    positions pos (int64 [B], device; negative = none); state bf16
+    [B][2][512] carried between calls.  cache: a bf16 tensor [B][rows][512],
+    or a (codes, scales) pair for the NVFP4 cache."""
+    B = kv.shape[0]
+    if state.dtype != torch.bfloat16 or tuple(state.shape) != (B, 2, D) or not state.is_contiguous():
+        raise ValueError("compress_step: state must be contiguous bf16 [B][2][512]")
+    if isinstance(cache, tuple):
+        codes, scales = cache
+        sb = _fp4_rows(codes, scales, "compress_step")
+        rows = codes.shape[1] if n_cache is None else n_cache
+        args = (NVFP4, _p(codes), _p(scales), sb, rows)
+    else:
+        if cache.dtype != torch.bfloat16 or cache.stride(-1) != 1 or cache.stride(-2) != D:
+            raise ValueError("compress_step: bf16 cache needs contiguous 512-wide rows")
+        rows = cache.shape[1] if n_cache is None else n_cache
+        args = (BF16, _p(cache), None, cache.stride(0) // D, rows)
+    check("csa2_compress_step", lib().csa2_compress_step(
+        B, _p(kv), kv.stride(0), _p(gate), gate.stride(0), _p(pos), _p(state), *args,
+        _stream(stream)))
+    return cache
+
+
+def quant_nvfp4(src: torch.Tensor, packed=None, scales=None, stream=None):
+    """src bf16 or f32 [rows][cols] (contiguous, cols % 16 == 0) -> (packed
+    uint8 [rows][cols/2], scales uint8 [rows][cols/16])."""
+    rows, cols = src.shape
+    if not src.is_contiguous() or src.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("quant_nvfp4: src must be contiguous bf16 or f32")
+    if packed is None:
+        packed = torch.empty((rows, cols // 2), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=src.device)
+    dt = F32 if src.dtype == torch.float32 else BF16
+    check("csa2_quant_nvfp4", lib().csa2_quant_nvfp4(_p(src), dt, rows, cols, _p(packed),
+                                                     _p(scales), _stream(stream)))
+    return packed, scales
+
+
 def index_scan(q, w, k, q_pos, scores=None, block_max=None, stream=None):
     """a2: indexer scores of every latent and/or per-block maxima.
 
@@ -184,6 +250,12 @@ class DecodePath:
             g0 = inp["cfg"].comp_pos0 // 2
             T = inp["raw"].shape[1]
             compress(inp["raw"], inp["gate"], inp["lat"][:, g0:g0 + T // 2], stream=stream)
+        if inp.get("tok_kv") is not None:
+            # the compressor's decode step: completes the pair ending at
+            # step_pos and writes its latent (NVFP4 or bf16) into the cache
+            cache = (inp["lat"], inp["lat_scale"]) if inp.get("lat_scale") is not None else inp["lat"]
+            compress_step(inp["tok_kv"], inp["tok_gate"], inp["step_pos"], inp["state"], cache,
+                          stream=stream)
         mark(1)
         index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,
                    stream=stream)

@@ -43,7 +43,7 @@ const char* csa2_status_string(int status) {
   }
 }
 
-int csa2_version(void) { return (1 << 16) | 0; }
+int csa2_version(void) { return (1 << 16) | 1; }
 
 size_t csa2_workspace_bytes(int op, int64_t R, int64_t n, int64_t k) {
   if (R <= 0) return 0;
@@ -75,6 +75,82 @@ int csa2_compress(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
   if (overlap(out, o_bytes, kv, kv_bytes) || overlap(out, o_bytes, gate, g_bytes)) return CSA2_EINVAL;
   clear_stale_error();
   return launched(csa2::launch_compress(B, T, kv, kv_sb, gate, g_sb, out, out_sb, stream));
+}
+
+int csa2_compress_nvfp4(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
+                        int64_t g_sb, uint8_t* codes, uint8_t* scale_e4m3, int64_t out_sb,
+                        hipStream_t stream) {
+  if (B < 0 || T < 0 || (T & 1)) return CSA2_EINVAL;
+  if (B == 0 || T == 0) return CSA2_OK;
+  if (B > 65535) return CSA2_EUNSUPPORTED;
+  if (!kv || !gate || !codes || !scale_e4m3) return CSA2_EINVAL;
+  if (!aligned(kv, 16) || !aligned(gate, 16) || !aligned(codes, 8)) return CSA2_EINVAL;
+  const int64_t rowsz = (int64_t)T * CSA2_D, G = T / 2;
+  if ((B > 1 && (kv_sb < rowsz || g_sb < rowsz || out_sb < G)) || kv_sb % 8 || g_sb % 8 ||
+      kv_sb < 0 || g_sb < 0 || out_sb < 0)
+    return CSA2_EINVAL;
+  const int64_t kv_bytes = ((int64_t)(B - 1) * kv_sb + rowsz) * 2;
+  const int64_t g_bytes = ((int64_t)(B - 1) * g_sb + rowsz) * 2;
+  const int64_t rows = (int64_t)(B - 1) * out_sb + G;
+  const int64_t c_bytes = rows * (CSA2_D / 2), s_bytes = rows * (CSA2_D / 16);
+  if (overlap(codes, c_bytes, kv, kv_bytes) || overlap(codes, c_bytes, gate, g_bytes) ||
+      overlap(scale_e4m3, s_bytes, kv, kv_bytes) || overlap(scale_e4m3, s_bytes, gate, g_bytes) ||
+      overlap(codes, c_bytes, scale_e4m3, s_bytes))
+    return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_compress_nvfp4(B, T, kv, kv_sb, gate, g_sb, codes, scale_e4m3,
+                                              out_sb, stream));
+}
+
+int csa2_compress_step(int B, const void* kv, int64_t kv_sb, const void* gate, int64_t g_sb,
+                       const int64_t* pos, void* state, csa2_dtype out_dt, void* out,
+                       uint8_t* out_scale, int64_t out_sb, int64_t n_cache, hipStream_t stream) {
+  if (B < 0 || n_cache < 0) return CSA2_EINVAL;
+  if (out_dt != CSA2_BF16 && out_dt != CSA2_NVFP4) return CSA2_EUNSUPPORTED;
+  if (B == 0) return CSA2_OK;
+  const bool fp4 = out_dt == CSA2_NVFP4;
+  if (!kv || !gate || !pos || !state || !out || (fp4 && !out_scale)) return CSA2_EINVAL;
+  if (!aligned(kv, 16) || !aligned(gate, 16) || !aligned(state, 16) || !aligned(pos, 8) ||
+      !aligned(out, fp4 ? 8 : 16))
+    return CSA2_EINVAL;
+  if ((B > 1 && (kv_sb < CSA2_D || g_sb < CSA2_D || out_sb < n_cache)) || kv_sb % 8 ||
+      g_sb % 8 || kv_sb < 0 || g_sb < 0 || out_sb < 0)
+    return CSA2_EINVAL;
+  const int64_t kv_bytes = ((int64_t)(B - 1) * kv_sb + CSA2_D) * 2;
+  const int64_t g_bytes = ((int64_t)(B - 1) * g_sb + CSA2_D) * 2;
+  const int64_t st_bytes = (int64_t)B * 2 * CSA2_D * 2;
+  const int64_t rows = n_cache > 0 ? (int64_t)(B - 1) * out_sb + n_cache : 0;
+  const int64_t o_bytes = rows * (fp4 ? CSA2_D / 2 : CSA2_D * 2);
+  const int64_t s_bytes = fp4 ? rows * (CSA2_D / 16) : 0;
+  if (overlap(state, st_bytes, kv, kv_bytes) || overlap(state, st_bytes, gate, g_bytes) ||
+      overlap(out, o_bytes, kv, kv_bytes) || overlap(out, o_bytes, gate, g_bytes) ||
+      overlap(out, o_bytes, state, st_bytes) ||
+      (fp4 && (overlap(out_scale, s_bytes, kv, kv_bytes) ||
+               overlap(out_scale, s_bytes, gate, g_bytes) ||
+               overlap(out_scale, s_bytes, state, st_bytes) ||
+               overlap(out_scale, s_bytes, out, o_bytes))))
+    return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_compress_step(B, kv, kv_sb, gate, g_sb, pos, state, fp4, out,
+                                             out_scale, out_sb, n_cache, stream));
+}
+
+int csa2_quant_nvfp4(const void* src, csa2_dtype src_dt, int64_t rows, int cols,
+                     uint8_t* packed, uint8_t* scale_e4m3, hipStream_t stream) {
+  if (rows < 0 || cols < 16 || cols % 16) return CSA2_EINVAL;
+  if (src_dt != CSA2_BF16 && src_dt != CSA2_F32) return CSA2_EUNSUPPORTED;
+  if (rows == 0) return CSA2_OK;
+  if (!src || !packed || !scale_e4m3) return CSA2_EINVAL;
+  if (!aligned(src, 16) || !aligned(packed, 8)) return CSA2_EINVAL;
+  if (rows > (int64_t(1) << 40) / cols) return CSA2_EUNSUPPORTED;
+  const int64_t n = rows * cols;
+  const int64_t src_bytes = n * (src_dt == CSA2_F32 ? 4 : 2);
+  if (overlap(packed, n / 2, src, src_bytes) || overlap(scale_e4m3, n / 16, src, src_bytes) ||
+      overlap(packed, n / 2, scale_e4m3, n / 16))
+    return CSA2_EINVAL;
+  clear_stale_error();
+  return launched(csa2::launch_quant_nvfp4(src, src_dt == CSA2_F32, rows, cols, packed,
+                                           scale_e4m3, stream));
 }
 
 int csa2_index_scores(int mode, int B, int Tq, const void* q, csa2_dtype q_dt, const float* w,

@@ -12,6 +12,16 @@ namespace csa2 {
 hipError_t launch_compress(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
                            int64_t g_sb, void* out, int64_t out_sb, hipStream_t s);
 
+hipError_t launch_compress_nvfp4(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
+                                 int64_t g_sb, uint8_t* codes, uint8_t* scales, int64_t out_sb,
+                                 hipStream_t s);
+hipError_t launch_compress_step(int B, const void* kv, int64_t kv_sb, const void* gate,
+                                int64_t g_sb, const int64_t* pos, void* state, bool fp4,
+                                void* out, uint8_t* out_scale, int64_t out_sb, int64_t n_cache,
+                                hipStream_t s);
+hipError_t launch_quant_nvfp4(const void* src, bool f32_in, int64_t rows, int cols,
+                              uint8_t* packed, uint8_t* scales, hipStream_t s);
+
 hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const void* k,
                              bool k_fp8, int64_t k_sb, int64_t n_cache, const int64_t* q_pos,
                              float* scores, int64_t s_stride, float* block_max,

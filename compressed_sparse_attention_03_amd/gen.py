@@ -27,6 +27,10 @@ Layout of one input set (all torch tensors on ``device``):
   raw, gate  bf16 [B][T_c][512]  compressor input (raw KV latents and gate
              logits) for raw positions raw_pos0 .. raw_pos0+T_c-1; its
              output belongs in lat rows raw_pos0/2 ..
+  tok_kv, tok_gate  bf16 [B][512]  (configs with a compressor decode step)
+             the token at raw position step_pos[b] = t_last (odd), whose
+             partner, token t_last - 1, is parked in state bf16 [B][2][512]
+             (kv row, gate row); the step writes lat row t_last // 2
 """
 from __future__ import annotations
 
@@ -56,6 +60,7 @@ class Config:
     comp_T: int = 0        # compressor input tokens (0 = no compressor)
     comp_pos0: int = 0     # raw position of the first compressor token
     comp_from_win: bool = False  # compressor input is a slice of the window ring
+    comp_step: bool = False  # one compressor decode step (pair completed at t_last)
     win_pos0: int = 0      # lowest raw position the window source must hold
     seed: int = 0
     scale: float = 512 ** -0.5
@@ -89,8 +94,9 @@ def _configs():
         seed=3, desc="8 sequences x 1,048,576 raw tokens, bf16 caches (no compressor step)")
     c5 = Config(
         "1m_lowp", B=32, Tq=1, N=524288, t_last=1048575, W_cap=128,
-        key_fmt="fp8", lat_fmt="nvfp4", win_fmt="fp8", win_pos0=1048575 - 127,
-        seed=4, desc="32 sequences x 1,048,576 raw tokens, NVFP4 latents, FP8 window/keys")
+        key_fmt="fp8", lat_fmt="nvfp4", win_fmt="fp8", win_pos0=1048575 - 127, comp_step=True,
+        seed=4, desc="32 sequences x 1,048,576 raw tokens, NVFP4 latents, FP8 window/keys; "
+                     "the compressor's decode step writes the newest latent first")
     c6 = Config(
         "1m_verify", B=8, Tq=5, N=524288, t_last=1048575, W_cap=256,
         win_pos0=1048575 - 4 - 127, seed=5,
@@ -182,6 +188,12 @@ def make_inputs(cfg: Config, device="cpu", seed: Optional[int] = None) -> dict:
         out["raw"], out["gate"] = raw, gate
     else:
         out["raw"] = out["gate"] = None
+    if cfg.comp_step:
+        assert cfg.t_last % 2 == 1 and cfg.t_last // 2 < N
+        out["tok_kv"] = _normal_bf16((B, D), g, dev)
+        out["tok_gate"] = _normal_bf16((B, D), g, dev)
+        out["state"] = _normal_bf16((B, 2, D), g, dev)
+        out["step_pos"] = torch.full((B,), cfg.t_last, dtype=torch.int64, device=dev)
     return out
 
 

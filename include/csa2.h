@@ -101,6 +101,66 @@ int csa2_compress(int B, int T, const void *kv, int64_t kv_sb,
                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * f1. Compressor writing the NVFP4 cache  ([NVFP4] section 3.2: the
+ * compressed KV is stored as E2M1 values in groups of 16 sharing one E4M3
+ * scale; during decode the unfinished half of a token pair waits in the
+ * compressor's state).
+ *
+ * Quantisation of a group of 16 values x (the section names the format, not
+ * the encoder; this is the plain reading):
+ *   scale   = the E4M3 value nearest to max|x| / 6, ties to the even code,
+ *             saturating at 448 (6 is the largest E2M1 magnitude);
+ *   code[i] = the E2M1 value nearest to x[i] / scale, ties to the even
+ *             code, saturating at +-6, sign bit from x[i] (x < 0);
+ *   a group whose scale is 0 stores all-zero codes.
+ * Both roundings are decided on the exact quotients.  csa2_dequant_nvfp4 is
+ * the inverse; a group of representable values (x = e2m1 * s with some
+ * |x| = 6 s) survives the round trip exactly.
+ *
+ * csa2_compress_nvfp4: the pooling of csa2_compress, kept in fp32 (not
+ *   rounded to bf16) and quantised in the same kernel.
+ *   kv, gate   : as for csa2_compress (T even, T = 0 or B = 0 is a no-op)
+ *   codes      : [B][rows][256] bytes, element 2i in the low nibble of byte
+ *                i; row g of sequence b at (b*out_sb + g)*256; 8-byte aligned
+ *   scale_e4m3 : [B][rows][32] bytes at (b*out_sb + g)*32
+ *   out_sb     : batch stride in ROWS (>= T/2 when B > 1), the layout
+ *                csa2_sparse_attn reads (lat, lat_scale, lat_sb).
+ *   Outputs must not overlap the inputs or each other.
+ *
+ * csa2_compress_step: one decode step for B sequences, each at its own raw
+ *   position pos[b] (device int64 [B]; negative = no token this step).
+ *   kv, gate : bf16 [B][512] with batch strides kv_sb, g_sb (elements)
+ *   state    : bf16 [B][2][512], device memory the caller allocates and
+ *              keeps between calls: the parked kv row, then its gate row
+ *   An even position t stores the token in state[b].  An odd position t
+ *   pools state[b] (token t-1) with the new token into cache row t/2 of
+ *   sequence b, which is written only if t/2 < n_cache (no error otherwise:
+ *   positions live on the device).  out_dt CSA2_BF16: out bf16 [B][rows][512]
+ *   (16-byte aligned), out_scale unused; CSA2_NVFP4: out = codes,
+ *   out_scale = scales, as for csa2_compress_nvfp4.  out_sb in rows
+ *   (>= n_cache when B > 1).  The written row is bit-identical to what
+ *   csa2_compress / csa2_compress_nvfp4 write for the same two tokens, so a
+ *   prefill of even length followed by decode steps fills the cache as one
+ *   batch call would.  A token at an odd position needs its partner parked
+ *   by an earlier step (or written into state by the caller).
+ *
+ * csa2_quant_nvfp4: the quantiser alone.  src [rows][cols] in src_dt
+ *   (CSA2_BF16 or CSA2_F32), 16-byte aligned, cols % 16 == 0; packed
+ *   [rows][cols/2] (8-byte aligned), scale_e4m3 [rows][cols/16].
+ * ---------------------------------------------------------------------- */
+int csa2_compress_nvfp4(int B, int T, const void *kv, int64_t kv_sb,
+                        const void *gate, int64_t g_sb, uint8_t *codes,
+                        uint8_t *scale_e4m3, int64_t out_sb,
+                        hipStream_t stream);
+int csa2_compress_step(int B, const void *kv, int64_t kv_sb, const void *gate,
+                       int64_t g_sb, const int64_t *pos, void *state,
+                       csa2_dtype out_dt, void *out, uint8_t *out_scale,
+                       int64_t out_sb, int64_t n_cache, hipStream_t stream);
+int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
+                     int cols, uint8_t *packed, uint8_t *scale_e4m3,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * a2 / a4. Indexer scores  ([NVFP4] section 3.3; [OQ3E] section 2.1).
  *
  *   score(p) = sum_{h<32} w[h] * max(0, q[h] . k[p])

@@ -316,8 +316,10 @@ def decode(inp: dict, K_b: int, K: int, W: int, scale: float, compress_first=Fal
 
     ``inp`` holds numpy arrays keyed as the input generator names them
     (q, sink, qs, ws, ks, qi, wi, ki, lat, lat_scale, win, win_scale, q_pos,
-    raw, gate) plus ``comp_pos0`` when ``compress_first``.  Returns a dict
-    of every intermediate."""
+    raw, gate) plus ``comp_pos0`` when ``compress_first``, and tok_kv,
+    tok_gate, state, step_pos for a compressor decode step, which runs
+    first whenever they are present.  Returns a dict of every
+    intermediate."""
     res = {}
     lat = inp["lat"]
     if compress_first:
@@ -326,7 +328,19 @@ def decode(inp: dict, K_b: int, K: int, W: int, scale: float, compress_first=Fal
         lat = lat.copy()
         lat[:, g0:g0 + comp_bits.shape[1]] = comp_bits
         res["comp"], res["comp64"] = comp_bits, comp64
-    res["lat"] = lat
+    lat_scale = inp.get("lat_scale")
+    if inp.get("tok_kv") is not None:
+        # the compressor's decode step completes a pair and writes its latent
+        state = inp["state"].copy()
+        lat = lat.copy()
+        if lat_scale is not None:
+            lat_scale = lat_scale.copy()
+            cache, fmt = (lat, lat_scale), "nvfp4"
+        else:
+            cache, fmt = lat, "bf16"
+        compress_decode(state, inp["tok_kv"], inp["tok_gate"], inp["step_pos"], cache,
+                        lat.shape[1], fmt)
+    res["lat"], res["lat_scale"] = lat, lat_scale
     q_pos = inp["q_pos"]
     B, Tq = q_pos.shape
     N = lat.shape[1]
@@ -336,7 +350,7 @@ def decode(inp: dict, K_b: int, K: int, W: int, scale: float, compress_first=Fal
     csc, cid = cand(inp["qi"], inp["wi"], inp["ki"], q_pos, blocks)
     sel = select(csc, K, ids=cid)
     out, lse = attn(inp["q"], lat, sel, inp["win"], q_pos, inp["sink"], W, scale,
-                    lat_scale=inp.get("lat_scale"), win_scale=inp.get("win_scale"))
+                    lat_scale=lat_scale, win_scale=inp.get("win_scale"))
     res.update(block_max=bm, forced=forced, blocks=blocks, cand_scores=csc,
                cand_ids=cid, sel=sel, out=out, lse=lse)
     return res

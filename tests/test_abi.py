@@ -163,3 +163,52 @@ def test_dequant_validation(L):
     assert L.csa2_dequant_nvfp4(FAKE, FAKE, 4, 24, FAKE, _lib.F32, None) == _lib.EINVAL  # cols % 16
     assert L.csa2_dequant_nvfp4(FAKE, NULL, 4, 32, FAKE, _lib.F32, None) == _lib.EINVAL
     assert L.csa2_dequant_nvfp4(FAKE, FAKE, 4, 32, ctypes.c_void_p(0x10002), _lib.BF16, None) == _lib.EINVAL
+
+
+def test_compress_nvfp4_validation(L):
+    s = None
+    A, G, C, S = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000))
+    assert L.csa2_compress_nvfp4(1, 3, A, 0, G, 0, C, S, 0, s) == _lib.EINVAL        # odd T
+    assert L.csa2_compress_nvfp4(0, 2, NULL, 0, NULL, 0, NULL, NULL, 0, s) == _lib.OK
+    assert L.csa2_compress_nvfp4(1, 2, A, 0, G, 0, C, NULL, 0, s) == _lib.EINVAL     # no scales
+    assert L.csa2_compress_nvfp4(1, 2, A, 0, G, 0, ctypes.c_void_p(0x300004), S, 0, s) == _lib.EINVAL
+    # batch stride (rows) smaller than the T/2 rows a sequence writes
+    assert L.csa2_compress_nvfp4(2, 8, A, 4096, G, 4096, C, S, 3, s) == _lib.EINVAL
+    # codes overlapping the input
+    assert L.csa2_compress_nvfp4(1, 4, A, 2048, G, 2048, ctypes.c_void_p(0x100100), S, 2, s) == _lib.EINVAL
+    assert L.csa2_compress_nvfp4(1, 4, A, 2048, G, 2048, C, ctypes.c_void_p(0x300040), 2, s) == _lib.EINVAL
+
+
+def test_compress_step_validation(L):
+    s = None
+    K, G, P, ST, O, SC = (ctypes.c_void_p(a) for a in
+                          (0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000))
+    ok = dict(B=2, kv=K, kv_sb=512, g=G, g_sb=512, pos=P, st=ST, dt=_lib.NVFP4, out=O, osc=SC,
+              out_sb=16, n=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.csa2_compress_step(a["B"], a["kv"], a["kv_sb"], a["g"], a["g_sb"], a["pos"],
+                                    a["st"], a["dt"], a["out"], a["osc"], a["out_sb"], a["n"], s)
+    assert call(B=0, kv=NULL) == _lib.OK
+    assert call(B=-1) == _lib.EINVAL
+    assert call(n=-1) == _lib.EINVAL
+    assert call(dt=_lib.FP8_E4M3) == _lib.EUNSUPPORTED
+    assert call(osc=NULL) == _lib.EINVAL                     # NVFP4 needs the scale rows
+    assert call(pos=ctypes.c_void_p(0x300004)) == _lib.EINVAL
+    assert call(kv_sb=256) == _lib.EINVAL                    # rows overlap
+    assert call(out_sb=8) == _lib.EINVAL                     # stride below n_cache
+    assert call(st=ctypes.c_void_p(0x100200)) == _lib.EINVAL  # state overlaps kv
+    assert call(out=ctypes.c_void_p(0x400100)) == _lib.EINVAL  # cache overlaps state
+    assert call(dt=_lib.BF16, out=ctypes.c_void_p(0x500008)) == _lib.EINVAL  # bf16 rows 16-aligned
+
+
+def test_quant_nvfp4_validation(L):
+    s = None
+    A, P, S = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000))
+    assert L.csa2_quant_nvfp4(A, _lib.BF16, 4, 24, P, S, s) == _lib.EINVAL   # cols % 16
+    assert L.csa2_quant_nvfp4(A, _lib.FP8_E4M3, 4, 32, P, S, s) == _lib.EUNSUPPORTED
+    assert L.csa2_quant_nvfp4(A, _lib.F32, 0, 32, P, S, s) == _lib.OK
+    assert L.csa2_quant_nvfp4(A, _lib.F32, 4, 32, NULL, S, s) == _lib.EINVAL
+    assert L.csa2_quant_nvfp4(MISALIGNED, _lib.F32, 4, 32, P, S, s) == _lib.EINVAL
+    assert L.csa2_quant_nvfp4(A, _lib.F32, 4, 32, ctypes.c_void_p(0x100010), S, s) == _lib.EINVAL

@@ -14,8 +14,8 @@ import torch
 
 from compressed_sparse_attention_03_amd import api, gen
 from oracle import csa2_ref as ref
-from tests.gpu_util import (BF16_TOL, LOWP_TOL, bf16_to_np, check_close, np_subset,
-                            oracle_path, rows_of, run_gpu_path, say, valid_sorted)
+from tests.gpu_util import (BF16_TOL, LOWP_TOL, bf16_to_np, check_close, check_fp4_pooling,
+                            np_subset, oracle_path, rows_of, run_gpu_path, say, valid_sorted)
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +194,8 @@ def test_chained_small(name, kw):
     res = oracle_path(host, cfg, compress_first=cfg.comp_T > 0)
     path = run_gpu_path(inp, compress_first=cfg.comp_T > 0)
     _compare_chain(cfg, path, res, list(range(cfg.R)))
+    if cfg.comp_step:
+        _check_step_row(cfg, inp, host, list(range(cfg.B)))
 
 
 def _compare_chain(cfg, path, res, rows):
@@ -229,8 +231,23 @@ def _full(name, seqs, queries=None):
         got = bf16_to_np(inp["lat"][list(seqs), g0:g0 + cfg.comp_T // 2])
         _, y64 = ref.compress(host["raw"], host["gate"])
         check_close("compressor rows", got, y64, BF16_TOL)
+    if cfg.comp_step:
+        _check_step_row(cfg, inp, host, seqs)
     del inp, path
     torch.cuda.empty_cache()
+
+
+def _check_step_row(cfg, inp, host, seqs):
+    """The latent the compressor's decode step wrote (row t_last // 2)."""
+    g = cfg.t_last // 2
+    raw = np.stack([host["state"][:, 0], host["tok_kv"]], 1)
+    gate = np.stack([host["state"][:, 1], host["tok_gate"]], 1)
+    if cfg.lat_fmt == "nvfp4":
+        check_fp4_pooling("decode-step row", inp["lat"][list(seqs), g:g + 1].cpu().numpy(),
+                          inp["lat_scale"][list(seqs), g:g + 1].cpu().numpy(), raw, gate)
+    else:
+        _, y64 = ref.compress(raw, gate)
+        check_close("decode-step row", bf16_to_np(inp["lat"][list(seqs), g:g + 1]), y64, BF16_TOL)
 
 
 def test_full_128k():

@@ -29,7 +29,7 @@ def _run_both(cfg, compress_first=False, q_pos=None, inp_edit=None):
     if inp_edit:
         inp_edit(inp)
     res = ref.decode(inp, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=compress_first)
-    inp_b = dict(inp, lat=res["lat"])
+    inp_b = dict(inp, lat=res["lat"], lat_scale=res["lat_scale"])
     rows = [brute.decode_row(inp_b, r, cfg.K_b, cfg.K, cfg.W, cfg.scale) for r in range(cfg.R)]
     return inp, res, rows
 
@@ -96,8 +96,17 @@ def test_short_contexts():
 
 def test_low_precision_formats_match_brute():
     cfg = gen.shrink(gen.CONFIGS["1m_lowp"], B=2, N=1024, t_last=2047, K_b=16, K=64, seed=24)
-    _, res, rows = _run_both(cfg)
+    inp, res, rows = _run_both(cfg)
     _compare(cfg, res, rows)
+    # the compressor's decode step wrote the newest latent (row 1023): the
+    # NVFP4 encoding of the parked token pooled with the new one
+    raw = np.stack([inp["state"][:, 0], inp["tok_kv"]], 1)
+    gate = np.stack([inp["state"][:, 1], inp["tok_gate"]], 1)
+    packed, scales, _ = ref.compress_nvfp4(raw, gate)
+    assert np.array_equal(res["lat"][:, 1023], packed[:, 0])
+    assert np.array_equal(res["lat_scale"][:, 1023], scales[:, 0])
+    assert not np.array_equal(inp["lat"][:, 1023], packed[:, 0])
+    assert np.array_equal(res["lat"][:, :1023], inp["lat"][:, :1023])
 
 
 def test_prefill_shape_matches_brute():
