@@ -54,6 +54,8 @@ def step_bytes(cfg) -> dict:
     keys_per_seq = n_vis(t_hi, cfg.N)  # one pass over the keys serves all queries of a sequence
     b = {}
     b["compress"] = B * (cfg.comp_T * D * 2 * 2 + (cfg.comp_T // 2) * D * 2) if cfg.comp_T else 0
+    if cfg.comp_step:  # new token + parked token (kv and gate rows), position; one latent row out
+        b["compress"] += B * (4 * D * 2 + 8 + lat_row)
     b["index_scan"] = B * keys_per_seq * DI * kel + R * (HI * DI * 2 + HI * 4 + nblk * 4 + 8)
     b["select_blocks"] = R * (nblk * 4 + cfg.K_b * 4)
     b["index_cand"] = R * (cfg.K_b * BLK * DI * kel + HI * DI * 2 + HI * 4 + cfg.K_b * 4 +
@@ -170,6 +172,34 @@ def time_layer_stack(steps, torch, gen, api):
         "step_hbm_frac": round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_bytes": total,
     }
+
+
+def time_compress_fp4(torch, api, launches=10):
+    """The compressor writing the NVFP4 cache for a whole 1M-token sequence
+    (1,048,576 raw tokens -> 524,288 latents): streaming, HBM-bound."""
+    T = 1 << 20
+    g = torch.Generator(device="cuda").manual_seed(7)
+    raw = torch.randn((1, T, D), generator=g, device="cuda").bfloat16()
+    gate = torch.randn((1, T, D), generator=g, device="cuda").bfloat16()
+    codes = torch.empty((1, T // 2, D // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, T // 2, D // 16), dtype=torch.uint8, device="cuda")
+    api.compress_nvfp4(raw, gate, codes, scales)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(launches):
+        api.compress_nvfp4(raw, gate, codes, scales)
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / launches
+    nbytes = 2 * T * D * 2 + (T // 2) * (D // 2 + D // 16)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] compress_nvfp4 1M tokens: {us:.1f} us/launch = {gbs:.0f} GB/s")
+    del raw, gate, codes, scales
+    return {"workload": "compressor with NVFP4 epilogue over one 1,048,576-token sequence "
+                        "(524,288 latents)", "us_per_launch": round(us, 2),
+            "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def scan_launch_us(torch, api, path, inp, launches):
@@ -308,7 +338,8 @@ def main():
         lsb = step_bytes(lcfg)
         lt = sum(lsb.values())
         extra["lowp_1m"] = {
-            "workload": "32 sequences x 1M ctx, NVFP4 latents, FP8 E4M3 window + index keys",
+            "workload": "32 sequences x 1M ctx, NVFP4 latents, FP8 E4M3 window + index keys; "
+                        "the step starts with the compressor's decode step (NVFP4 write)",
             "queries_per_s": round(lcfg.R / (lms * 1e-3), 1), "ms_per_step": round(lms, 4),
             "step_hbm_frac": round(lt / (lms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "index_scan_GBs_eager_stage": round(lsb["index_scan"] / (lst["index_scan"] * 1e-3) / 1e9, 1),
@@ -331,6 +362,8 @@ def main():
         del vinp
         torch.cuda.empty_cache()
         extra["layer_stack_1m"] = time_layer_stack(max(3, args.steps // 4), torch, gen, api)
+        torch.cuda.empty_cache()
+        extra["compress_nvfp4_1m"] = time_compress_fp4(torch, api)
         torch.cuda.empty_cache()
         pcfg, pinp, ppath, pms, pst = time_config("prefill", 2, 1, torch, gen, api)
         del ppath

@@ -26,56 +26,19 @@
 namespace csa2 {
 
 // The pooled value of one channel: softmax over the two gate logits, then
-// the weighted sum of the two tokens.  Every cache writer calls this one
-// function, so the bf16, NVFP4 and decode-step outputs agree bit for bit.
+// the weighted sum of the two tokens.  With two logits the softmax weight of
+// token 0 is 1 / (1 + e^(z1 - z0)), so one exponential and one reciprocal
+// suffice: y = a1 + w0 (a0 - a1).  The hardware exp2 and reciprocal (about
+// one ulp each) keep the pooled value within a few fp32 ulps of
+// max(|a0|, |a1|) of the exact one, and make the kernel streaming-bound
+// rather than ALU-bound.  Every cache writer calls this one function, so the
+// bf16, NVFP4 and decode-step outputs agree bit for bit.
 __device__ __forceinline__ float pool_pair(float a0, float a1, float z0, float z1) {
-  const float m = fmaxf(z0, z1);
-  const float e0 = expf(z0 - m), e1 = expf(z1 - m);
-  // the fused multiply-add is written out so that no kernel's contraction
-  // choice can change the bits
-  return fmaf(e0, a0, e1 * a1) / (e0 + e1);
+  const float e = __builtin_amdgcn_exp2f((z1 - z0) * 1.4426950408889634f);
+  const float w0 = __builtin_amdgcn_rcpf(1.0f + e);
+  return fmaf(w0, a0 - a1, a1);
 }
 
-__global__ __launch_bounds__(256) void compress_kernel(
-    const uint16_t* __restrict__ kv, int64_t kv_sb, const uint16_t* __restrict__ gate,
-    int64_t g_sb, uint16_t* __restrict__ out, int64_t out_sb, int G) {
-  // 64 threads per group row (8 channels each); 4 groups per 256-thread block.
-  const int b = blockIdx.y;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= G) return;
-  const int c0 = (threadIdx.x & 63) * 8;
-  const uint16_t* x0p = kv + b * kv_sb + (int64_t)(2 * g) * D + c0;
-  const uint16_t* l0p = gate + b * g_sb + (int64_t)(2 * g) * D + c0;
-  const u32x4 x0 = *reinterpret_cast<const u32x4*>(x0p);
-  const u32x4 x1 = *reinterpret_cast<const u32x4*>(x0p + D);
-  const u32x4 l0 = *reinterpret_cast<const u32x4*>(l0p);
-  const u32x4 l1 = *reinterpret_cast<const u32x4*>(l0p + D);
-  u32x4 y;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float r[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int sh = 16 * h;
-      const float a0 = bf16_to_f32((x0[i] >> sh) & 0xffffu);
-      const float a1 = bf16_to_f32((x1[i] >> sh) & 0xffffu);
-      const float z0 = bf16_to_f32((l0[i] >> sh) & 0xffffu);
-      const float z1 = bf16_to_f32((l1[i] >> sh) & 0xffffu);
-      r[h] = pool_pair(a0, a1, z0, z1);
-    }
-    y[i] = pack_bf16x2(r[0], r[1]);
-  }
-  *reinterpret_cast<u32x4*>(out + b * out_sb + (int64_t)g * D + c0) = y;
-}
-
-hipError_t launch_compress(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
-                           int64_t g_sb, void* out, int64_t out_sb, hipStream_t s) {
-  const int G = T / 2;
-  dim3 grid((G + 3) / 4, B);
-  hipLaunchKernelGGL(compress_kernel, grid, dim3(256), 0, s, (const uint16_t*)kv, kv_sb,
-                     (const uint16_t*)gate, g_sb, (uint16_t*)out, out_sb, G);
-  return hipGetLastError();
-}
 
 
 // ---- NVFP4 group quantiser ------------------------------------------------
@@ -95,8 +58,35 @@ __device__ __forceinline__ uint32_t e4m3_nearest(float q) {
   return (uint32_t)rintf(q * 512.0f);
 }
 
-// One group of 16 values -> its scale code and 16 E2M1 codes packed low
-// nibble first (element 2i in bits 8i..8i+3 of the 64-bit word).
+// Scale code of a group from the largest magnitude in it.
+__device__ __forceinline__ uint32_t fp4_scale(float amax) { return e4m3_nearest(amax / 6.0f); }
+
+// E2M1 codes of 8 values under scale code sc, element i in bits 4i..4i+3.
+__device__ __forceinline__ uint32_t fp4_codes8(const float* x, uint32_t sc) {
+  if (sc == 0u) return 0u;
+  const float s = e4m3_to_f32(sc);
+  // rounding midpoints between neighbouring E2M1 magnitudes, times the scale
+  // (exact: at most 7 significant bits, far from fp32's range limits)
+  const float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s;
+  const float t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = fabsf(x[i]);
+    // binary search over the 7 midpoints; a tie goes to the magnitude with
+    // an even code: 0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2,
+    // 3.5 -> 4, 5 -> 4 (hence >= at 0.75, 1.75, 3.5 and > elsewhere)
+    const bool hi = a >= t3;
+    const bool mid = a >= (hi ? t5 : t1);
+    const bool lo = a > (hi ? (mid ? t6 : t4) : (mid ? t2 : t0));
+    const uint32_t mag = (hi ? 4u : 0u) | (mid ? 2u : 0u) | (lo ? 1u : 0u);
+    w |= (mag | (x[i] < 0.0f ? 8u : 0u)) << (4 * i);
+  }
+  return w;
+}
+
+// One group of 16 values -> its scale code and 16 codes packed low nibble
+// first (element 2i in the low nibble of byte i).
 struct Fp4Group {
   u32x2 codes;
   uint32_t scale;
@@ -107,25 +97,8 @@ __device__ __forceinline__ Fp4Group quantise16(const float (&x)[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
   Fp4Group r;
-  r.scale = e4m3_nearest(amax / 6.0f);
-  r.codes = u32x2{0u, 0u};
-  if (r.scale == 0u) return r;
-  const float s = e4m3_to_f32(r.scale);
-  // rounding midpoints between neighbouring E2M1 magnitudes, times the scale
-  // (exact: at most 7 significant bits, far from fp32's range limits)
-  const float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s;
-  const float t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float a = fabsf(x[i]);
-    // a tie goes to the magnitude with an even code: 0.25 -> 0, 0.75 -> 1,
-    // 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4
-    const uint32_t mag = (uint32_t)(a > t0) + (uint32_t)(a >= t1) + (uint32_t)(a > t2) +
-                         (uint32_t)(a >= t3) + (uint32_t)(a > t4) + (uint32_t)(a >= t5) +
-                         (uint32_t)(a > t6);
-    const uint32_t code = mag | (x[i] < 0.0f ? 8u : 0u);
-    r.codes[i >> 3] |= code << (4 * (i & 7));
-  }
+  r.scale = fp4_scale(amax);
+  r.codes = u32x2{fp4_codes8(x, r.scale), fp4_codes8(x + 8, r.scale)};
   return r;
 }
 
@@ -134,22 +107,6 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4& v, float* x) {
   for (int i = 0; i < 4; ++i) {
     x[2 * i] = bf16_to_f32(v[i] & 0xffffu);
     x[2 * i + 1] = bf16_to_f32(v[i] >> 16);
-  }
-}
-
-// 16 pooled channels [c0, c0+16) of latent g from token rows t0 = 2g and
-// t0 + 1 (row pointers at channel c0).
-__device__ __forceinline__ void pool16(const uint16_t* x0p, const uint16_t* x1p,
-                                       const uint16_t* l0p, const uint16_t* l1p, float (&y)[16]) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    float a0[8], a1[8], z0[8], z1[8];
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(x0p + 8 * h), a0);
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(x1p + 8 * h), a1);
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(l0p + 8 * h), z0);
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(l1p + 8 * h), z1);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[8 * h + i] = pool_pair(a0[i], a1[i], z0[i], z1[i]);
   }
 }
 
@@ -175,23 +132,65 @@ __device__ __forceinline__ void store16(const float (&y)[16], void* row, uint8_t
   }
 }
 
-// Compressor with the NVFP4 epilogue: 32 lanes per latent (16 channels
-// each), 8 latents per 256-thread block.  codes: [B][rows][256] bytes,
-// scales [B][rows][32], batch stride out_sb rows for both.
-__global__ __launch_bounds__(256) void compress_fp4_kernel(
+// The compressor over whole rows: one wave per latent row at a time, 8
+// channels per lane, so every load instruction reads 1 KiB of one row
+// contiguously (non-temporal: nothing is read twice).  Each wave takes two
+// consecutive latents and issues all eight row loads before using any.
+// FP4 = false: bf16 rows [B][rows][512] (each lane stores 16 bytes).
+// FP4 = true: the NVFP4 epilogue -- the two lanes of a 16-channel group
+// exchange their partial maxima by DPP, each stores its 8 codes (4 bytes)
+// and the even lane the group's scale byte; codes [B][rows][256], scales
+// [B][rows][32].  Batch stride out_sb: in elements for bf16 (any multiple of
+// 8), in rows for NVFP4.
+constexpr int CF_LAT_PER_WAVE = 2;
+
+template <bool FP4>
+__global__ __launch_bounds__(256) void compress_rows_kernel(
     const uint16_t* __restrict__ kv, int64_t kv_sb, const uint16_t* __restrict__ gate,
-    int64_t g_sb, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int64_t out_sb,
-    int G) {
+    int64_t g_sb, void* __restrict__ out, uint8_t* __restrict__ scales, int64_t out_sb, int G) {
   const int b = blockIdx.y;
-  const int g = blockIdx.x * 8 + (threadIdx.x >> 5);
-  if (g >= G) return;
-  const int c0 = (threadIdx.x & 31) * 16;
-  const int64_t x0 = b * kv_sb + (int64_t)(2 * g) * D + c0;
-  const int64_t z0 = b * g_sb + (int64_t)(2 * g) * D + c0;
-  float y[16];
-  pool16(kv + x0, kv + x0 + D, gate + z0, gate + z0 + D, y);
-  const int64_t row = b * out_sb + g;
-  store16<true>(y, codes + row * (D / 2), scales + row * (D / 16), c0);
+  const int lane = threadIdx.x & 63;
+  const int g0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * CF_LAT_PER_WAVE;
+  if (g0 >= G) return;  // whole wave
+  const int c0 = lane * 8;
+  u32x4 v[CF_LAT_PER_WAVE][4];
+#pragma unroll
+  for (int j = 0; j < CF_LAT_PER_WAVE; ++j) {
+    if (g0 + j < G) {
+      const u32x4* x = reinterpret_cast<const u32x4*>(kv + b * kv_sb + (int64_t)(2 * (g0 + j)) * D + c0);
+      const u32x4* z = reinterpret_cast<const u32x4*>(gate + b * g_sb + (int64_t)(2 * (g0 + j)) * D + c0);
+      v[j][0] = __builtin_nontemporal_load(x);
+      v[j][1] = __builtin_nontemporal_load(x + D / 8);
+      v[j][2] = __builtin_nontemporal_load(z);
+      v[j][3] = __builtin_nontemporal_load(z + D / 8);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < CF_LAT_PER_WAVE; ++j) {
+    if (g0 + j >= G) break;  // whole wave
+    float a0[8], a1[8], z0[8], z1[8], y[8];
+    unpack_bf16x8(v[j][0], a0);
+    unpack_bf16x8(v[j][1], a1);
+    unpack_bf16x8(v[j][2], z0);
+    unpack_bf16x8(v[j][3], z1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = pool_pair(a0[i], a1[i], z0[i], z1[i]);
+    if constexpr (FP4) {
+      const int64_t row = b * out_sb + g0 + j;
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(y[i]));
+      am = fmaxf(am, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(am))));  // partner lane
+      const uint32_t sc = fp4_scale(am);
+      reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(out) + row * (D / 2))[lane] = fp4_codes8(y, sc);
+      if ((lane & 1) == 0) scales[row * (D / 16) + (lane >> 1)] = (uint8_t)sc;
+    } else {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+      reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + b * out_sb + (int64_t)(g0 + j) * D)[lane] = o;
+    }
+  }
 }
 
 // One decode step of the compressor for B sequences, each at its own raw
@@ -206,25 +205,43 @@ __global__ __launch_bounds__(256) void compress_step_kernel(
     void* __restrict__ out, uint8_t* __restrict__ out_scale, int64_t out_sb, int64_t n_cache) {
   const int b = blockIdx.x * 8 + (threadIdx.x >> 5);
   if (b >= B) return;
-  const int64_t t = pos[b];
-  if (t < 0) return;
   const int c0 = (threadIdx.x & 31) * 16;
-  const uint16_t* xn = kv + b * kv_sb + c0;
-  const uint16_t* zn = gate + b * g_sb + c0;
-  uint16_t* sx = state + (int64_t)b * 2 * D + c0;  // parked kv row, then gate row
-  uint16_t* sz = sx + D;
+  const u32x4* xn = reinterpret_cast<const u32x4*>(kv + b * kv_sb + c0);
+  const u32x4* zn = reinterpret_cast<const u32x4*>(gate + b * g_sb + c0);
+  u32x4* sx = reinterpret_cast<u32x4*>(state + (int64_t)b * 2 * D + c0);  // parked kv row
+  u32x4* sz = sx + D / 8;                                                   // its gate row
+  // the position, the new token and the parked one are fetched together
+  const int64_t t = pos[b];
+  u32x4 x[2][2], z[2][2];  // [parked, new][half]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    x[0][h] = sx[h];
+    z[0][h] = sz[h];
+    x[1][h] = xn[h];
+    z[1][h] = zn[h];
+  }
+  if (t < 0) return;
   if ((t & 1) == 0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      reinterpret_cast<u32x4*>(sx)[h] = reinterpret_cast<const u32x4*>(xn)[h];
-      reinterpret_cast<u32x4*>(sz)[h] = reinterpret_cast<const u32x4*>(zn)[h];
+      sx[h] = x[1][h];
+      sz[h] = z[1][h];
     }
     return;
   }
   const int64_t g = t >> 1;
   if (g >= n_cache) return;
   float y[16];
-  pool16(sx, xn, sz, zn, y);
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float a0[8], a1[8], z0[8], z1[8];
+    unpack_bf16x8(x[0][h], a0);
+    unpack_bf16x8(x[1][h], a1);
+    unpack_bf16x8(z[0][h], z0);
+    unpack_bf16x8(z[1][h], z1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[8 * h + i] = pool_pair(a0[i], a1[i], z0[i], z1[i]);
+  }
   const int64_t row = b * out_sb + g;
   if constexpr (FP4)
     store16<true>(y, static_cast<uint8_t*>(out) + row * (D / 2), out_scale + row * (D / 16), c0);
@@ -259,14 +276,30 @@ __global__ __launch_bounds__(256) void quant_fp4_kernel(const void* __restrict__
   scales[i] = (uint8_t)q.scale;
 }
 
+static hipError_t launch_rows(bool fp4, int B, int T, const void* kv, int64_t kv_sb,
+                              const void* gate, int64_t g_sb, void* out, uint8_t* scales,
+                              int64_t out_sb, hipStream_t s) {
+  const int G = T / 2;
+  constexpr int per_block = 4 * CF_LAT_PER_WAVE;
+  dim3 grid((G + per_block - 1) / per_block, B);
+  if (fp4)
+    hipLaunchKernelGGL(compress_rows_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)kv,
+                       kv_sb, (const uint16_t*)gate, g_sb, out, scales, out_sb, G);
+  else
+    hipLaunchKernelGGL(compress_rows_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)kv,
+                       kv_sb, (const uint16_t*)gate, g_sb, out, scales, out_sb, G);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
+                           int64_t g_sb, void* out, int64_t out_sb, hipStream_t s) {
+  return launch_rows(false, B, T, kv, kv_sb, gate, g_sb, out, nullptr, out_sb, s);
+}
+
 hipError_t launch_compress_nvfp4(int B, int T, const void* kv, int64_t kv_sb, const void* gate,
                                  int64_t g_sb, uint8_t* codes, uint8_t* scales, int64_t out_sb,
                                  hipStream_t s) {
-  const int G = T / 2;
-  dim3 grid((G + 7) / 8, B);
-  hipLaunchKernelGGL(compress_fp4_kernel, grid, dim3(256), 0, s, (const uint16_t*)kv, kv_sb,
-                     (const uint16_t*)gate, g_sb, codes, scales, out_sb, G);
-  return hipGetLastError();
+  return launch_rows(true, B, T, kv, kv_sb, gate, g_sb, codes, scales, out_sb, s);
 }
 
 hipError_t launch_compress_step(int B, const void* kv, int64_t kv_sb, const void* gate,

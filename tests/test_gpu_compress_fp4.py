@@ -156,7 +156,9 @@ def test_compress_step_stream(fmt):
         for b in range(B):
             m[b, (start[b] + 1) // 2 if start[b] % 2 == 0 else start[b] // 2:min(stop[b] // 2, n_cache)] = True
         check_close("compress_step bf16", got[m], y64[:, :n_cache][m], BF16_TOL)
-        assert np.all(np.abs(got[m] - y64[:, :n_cache][m]) <= np.abs(y64[:, :n_cache][m]) * 2 ** -8 + 1e-30)
+        x = ref.bf16_array(r[:, :2 * n_cache]).reshape(B, n_cache, 2, 512)
+        slack = 1e-6 * (np.abs(x[:, :, 0]) + np.abs(x[:, :, 1]))
+        assert np.all(np.abs(got[m] - y64[:, :n_cache][m]) <= np.abs(y64[:, :n_cache][m]) * 2 ** -8 + slack[m])
     else:
         check_fp4_pooling("compress_step nvfp4", cache[0][1:2, 0:n_cache].cpu().numpy(),
                           cache[1][1:2, 0:n_cache].cpu().numpy(), r[1:2, :2 * n_cache],

@@ -45,8 +45,11 @@ def test_compress_stage_tiny():
     bits, y64 = ref.compress(host["raw"], host["gate"])
     got = bf16_to_np(out)
     check_close("compress", got, y64, BF16_TOL)
-    # stronger than the bar: within one bf16 rounding of the exact value
-    assert np.all(np.abs(got - y64) <= np.abs(y64) * 2 ** -8 + 1e-30)
+    # stronger than the bar: within one bf16 rounding of the exact value, up
+    # to the fp32 pooling error (1e-6 of the two tokens' magnitudes)
+    x = ref.bf16_array(host["raw"]).reshape(*y64.shape[:2], 2, 512)
+    slack = 1e-6 * (np.abs(x[:, :, 0]) + np.abs(x[:, :, 1]))
+    assert np.all(np.abs(got - y64) <= np.abs(y64) * 2 ** -8 + slack)
     exact = (gen.to_numpy(out) == bits).mean()
     say(f"  compress: {exact * 100:.3f}% of outputs bit-identical to the oracle's bf16")
 
