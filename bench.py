@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "CSA2 decode queries/s (64 heads) at 1M ctx; % HBM peak; prefill indexer MFMA %"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak
-MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA peak
+MFMA_BF16_PEAK_TFS = 2500.0
+MFMA_FP8_PEAK_TFS = 5000.0  # MI355X dense fp8 MFMA peak
 D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
 
 
@@ -377,6 +378,18 @@ def main():
             "stages_us_eager": {k: round(v * 1e3, 2) for k, v in pst.items()},
         }
         del pinp
+        torch.cuda.empty_cache()
+        fcfg, finp, fpath, fms, fst = time_config("prefill_fp8", 2, 1, torch, gen, api)
+        del fpath
+        ftfs = prefill_indexer_flops(fcfg) / (fst["index_scan"] * 1e-3) / 1e12
+        extra["prefill_fp8"] = {
+            "workload": "the same chunked prefill with FP8 E4M3 index keys (FP8 MFMA indexer)",
+            "indexer_TFLOPs": round(ftfs, 2), "indexer_mfma_frac_fp8": round(ftfs / MFMA_FP8_PEAK_TFS, 4),
+            "indexer_mfma_frac_of_bf16_peak": round(ftfs / MFMA_BF16_PEAK_TFS, 4),
+            "tokens_per_s": round(fcfg.R / (fms * 1e-3), 1), "ms_per_step": round(fms, 3),
+            "stages_us_eager": {k: round(v * 1e3, 2) for k, v in fst.items()},
+        }
+        del finp
         torch.cuda.empty_cache()
         inp = gen.make_inputs(cfg, device="cuda") if not args.no_cpu_baseline else None
     result["extra"] = extra

@@ -177,150 +177,308 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 // ---- several queries per sequence: key tiles shared through LDS -------------
 // A block = NW waves x QW queries = NW*QW consecutive queries of one
-// sequence, over one key range.  32-key tiles (8 KiB of bf16 keys) are read
-// coalesced by the whole block, DEPTH tiles ahead, into a double-buffered LDS
-// tile that every wave uses for all of its queries: the keys cross HBM once
-// per NW*QW queries.  v_mfma_f32_32x32x16_bf16: A = 32 heads x 16 dims of a
-// query (registers, loaded once), B = 16 dims x 32 keys of the LDS tile,
-// D = heads x keys; lane l holds key l%32 and heads 8(i/4) + 4(l/32) + i%4 of
-// accumulator element i.  Epilogue per query and 32 keys: ReLU x w_h over the
-// lane's 16 heads, one cross-half shuffle for the other 16, causal mask, max
-// over each 8-key block.
+// sequence, over one key range.  32-key tiles (8 KiB of bf16 keys, 4 KiB of
+// FP8) are read coalesced by the whole block, DEPTH tiles ahead, into a
+// double-buffered LDS tile that every wave uses for all of its queries: the
+// keys cross HBM once per NW*QW queries.
+// bf16 keys: v_mfma_f32_32x32x16_bf16, 8 per query and tile (K = 16 dims
+// each); FP8 keys: v_mfma_f32_32x32x64_f8f6f4 on E4M3 codes, 2 per query and
+// tile (the query rounded to E4M3 once, exact for the small integers index
+// queries take).  A = 32 heads x K dims of a query (registers, loaded once),
+// B = K dims x 32 keys from the LDS tile, D = heads x keys; lane l holds key
+// l % 32 and heads 8(i/4) + 4(l/32) + i%4 of accumulator element i.  Lane
+// half h = l / 32 supplies the same dims of A and B (the dot product does not
+// care which dims a k-slot carries).
+// Each wave issues the MFMAs of all its queries before their epilogues, so
+// the epilogue of one query runs on the vector ALU while the matrix core
+// works on the next.  Epilogue per query and 32 keys: ReLU x w_h over the
+// lane's 16 heads, the other 16 from the partner half by one lane swap
+// (v_permlane32_swap; with two queries one swap serves both, each half of
+// the wave then finishing one query), causal mask, max over each 8-key block
+// by three DPP steps.
 // Prefill (thousands of queries, MFMA-bound): 8 waves x 2 queries, 8 key
 // ranges with the range as the block id's low index, so that each XCD keeps
 // "its" range resident in L2 while all query groups stream through it.
-// Verification decode (a few queries per sequence, HBM-bound): 4 waves x 2
-// queries, 3 tiles in flight, enough key ranges to fill the chip.
-constexpr int TS_TILE = 32;              // keys per tile
-constexpr int TS_LD = DI * 2 + 16;       // LDS bytes per key row (padded)
+// Verification decode (a few queries per sequence, HBM-bound): 8 waves x 1
+// query, 6 tiles in flight, enough key ranges to fill the chip.
+constexpr int TS_TILE = 32;  // keys per tile
 
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+template <typename KT>
+struct TileKeys;
+template <>
+struct TileKeys<KBf16> {
+  static constexpr int ROWB = DI * 2;      // bytes per key row
+  static constexpr int LD = ROWB + 16;     // LDS pitch (padded)
+  static constexpr int NK = 8;             // MFMAs per query and tile
+  typedef bf16x8 Op;                       // one MFMA operand
+  typedef bf16x8 QOp[8];
+};
+template <>
+struct TileKeys<KFp8> {
+  static constexpr int ROWB = DI;
+  static constexpr int LD = ROWB + 16;
+  static constexpr int NK = 2;
+  typedef i32x8 Op;
+  typedef i32x8 QOp[2];
+};
 
-template <int NW, int QW, int DEPTH>
+// this lane's A operands of query row r (32 heads x 128 dims)
+__device__ __forceinline__ void tile_query(const uint16_t* q, int kn, int half, bf16x8 (&qa)[8]) {
+  const uint16_t* qr = q + kn * DI + 8 * half;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) qa[c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+}
+__device__ __forceinline__ void tile_query(const uint16_t* q, int kn, int half, i32x8 (&qa)[2]) {
+  const uint16_t* qr = q + kn * DI + 32 * half;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(qr + 64 * c);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x4 x = p[v];  // 8 bf16 -> 8 E4M3 codes = operand words 2v, 2v+1
+      qa[c][2 * v] = (int)(bf16_to_e4m3(x[0] & 0xffffu) | (bf16_to_e4m3(x[0] >> 16) << 8) |
+                           (bf16_to_e4m3(x[1] & 0xffffu) << 16) | (bf16_to_e4m3(x[1] >> 16) << 24));
+      qa[c][2 * v + 1] = (int)(bf16_to_e4m3(x[2] & 0xffffu) | (bf16_to_e4m3(x[2] >> 16) << 8) |
+                               (bf16_to_e4m3(x[3] & 0xffffu) << 16) | (bf16_to_e4m3(x[3] >> 16) << 24));
+    }
+  }
+}
+
+// this lane's B operands (key kn, the same dims as tile_query) from the tile
+__device__ __forceinline__ void tile_key(const uint8_t* tile, int kn, int half, bf16x8 (&kb)[8]) {
+  const uint8_t* row = tile + kn * TileKeys<KBf16>::LD + 16 * half;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) kb[c] = *reinterpret_cast<const bf16x8*>(row + 32 * c);
+}
+__device__ __forceinline__ void tile_key(const uint8_t* tile, int kn, int half, i32x8 (&kb)[2]) {
+  const uint8_t* row = tile + kn * TileKeys<KFp8>::LD + 32 * half;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(row + 64 * c);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + 64 * c + 16);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      kb[c][v] = (int)lo[v];
+      kb[c][4 + v] = (int)hi[v];
+    }
+  }
+}
+
+__device__ __forceinline__ f32x16 tile_mfma(const bf16x8 (&qa)[8], const bf16x8 (&kb)[8]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[c], kb[c], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ f32x16 tile_mfma(const i32x8 (&qa)[2], const i32x8 (&kb)[2]) {
+  f32x16 acc = {};
+  // format code 0 = FP8 E4M3 for both operands; the scale operands are unused
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[c], kb[c], acc, 0, 0, 0, 0, 0, 0);
+  return acc;
+}
+
+template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
 __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
+  using TK = TileKeys<KT>;
   constexpr int NT = NW * 64;
-  constexpr int NQ = NW * QW;                     // queries per block
-  constexpr int LPT = TS_TILE * DI * 2 / 16 / NT;  // 16-byte loads per thread per tile
-  static_assert(LPT >= 1 && LPT * NT * 16 == TS_TILE * DI * 2, "tile split");
-  __shared__ __align__(16) uint8_t kt[2][TS_TILE * TS_LD];
+  constexpr int NQ = NW * QW;                   // queries per block
+  constexpr int PIECES = TS_TILE * TK::ROWB / 16;  // 16-byte pieces per tile
+  constexpr int PPR = TK::ROWB / 16;            // pieces per row
+  constexpr int LPT = (PIECES + NT - 1) / NT;   // pieces per thread
+  __shared__ __align__(16) uint8_t kt[2][TS_TILE * TK::LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, kn = lane & 31;
   const int chunk = blockIdx.x;
   const int b = blockIdx.z;
   const int j0 = blockIdx.y * NQ + wave * QW;  // this wave's first query
-  const int64_t k0 = (int64_t)chunk * keys_per_chunk;
-  const int64_t k1 = min(a.n_cache, k0 + keys_per_chunk);
-  const int64_t nblk = (a.n_cache + BLK - 1) / BLK;
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + b * a.k_sb;
+  // key positions fit in 32 bits (the cache holds at most 2^27 latents)
+  const int k0 = (int)(chunk * keys_per_chunk);
+  const int k1 = (int)min(a.n_cache, (int64_t)k0 + keys_per_chunk);
+  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + b * a.k_sb * (TK::ROWB / DI);
 
-  // query operands and per-lane head weights
-  bf16x8 qa[QW][8];
+  // query operands, per-lane head weights and output rows
+  typename TK::QOp qa[QW];
   float wl[QW][16];
-  int64_t nv[QW], rows[QW];
+  int nv[QW];
+  int64_t rows[QW];
   bool qok[QW];
+  float* bm_row[QW];
 #pragma unroll
   for (int qi = 0; qi < QW; ++qi) {
     const int j = j0 + qi;
     qok[qi] = j < a.Tq;
     const int64_t r = (int64_t)b * a.Tq + (qok[qi] ? j : a.Tq - 1);
     rows[qi] = r;
-    const uint16_t* qr = a.q + r * (HI * DI) + kn * DI + 8 * half;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qa[qi][c] = *reinterpret_cast<const bf16x8*>(qr + 16 * c);
+    tile_query(a.q + r * (HI * DI), kn, half, qa[qi]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) wl[qi][i] = a.w[r * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
-    nv[qi] = qok[qi] ? n_visible(a.q_pos[r], a.n_cache) : 0;
+    nv[qi] = qok[qi] ? (int)n_visible(a.q_pos[r], a.n_cache) : 0;
+    bm_row[qi] = a.block_max ? a.block_max + r * a.bm_stride : nullptr;
   }
   // visible range of the whole block (queries are consecutive)
-  int64_t nv_blk;
+  int nv_blk;
   {
     const int jl = min(a.Tq - 1, (int)blockIdx.y * NQ + NQ - 1);
     const int jf = min(a.Tq - 1, (int)blockIdx.y * NQ);
-    nv_blk = max(n_visible(a.q_pos[(int64_t)b * a.Tq + jl], a.n_cache),
-                 n_visible(a.q_pos[(int64_t)b * a.Tq + jf], a.n_cache));
+    nv_blk = (int)max(n_visible(a.q_pos[(int64_t)b * a.Tq + jl], a.n_cache),
+                      n_visible(a.q_pos[(int64_t)b * a.Tq + jf], a.n_cache));
   }
-  // staging: load u of a tile -> (row (u NT + tid) / 16, 16-byte piece tid % 16)
-  const int spiece = tid & 15;
-  const int64_t kend = min(k1, max(k0, nv_blk));  // keys that need computing
-  auto load_tile = [&](int64_t t0, u32x4 (&v)[LPT]) {
+  // staging: piece u*NT + tid of a tile -> row / PPR, 16-byte piece % PPR
+  const int kend = min(k1, max(k0, nv_blk));  // keys that need computing
+  // rows past kend repeat row kend - 1: every query of the block masks them
+  // (p >= kend means p >= k1 or p >= every query's horizon)
+  auto load_tile = [&](int t0, u32x4 (&v)[LPT]) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
-      const int64_t row = t0 + (u * NT + tid) / 16;
-      v[u] = (u32x4){0u, 0u, 0u, 0u};
-      if (row < kend) v[u] = *reinterpret_cast<const u32x4*>(kb + row * DI + 8 * spiece);
+      const int pc = u * NT + tid;
+      const int row = min(t0 + pc / PPR, kend - 1);
+      if (pc < PIECES)
+        v[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)row * TK::ROWB + 16 * (pc % PPR));
     }
   };
-  auto compute = [&](int64_t t0, const uint8_t* tile) {
-    const int64_t p = t0 + kn;  // this lane's key
-    bf16x8 kbop[8];
+  auto store_tile = [&](uint8_t* tile, const u32x4 (&v)[LPT]) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      kbop[c] = *reinterpret_cast<const bf16x8*>(tile + kn * TS_LD + 32 * c + 16 * half);
+    for (int u = 0; u < LPT; ++u) {
+      const int pc = u * NT + tid;
+      if (pc < PIECES) *reinterpret_cast<u32x4*>(tile + (pc / PPR) * TK::LD + 16 * (pc % PPR)) = v[u];
+    }
+  };
+  struct Accs {
+    f32x16 v[QW];
+  };
+  // the MFMAs of all queries of the wave on one tile
+  auto mma = [&](const uint8_t* tile, Accs& A) {
+    typename TK::QOp kop;
+    tile_key(tile, kn, half, kop);
 #pragma unroll
-    for (int qi = 0; qi < QW; ++qi) {
-      if (!qok[qi]) continue;  // wave-uniform
-      float s = -INFINITY;
-      if (t0 < nv[qi]) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[qi][c], kbop[c], acc, 0, 0, 0);
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sum = fmaf(wl[qi][i], fmaxf(acc[i], 0.f), sum);
-        sum += __shfl_xor(sum, 32, 64);
-        s = p < nv[qi] ? sum : -INFINITY;
-      }
-      if (a.scores && half == 0 && p < k1) a.scores[rows[qi] * a.s_stride + p] = s;
+    for (int qi = 0; qi < QW; ++qi) A.v[qi] = tile_mfma(qa[qi], kop);
+  };
+  // the epilogue of one tile: ReLU . w . head sum, causal mask, block max
+  auto epi = [&](int t0, const Accs& A) {
+    const int p = t0 + kn;  // this lane's key
+    auto finish = [&](float s, int nv_l, bool ok_l, int64_t row_l, float* bm_l) {
+      s = p < nv_l ? s : -INFINITY;
+      if (a.scores && ok_l && p < k1) a.scores[row_l * a.s_stride + p] = s;
       if (a.block_max) {
         float m = s;
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
-        const int64_t blk = p >> 3;
-        if (half == 0 && (kn & 7) == 0 && blk < nblk && p < k1)
-          a.block_max[rows[qi] * a.bm_stride + blk] = m;
+        m = fmaxf(m, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(m))));   // quad_perm [1,0,3,2]
+        m = fmaxf(m, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(m))));   // quad_perm [2,3,0,1]
+        m = fmaxf(m, __uint_as_float(dpp_mov<0x141>(__float_as_uint(m))));  // row_half_mirror
+        if (ok_l && (kn & 7) == 0 && p < k1) bm_l[p >> 3] = m;
+      }
+    };
+    if constexpr (QW % 2 == 0) {
+      // queries in pairs: one lane swap leaves the full head sum of query
+      // qp in lanes 0-31 and of query qp+1 in lanes 32-63, so the mask,
+      // block max and stores run once for both
+#pragma unroll
+      for (int qp = 0; qp < QW; qp += 2) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s0 = fmaf(wl[qp][i], relu(A.v[qp][i]), s0);
+          s1 = fmaf(wl[qp + 1][i], relu(A.v[qp + 1][i]), s1);
+        }
+        // lanes 32-63 of s0 <-> lanes 0-31 of s1
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1),
+                                                         false, false);
+        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        finish(tot, half ? nv[qp + 1] : nv[qp], half ? qok[qp + 1] : qok[qp],
+               half ? rows[qp + 1] : rows[qp], half ? bm_row[qp + 1] : bm_row[qp]);
+      }
+    } else {
+#pragma unroll
+      for (int qi = 0; qi < QW; ++qi) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum = fmaf(wl[qi][i], relu(A.v[qi][i]), sum);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum),
+                                                         false, false);
+        sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // both halves' heads
+        finish(sum, nv[qi], qok[qi] && half == 0, rows[qi], bm_row[qi]);
       }
     }
   };
+  auto compute = [&](int t0, const uint8_t* tile) {
+    Accs A;
+    mma(tile, A);
+    epi(t0, A);
+  };
   // keys past every query's horizon: masked scores and block maxima only
-  auto masked = [&](int64_t t0) {
-    const int64_t p = t0 + kn;
+  auto masked = [&](int t0) {
+    const int p = t0 + kn;
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
       if (!qok[qi]) continue;
       if (a.scores && half == 0 && p < k1) a.scores[rows[qi] * a.s_stride + p] = -INFINITY;
-      const int64_t blk = p >> 3;
-      if (a.block_max && half == 0 && (kn & 7) == 0 && blk < nblk && p < k1)
-        a.block_max[rows[qi] * a.bm_stride + blk] = -INFINITY;
+      if (a.block_max && half == 0 && (kn & 7) == 0 && p < k1) bm_row[qi][p >> 3] = -INFINITY;
     }
   };
 
-  u32x4 stage[DEPTH][LPT];
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (k0 + d * TS_TILE < kend) load_tile(k0 + d * TS_TILE, stage[d]);
-  int buf = 0;
-  int64_t t0 = k0;
-  for (; t0 < kend; t0 += DEPTH * TS_TILE) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int64_t tt = t0 + d * TS_TILE;
-      if (tt < kend) {  // block-uniform
-#pragma unroll
-        for (int u = 0; u < LPT; ++u) {
-          const int row = (u * NT + tid) / 16;
-          *reinterpret_cast<u32x4*>(&kt[buf][row * TS_LD + 16 * spiece]) = stage[d][u];
+  if constexpr (PIPE) {
+    // software pipeline over tiles: the MFMAs of tile i+1 are issued before
+    // the epilogue of tile i, so the matrix core and the vector ALU of a wave
+    // work side by side; two tiles staged in registers (even / odd)
+    static_assert(DEPTH == 2, "pipelined loop stages tiles in pairs");
+    u32x4 stage[2][LPT];
+    if (k0 < kend) load_tile(k0, stage[0]);
+    if (k0 + TS_TILE < kend) load_tile(k0 + TS_TILE, stage[1]);
+    int buf = 0;
+    auto step = [&](int tt, u32x4 (&st)[LPT], Accs& A) {
+      store_tile(kt[buf], st);
+      __syncthreads();
+      if (tt + 2 * TS_TILE < kend) load_tile(tt + 2 * TS_TILE, st);
+      mma(kt[buf], A);
+      buf ^= 1;
+    };
+    Accs A0, A1;
+    int tt = k0;
+    if (tt < kend) {
+      step(tt, stage[0], A0);
+      for (;;) {  // block-uniform trip count
+        if (tt + TS_TILE >= kend) {
+          epi(tt, A0);
+          break;
         }
-        __syncthreads();
-        if (tt + DEPTH * TS_TILE < kend) load_tile(tt + DEPTH * TS_TILE, stage[d]);
-        compute(tt, kt[buf]);
-        buf ^= 1;
+        step(tt + TS_TILE, stage[1], A1);
+        epi(tt, A0);
+        tt += TS_TILE;
+        if (tt + TS_TILE >= kend) {
+          epi(tt, A1);
+          break;
+        }
+        step(tt + TS_TILE, stage[0], A0);
+        epi(tt, A1);
+        tt += TS_TILE;
+      }
+    }
+  } else {
+    // DEPTH tiles in flight: the loads of the tile DEPTH ahead are issued as
+    // soon as the current tile is in LDS
+    u32x4 stage[DEPTH][LPT];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (k0 + d * TS_TILE < kend) load_tile(k0 + d * TS_TILE, stage[d]);
+    int buf = 0;
+    int t0 = k0;
+    for (; t0 < kend; t0 += DEPTH * TS_TILE) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int tt = t0 + d * TS_TILE;
+        if (tt < kend) {  // block-uniform
+          store_tile(kt[buf], stage[d]);
+          __syncthreads();
+          if (tt + DEPTH * TS_TILE < kend) load_tile(tt + DEPTH * TS_TILE, stage[d]);
+          compute(tt, kt[buf]);
+          buf ^= 1;
+        }
       }
     }
   }
   // the tiles of the range that no query sees
-  for (int64_t tt = max(k0, (kend + TS_TILE - 1) / TS_TILE * TS_TILE); tt < k1; tt += TS_TILE)
+  for (int tt = max(k0, (kend + TS_TILE - 1) / TS_TILE * TS_TILE); tt < k1; tt += TS_TILE)
     masked(tt);
 }
 
@@ -341,14 +499,17 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
                              int64_t bm_stride, hipStream_t s) {
   ScanArgs a{(const uint16_t*)q, w, k, k_sb, n_cache, q_pos, Tq,
              scores, s_stride, block_max, bm_stride, 1};
-  if (!k_fp8 && Tq >= 64) {
+  if (Tq >= 64) {
     // many queries: MFMA-bound.  8 key ranges, tile-aligned (so block-aligned).
     constexpr int CH = 8;
     int64_t kpc = (n_cache + CH - 1) / CH;
     kpc = (kpc + TS_TILE - 1) / TS_TILE * TS_TILE;
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
     dim3 grid(nchunks, (unsigned)((Tq + 15) / 16), (unsigned)B);
-    hipLaunchKernelGGL((tile_scan_kernel<8, 2, 1>), grid, dim3(512), 0, s, a, kpc);
+    if (k_fp8)
+      hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KFp8>), grid, dim3(512), 0, s, a, kpc);
+    else
+      hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KBf16>), grid, dim3(512), 0, s, a, kpc);
     return hipGetLastError();
   }
   if (!k_fp8 && Tq >= 2) {
@@ -362,7 +523,7 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
     const int64_t kpc = (n_tiles32 + ch - 1) / ch * TS_TILE;
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
     dim3 grid(nchunks, (unsigned)groups, (unsigned)B);
-    hipLaunchKernelGGL((tile_scan_kernel<8, 1, 6>), grid, dim3(512), 0, s, a, kpc);
+    hipLaunchKernelGGL((tile_scan_kernel<8, 1, 6, false, KBf16>), grid, dim3(512), 0, s, a, kpc);
     return hipGetLastError();
   }
 

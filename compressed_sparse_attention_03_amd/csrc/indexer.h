@@ -163,6 +163,12 @@ __device__ __forceinline__ constexpr int64_t key_elem_bytes() {
   return std::is_same<KT, KFp8>::value ? 1 : 2;
 }
 
+// ReLU as an integer max on the fp32 bit pattern: every negative value
+// (sign bit set) is a negative int32 and becomes +0, every non-negative one
+// keeps its bits.  One v_max_i32, where fmaxf costs an extra canonicalising
+// v_max_f32 per input in IEEE mode.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ---- the fused contraction + epilogue -------------------------------------
 // Returns, in every lane, the score of key l%16 of the tile.
 __device__ __forceinline__ float tile_score(const QBf16& Q, const KBf16& K) {
@@ -175,8 +181,8 @@ __device__ __forceinline__ float tile_score(const QBf16& Q, const KBf16& K) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s = fmaf(Q.w[0][i], fmaxf(acc0[i], 0.f), s);
-    s = fmaf(Q.w[1][i], fmaxf(acc1[i], 0.f), s);
+    s = fmaf(Q.w[0][i], relu(acc0[i]), s);
+    s = fmaf(Q.w[1][i], relu(acc1[i]), s);
   }
   s += __shfl_xor(s, 16, 64);
   s += __shfl_xor(s, 32, 64);
@@ -191,8 +197,8 @@ __device__ __forceinline__ float tile_score(const QFp8& Q, const KFp8& K) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s = fmaf(Q.w[0][i], fmaxf(acc0[i], 0.f), s);
-    s = fmaf(Q.w[1][i], fmaxf(acc1[i], 0.f), s);
+    s = fmaf(Q.w[0][i], relu(acc0[i]), s);
+    s = fmaf(Q.w[1][i], relu(acc1[i]), s);
   }
   s += __shfl_xor(s, 16, 64);
   s += __shfl_xor(s, 32, 64);

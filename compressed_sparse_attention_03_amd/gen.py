@@ -102,7 +102,9 @@ def _configs():
         win_pos0=1048575 - 4 - 127, seed=5,
         desc="speculative verification at 1M: 8 sequences x 5 draft tokens at the end of "
              "1,048,576 raw tokens, bf16 caches")
-    return {c.name: c for c in (c1, c2, c3, c4, c5, c6)}
+    c7 = replace(c3, name="prefill_fp8", key_fmt="fp8", seed=6,
+                 desc="the chunked prefill with FP8 E4M3 index keys (integer-valued, exact)")
+    return {c.name: c for c in (c1, c2, c3, c4, c5, c6, c7)}
 
 
 CONFIGS = _configs()

@@ -67,6 +67,10 @@ def test_compress_stage_tiny():
     ("1m_verify", dict(B=2, Tq=2, N=4103, t_last=8205, K_b=64, win_pos0=8205 - 128, seed=66)),
     ("prefill", dict(B=2, Tq=64, N=4096, t_last=8191, K_b=32, K=64, comp_T=0,
                      shared_indexer=False, seed=41)),
+    # FP8 keys, many queries: the FP8 tile scan (v_mfma 32x32x64 on E4M3)
+    ("prefill_fp8", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=42)),
+    ("prefill_fp8", dict(B=2, Tq=70, N=3001, t_last=6001, K_b=32, K=64, comp_T=0,
+                         shared_indexer=False, seed=43)),
 ])
 def test_scan_cand_select_stages(name, kw):
     cfg = gen.shrink(gen.CONFIGS[name], **kw)
@@ -260,6 +264,11 @@ def test_full_128k():
 def test_full_prefill_sampled_queries():
     Tq = gen.CONFIGS["prefill"].Tq
     _full("prefill", seqs=[0], queries=[0, 1, 2, 127, 128, 1000, 4095, 4096, 6000, Tq - 2, Tq - 1])
+
+
+def test_full_prefill_fp8_sampled_queries():
+    Tq = gen.CONFIGS["prefill_fp8"].Tq
+    _full("prefill_fp8", seqs=[0], queries=[0, 5, 300, 4097, Tq - 1])
 
 
 def test_full_1m():
