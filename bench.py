@@ -112,7 +112,7 @@ def time_config(name, steps, warmup, torch, gen, api):
     cfg = gen.CONFIGS[name]
     log(f"[bench] {name}: generating inputs (B={cfg.B}, N={cfg.N}, seed={cfg.seed})")
     inp = gen.make_inputs(cfg, device="cuda")
-    path = api.DecodePath(cfg.B, cfg.Tq, cfg.N, cfg.K_b, cfg.K, cfg.W)
+    path = api.DecodePath(cfg.B, cfg.Tq, cfg.N, cfg.K_b, cfg.K, cfg.W, one_indexer=cfg.shared_indexer)
     comp = cfg.comp_T > 0
     torch.cuda.synchronize()
     for _ in range(warmup):

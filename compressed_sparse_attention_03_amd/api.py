@@ -152,6 +152,19 @@ def index_cand(q, w, k, q_pos, blocks, scores, ids, stream=None):
     return scores, ids
 
 
+def gather_scores(all_scores, q_pos, blocks, scores, ids, n_cache=None, stream=None):
+    """a4 from stored scores: the candidates' entries of the scan's score
+    matrix all_scores f32 [B*Tq][>=N] (same output as index_cand).  q_pos
+    int64 [B][Tq], blocks int32 [B*Tq][K_b]."""
+    B, Tq = q_pos.shape
+    K_b = blocks.shape[1]
+    N = all_scores.shape[1] if n_cache is None else n_cache
+    assert blocks.is_contiguous() and q_pos.is_contiguous() and all_scores.stride(1) == 1
+    check("csa2_gather_scores", lib().csa2_gather_scores(
+        B, Tq, _p(all_scores), all_scores.stride(0), N, _p(q_pos), _p(blocks), K_b, _p(scores),
+        _p(ids), scores.stride(0), _stream(stream)))
+    return scores, ids
+
 def select_topk(scores, k: int, out, ids=None, forced=None, force_last=False, ws=None,
                 stream=None):
     """a3 / a5: top-k ids per row (ascending, -1 padded).  ``ws``: scratch of
@@ -218,14 +231,22 @@ class DecodePath:
     The call order is the method's (NVFP4 article, section 3 call tree):
     [compressor] -> candidate-source scan + block max -> block top-K_b with
     the newest block kept -> current-layer indexer over the candidates ->
-    position top-K -> sparse attention over Sel + window with sinks."""
+    position top-K -> sparse attention over Sel + window with sinks.
+
+    one_indexer: the same indexer (q, w, k) serves both stages (the chunked
+    prefill); the scan then also keeps every score and the candidate stage
+    gathers them (csa2_gather_scores) instead of scoring again."""
 
     def __init__(self, B: int, Tq: int, N: int, K_b: int = 2048, K: int = 512, W: int = 128,
-                 device="cuda"):
+                 device="cuda", one_indexer: bool = False):
         self.B, self.Tq, self.N, self.K_b, self.K, self.W = B, Tq, N, K_b, K, W
         R = B * Tq
         nblk = (N + BLK - 1) // BLK
         dev = torch.device(device)
+        self.one_indexer = one_indexer
+        # row stride a multiple of 4 floats (16-byte rows for the gather)
+        self.all_scores = (torch.empty((R, (N + 3) // 4 * 4), dtype=torch.float32, device=dev)
+                           if one_indexer else None)
         self.block_max = torch.empty((R, nblk), dtype=torch.float32, device=dev)
         self.blocks = torch.empty((R, K_b), dtype=torch.int32, device=dev)
         self.cand_scores = torch.empty((R, K_b * BLK), dtype=torch.float32, device=dev)
@@ -258,13 +279,19 @@ class DecodePath:
                           stream=stream)
         mark(1)
         index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,
-                   stream=stream)
+                   scores=self.all_scores, stream=stream)
         mark(2)
         select_topk(self.block_max, self.K_b, self.blocks, force_last=True, ws=self.sel_ws,
                     stream=stream)
         mark(3)
-        index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], self.blocks, self.cand_scores,
-                   self.cand_ids, stream=stream)
+        if self.one_indexer:
+            if not (inp["qi"] is inp["qs"] and inp["wi"] is inp["ws"] and inp["ki"] is inp["ks"]):
+                raise ValueError("one_indexer path needs the same indexer for both stages")
+            gather_scores(self.all_scores, inp["q_pos"], self.blocks, self.cand_scores,
+                          self.cand_ids, n_cache=self.N, stream=stream)
+        else:
+            index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], self.blocks,
+                       self.cand_scores, self.cand_ids, stream=stream)
         mark(4)
         select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids, ws=self.sel_ws,
                     stream=stream)

@@ -194,6 +194,32 @@ int csa2_index_scores(int mode, int B, int Tq, const void* q, csa2_dtype q_dt, c
                                           K_b, scores, ids_out, s_stride, stream));
 }
 
+int csa2_gather_scores(int B, int Tq, const float* all, int64_t a_stride, int64_t n_cache,
+                       const int64_t* q_pos, const int32_t* cand_blocks, int K_b, float* scores,
+                       int32_t* ids_out, int64_t s_stride, hipStream_t stream) {
+  if (B < 0 || Tq < 0 || n_cache < 0) return CSA2_EINVAL;
+  if (n_cache > kMaxN * 8) return CSA2_EUNSUPPORTED;
+  const int64_t R = (int64_t)B * Tq;
+  if (R == 0) return CSA2_OK;
+  if (!q_pos || !cand_blocks || !scores || !ids_out || K_b < 1) return CSA2_EINVAL;
+  if (K_b > kMaxN / CSA2_BLOCK) return CSA2_EUNSUPPORTED;
+  if (R > 65535) return CSA2_EUNSUPPORTED;
+  if (s_stride < (int64_t)K_b * CSA2_BLOCK || s_stride % 4) return CSA2_EINVAL;
+  if (!aligned(scores, 16) || !aligned(ids_out, 16)) return CSA2_EINVAL;
+  if (n_cache > 0 && (!all || !aligned(all, 16) || a_stride < n_cache || a_stride % 4))
+    return CSA2_EINVAL;
+  const int64_t o_bytes = ((R - 1) * s_stride + (int64_t)K_b * CSA2_BLOCK) * 4;
+  if (overlap(scores, o_bytes, ids_out, o_bytes)) return CSA2_EINVAL;
+  if (n_cache > 0) {
+    const int64_t a_bytes = ((R - 1) * a_stride + n_cache) * 4;
+    if (overlap(scores, o_bytes, all, a_bytes) || overlap(ids_out, o_bytes, all, a_bytes))
+      return CSA2_EINVAL;
+  }
+  clear_stale_error();
+  return launched(csa2::launch_gather_cand(R, all, a_stride, n_cache, q_pos, cand_blocks, K_b,
+                                           scores, ids_out, s_stride, stream));
+}
+
 int csa2_select_topk(int R, int64_t n, const float* scores, int64_t s_stride, const int32_t* ids,
                      int64_t id_stride, const int32_t* forced, int force_last, int k, int32_t* out,
                      int64_t o_stride, void* ws, size_t ws_bytes, hipStream_t stream) {

@@ -107,4 +107,67 @@ hipError_t launch_index_cand(int B, int Tq, const void* q, const float* w, const
   return hipGetLastError();
 }
 
+
+// ---- candidates from stored scan scores --------------------------------------
+// With one indexer for both stages the candidates' scores are entries of the
+// scan's score matrix: one thread per candidate block copies its 8 scores
+// (two 16-byte loads, two 16-byte stores for scores and for ids), masking
+// latents past the query's horizon exactly as the candidate kernel does.
+// Consecutive threads take consecutive entries of the (ascending) block
+// list, so neighbouring reads often share cache lines.
+__global__ __launch_bounds__(256) void gather_cand_kernel(
+    const float* __restrict__ all, int64_t a_stride, int64_t n_cache,
+    const int64_t* __restrict__ q_pos, const int32_t* __restrict__ blocks, int K_b,
+    float* __restrict__ scores, int32_t* __restrict__ ids, int64_t s_stride) {
+  const int64_t r = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= K_b) return;
+  const int64_t nv = indexer::n_visible(q_pos[r], n_cache);
+  const int blk = blocks[r * K_b + j];
+  const int64_t p0 = (int64_t)blk * BLK;
+  float v[8];
+  int id[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v[i] = -INFINITY;
+    id[i] = -1;
+  }
+  if (blk >= 0 && p0 < nv) {
+    const float* src = all + r * a_stride + p0;
+    if (p0 + 8 <= nv) {
+      const f32x4 lo = reinterpret_cast<const f32x4*>(src)[0];
+      const f32x4 hi = reinterpret_cast<const f32x4*>(src)[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = lo[i];
+        v[4 + i] = hi[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) id[i] = (int)(p0 + i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (p0 + i < nv) {
+          v[i] = src[i];
+          id[i] = (int)(p0 + i);
+        }
+    }
+  }
+  f32x4* so = reinterpret_cast<f32x4*>(scores + r * s_stride + 8 * (int64_t)j);
+  u32x4* io = reinterpret_cast<u32x4*>(ids + r * s_stride + 8 * (int64_t)j);
+  so[0] = f32x4{v[0], v[1], v[2], v[3]};
+  so[1] = f32x4{v[4], v[5], v[6], v[7]};
+  io[0] = u32x4{(unsigned)id[0], (unsigned)id[1], (unsigned)id[2], (unsigned)id[3]};
+  io[1] = u32x4{(unsigned)id[4], (unsigned)id[5], (unsigned)id[6], (unsigned)id[7]};
+}
+
+hipError_t launch_gather_cand(int64_t R, const float* all, int64_t a_stride, int64_t n_cache,
+                              const int64_t* q_pos, const int32_t* blocks, int K_b, float* scores,
+                              int32_t* ids, int64_t s_stride, hipStream_t s) {
+  dim3 grid((unsigned)((K_b + 255) / 256), (unsigned)R);
+  hipLaunchKernelGGL(gather_cand_kernel, grid, dim3(256), 0, s, all, a_stride, n_cache, q_pos,
+                     blocks, K_b, scores, ids, s_stride);
+  return hipGetLastError();
+}
+
 }  // namespace csa2

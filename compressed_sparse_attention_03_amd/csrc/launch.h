@@ -32,6 +32,10 @@ hipError_t launch_index_cand(int B, int Tq, const void* q, const float* w, const
                              const int32_t* blocks, int K_b, float* scores, int32_t* ids,
                              int64_t s_stride, hipStream_t s);
 
+hipError_t launch_gather_cand(int64_t R, const float* all, int64_t a_stride, int64_t n_cache,
+                              const int64_t* q_pos, const int32_t* blocks, int K_b, float* scores,
+                              int32_t* ids, int64_t s_stride, hipStream_t s);
+
 size_t select_workspace_bytes(int64_t R, int64_t n, int64_t k);
 hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_stride,
                               const int32_t* ids, int64_t id_stride, const int32_t* forced,

@@ -201,6 +201,29 @@ int csa2_index_scores(int mode, int B, int Tq, const void *q, csa2_dtype q_dt,
                       int64_t bm_stride, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * a4 from stored scores ([NVFP4] section 3.3: the candidate-source indexer
+ * scores every position and the current layer's indexer re-scores the
+ * candidates; where one indexer serves both stages, as in the chunked
+ * prefill, the candidates' scores are entries of the scan's score matrix).
+ * Gathers them instead of recomputing; the output is exactly that of
+ * csa2_index_scores(CSA2_SCORES_CAND) for the same (q, w, k):
+ *   all        : f32 [B*Tq][a_stride >= n_cache], the SCAN scores; 16-byte
+ *                aligned, a_stride % 4 == 0
+ *   q_pos      : int64 [B][Tq];  cand_blocks, K_b : as for CAND
+ *   scores     : f32 [B*Tq][s_stride >= 8*K_b], column 8j+i = latent
+ *                8*cand_blocks[j]+i, -inf when the block id is -1 or the
+ *                latent is not visible (n_vis of the query's position)
+ *   ids_out    : int32, same shape, that latent's index or -1
+ *   scores and ids_out 16-byte aligned, s_stride % 4 == 0, no overlap.
+ * Precondition: block ids are -1 or < ceil(n_cache/8).
+ * ---------------------------------------------------------------------- */
+int csa2_gather_scores(int B, int Tq, const float *all, int64_t a_stride,
+                       int64_t n_cache, const int64_t *q_pos,
+                       const int32_t *cand_blocks, int K_b, float *scores,
+                       int32_t *ids_out, int64_t s_stride,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * a3 / a5. Top-k selection  ([NVFP4] section 3.3).
  *
  * Per row r < R over entries j < n: an entry is valid when its id is >= 0

@@ -67,7 +67,7 @@ def valid_sorted(a):
 
 def run_gpu_path(inp, compress_first=True):
     cfg = inp["cfg"]
-    path = api.DecodePath(cfg.B, cfg.Tq, cfg.N, cfg.K_b, cfg.K, cfg.W)
+    path = api.DecodePath(cfg.B, cfg.Tq, cfg.N, cfg.K_b, cfg.K, cfg.W, one_indexer=cfg.shared_indexer)
     path.run(inp, cfg.scale, compress_first=compress_first)
     torch.cuda.synchronize()
     return path

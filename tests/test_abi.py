@@ -212,3 +212,16 @@ def test_quant_nvfp4_validation(L):
     assert L.csa2_quant_nvfp4(A, _lib.F32, 4, 32, NULL, S, s) == _lib.EINVAL
     assert L.csa2_quant_nvfp4(MISALIGNED, _lib.F32, 4, 32, P, S, s) == _lib.EINVAL
     assert L.csa2_quant_nvfp4(A, _lib.F32, 4, 32, ctypes.c_void_p(0x100010), S, s) == _lib.EINVAL
+
+
+def test_gather_scores_validation(L):
+    s = None
+    A, Q, BL, S, I = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000))
+    assert L.csa2_gather_scores(0, 4, NULL, 0, 10, NULL, NULL, 1, NULL, NULL, 8, s) == _lib.OK
+    assert L.csa2_gather_scores(1, 1, A, 64, 64, Q, BL, 0, S, I, 8, s) == _lib.EINVAL      # K_b < 1
+    assert L.csa2_gather_scores(1, 1, A, 64, 64, Q, BL, 2, S, I, 8, s) == _lib.EINVAL      # s_stride < 16
+    assert L.csa2_gather_scores(1, 1, A, 62, 62, Q, BL, 2, S, I, 16, s) == _lib.EINVAL     # a_stride % 4
+    assert L.csa2_gather_scores(1, 1, A, 32, 64, Q, BL, 2, S, I, 16, s) == _lib.EINVAL     # a_stride < n
+    assert L.csa2_gather_scores(1, 1, A, 64, 64, Q, BL, 2, ctypes.c_void_p(0x400004), I, 16, s) == _lib.EINVAL
+    assert L.csa2_gather_scores(1, 1, A, 64, 64, Q, BL, 2, S, ctypes.c_void_p(0x400020), 16, s) == _lib.EINVAL
+    assert L.csa2_gather_scores(1, 1, A, 64, 64, Q, BL, 2, ctypes.c_void_p(0x100040), I, 16, s) == _lib.EINVAL

@@ -77,7 +77,8 @@ def test_scan_cand_select_stages(name, kw):
     inp = _inputs(cfg)
     host = np_subset(inp)
     R, nblk = cfg.R, cfg.nblk
-    scores = torch.empty((R, cfg.N), dtype=torch.float32, device="cuda")
+    # rows padded to a multiple of 4 floats, as the score gather needs
+    scores = torch.empty((R, (cfg.N + 3) // 4 * 4), dtype=torch.float32, device="cuda")[:, :cfg.N]
     bm = torch.empty((R, nblk), dtype=torch.float32, device="cuda")
     api.index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], scores=scores, block_max=bm)
     torch.cuda.synchronize()
@@ -102,6 +103,17 @@ def test_scan_cand_select_stages(name, kw):
     csc_ref, cid_ref = ref.cand(host["qi"], host["wi"], host["ki"], host["q_pos"], blk_ref)
     assert np.array_equal(cid.cpu().numpy(), cid_ref), "candidate ids"
     assert np.array_equal(csc.cpu().numpy().astype(np.float64), csc_ref), "candidate scores"
+
+    # the same candidates' entries gathered from the scan's own scores equal
+    # the candidate indexer run with the scan's (q, w, k)
+    gsc = torch.empty((R, cfg.K_b * 8), dtype=torch.float32, device="cuda")
+    gid = torch.empty((R, cfg.K_b * 8), dtype=torch.int32, device="cuda")
+    api.gather_scores(scores, inp["q_pos"], blocks, gsc, gid, n_cache=cfg.N)
+    torch.cuda.synchronize()
+    gsc_ref, gid_ref = (csc_ref, cid_ref) if cfg.shared_indexer else \
+        ref.cand(host["qs"], host["ws"], host["ks"], host["q_pos"], blk_ref)
+    assert np.array_equal(gid.cpu().numpy(), gid_ref), "gathered candidate ids"
+    assert np.array_equal(gsc.cpu().numpy().astype(np.float64), gsc_ref), "gathered candidate scores"
 
     sel = torch.empty((R, cfg.K), dtype=torch.int32, device="cuda")
     api.select_topk(csc, cfg.K, sel, ids=cid)
