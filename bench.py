@@ -4,14 +4,18 @@
 A step is one pass of the whole path over one batch: candidate-source
 indexer scan with the fused block max -> block top-2048 (newest block kept)
 -> current-layer indexer over the 16,384 candidates -> position top-512 ->
-sparse attention over the 512 latents + 128-token window with sinks.  The 1M
-workloads have no compressor step (their cache is given); the compressor is
-timed inside the prefill pass, which pools its 8192-token chunk.
+sparse attention over the 512 latents + 128-token window with sinks.  The
+bf16 1M workload has no compressor step (its cache is given); the
+compressor is timed in the low-precision 1M step (its decode step writes the
+newest NVFP4 latent), in the prefill pass (which pools its 8192-token chunk)
+and on its own over a whole 1M-token sequence.
 
 The headline workload is 1M-context decode: 8 sequences x 1,048,576 raw
 tokens (524,288 bf16 latents of 512, bf16 index keys), one query each.
 Inputs are seeded synthetic tensors already resident in HBM when the timed
-region starts.  Prints ONE JSON line (see the design doc for every field).
+region starts.  Prints ONE JSON line: the headline metric with its roofline
+(the scan kernel against the HBM peak), the CPU oracle's rate, and the
+secondary workloads under "extra".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                   [--only-main] [--calib]

@@ -27,7 +27,7 @@
  * host memory in the same logical layouts the device library uses; strides
  * are in elements, innermost dimension contiguous.
  *
- * Readings of points the pages leave open (each is listed in the design doc):
+ * Readings of points the pages leave open:
  *   - latent g pools raw tokens 2g and 2g+1; a query at raw position t sees
  *     latent g iff 2g+1 <= t, i.e. n_vis(t) = min(N, (t+1)/2);
  *   - block b holds latents [8b, 8b+8); its score is the max over its
