@@ -174,4 +174,22 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48): two register-to-register lane swaps (v_permlane16_swap pairs rows
+// 0/1 and 2/3, v_permlane32_swap the two halves), no LDS round trip.  Every
+// lane gets the result of its column.
+template <typename F>
+__device__ __forceinline__ float across_rows(float v, F op) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float v) {
+  return across_rows(v, [](float x, float y) { return x + y; });
+}
+__device__ __forceinline__ float max_across_rows(float v) {
+  return across_rows(v, [](float x, float y) { return fmaxf(x, y); });
+}
+
 }  // namespace csa2

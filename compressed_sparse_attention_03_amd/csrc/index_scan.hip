@@ -145,10 +145,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       }
       if (a.scores && g == 0 && p < a.n_cache) a.scores[r * a.s_stride + p] = s;
       if (a.block_max) {
-        float m = s;
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        const float m = max_of_8_lanes(s);
         const int64_t blk = p >> 3;
         if (g == 0 && (kl & 7) == 0 && blk < nblk) a.block_max[r * a.bm_stride + blk] = m;
       }
@@ -362,10 +359,7 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
       s = p < nv_l ? s : -INFINITY;
       if (a.scores && ok_l && p < k1) a.scores[row_l * a.s_stride + p] = s;
       if (a.block_max) {
-        float m = s;
-        m = fmaxf(m, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(m))));   // quad_perm [1,0,3,2]
-        m = fmaxf(m, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(m))));   // quad_perm [2,3,0,1]
-        m = fmaxf(m, __uint_as_float(dpp_mov<0x141>(__float_as_uint(m))));  // row_half_mirror
+        const float m = max_of_8_lanes(s);
         if (ok_l && (kn & 7) == 0 && p < k1) bm_l[p >> 3] = m;
       }
     };

@@ -169,6 +169,13 @@ __device__ __forceinline__ constexpr int64_t key_elem_bytes() {
 // v_max_f32 per input in IEEE mode.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Max over each group of 8 consecutive lanes, by DPP within the lanes' row.
+__device__ __forceinline__ float max_of_8_lanes(float m) {
+  m = fmaxf(m, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(m))));   // quad_perm [1,0,3,2]
+  m = fmaxf(m, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(m))));   // quad_perm [2,3,0,1]
+  return fmaxf(m, __uint_as_float(dpp_mov<0x141>(__float_as_uint(m))));  // row_half_mirror
+}
+
 // ---- the fused contraction + epilogue -------------------------------------
 // Returns, in every lane, the score of key l%16 of the tile.
 __device__ __forceinline__ float tile_score(const QBf16& Q, const KBf16& K) {
@@ -184,9 +191,7 @@ __device__ __forceinline__ float tile_score(const QBf16& Q, const KBf16& K) {
     s = fmaf(Q.w[0][i], relu(acc0[i]), s);
     s = fmaf(Q.w[1][i], relu(acc1[i]), s);
   }
-  s += __shfl_xor(s, 16, 64);
-  s += __shfl_xor(s, 32, 64);
-  return s;
+  return sum_across_rows(s);  // the four head groups of this key
 }
 
 __device__ __forceinline__ float tile_score(const QFp8& Q, const KFp8& K) {
@@ -200,9 +205,7 @@ __device__ __forceinline__ float tile_score(const QFp8& Q, const KFp8& K) {
     s = fmaf(Q.w[0][i], relu(acc0[i]), s);
     s = fmaf(Q.w[1][i], relu(acc1[i]), s);
   }
-  s += __shfl_xor(s, 16, 64);
-  s += __shfl_xor(s, 32, 64);
-  return s;
+  return sum_across_rows(s);  // the four head groups of this key
 }
 
 }  // namespace indexer

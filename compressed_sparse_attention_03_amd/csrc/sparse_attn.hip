@@ -307,8 +307,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
         lg[st][i] = sm.rvalid[row] ? s[st][i] * a.scale * rs[st][i] : -INFINITY;
         mt = fmaxf(mt, lg[st][i]);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max_across_rows(mt);
     // row validity does not depend on the head, and the 64 lanes together
     // hold all 32 rows: the ballot is the same answer for the whole wave
     bool mine = false;
@@ -364,8 +363,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   }
 
   // full row sum for this head (each lane group held a quarter of the rows)
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = sum_across_rows(l_run);
   const int h = 16 * wave + hl;
   if (a.splits > 1) {
     float* pp = a.part + ((r * a.splits + split) * HQ + h) * PART;
