@@ -58,6 +58,14 @@ double csa2ref_e2m1(uint8_t nibble) {
   return s ? -mag : mag;
 }
 
+/* OCP MX E8M0 scale: 2^(e-127) for e < 255; 0xFF is NaN.  The format of
+ * the per-32 scales of MXFP4 (the NVFP4 article's section 4 names MXFP4 as
+ * E2M1 values with one UE8M0 scale per 32 elements). */
+double csa2ref_e8m0(uint8_t bits) {
+  if (bits == 0xFF) return NAN;
+  return ldexp(1.0, (int)bits - 127);
+}
+
 /* Round a double to the nearest bfloat16 (8 significant bits, binary32
  * exponent range), ties to even, by scaling to the value's quantum and
  * rounding with nearbyint() under the default round-to-nearest-even mode. */
@@ -139,6 +147,15 @@ static void decode_key_row(const void *k, int k_fmt, int64_t row, double *dst) {
   if (k_fmt == CSA2REF_BF16) {
     const uint16_t *p = (const uint16_t *)k + row * CSA2REF_DI;
     for (int d = 0; d < CSA2REF_DI; ++d) dst[d] = csa2ref_bf16(p[d]);
+  } else if (k_fmt == CSA2REF_MXFP4) {
+    /* the oracle's packed row: 64 code bytes (dim 2i in the low nibble of
+     * byte i) then the 4 E8M0 scales of dims 0-31, 32-63, 64-95, 96-127 */
+    const uint8_t *p = (const uint8_t *)k + row * CSA2REF_MXFP4_ROW;
+    for (int d = 0; d < CSA2REF_DI; ++d) {
+      uint8_t byte = p[d / 2];
+      uint8_t nib = (d & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+      dst[d] = csa2ref_e2m1(nib) * csa2ref_e8m0(p[64 + d / 32]);
+    }
   } else {
     const uint8_t *p = (const uint8_t *)k + row * CSA2REF_DI;
     for (int d = 0; d < CSA2REF_DI; ++d) dst[d] = csa2ref_e4m3(p[d]);
@@ -178,7 +195,7 @@ void csa2ref_scan(int B, int Tq, const uint16_t *q, const float *w,
     const float *wr = w + (int64_t)r * CSA2REF_HI;
     const void *kb = (k_fmt == CSA2REF_BF16)
                          ? (const void *)((const uint16_t *)k + b * k_sb)
-                         : (const void *)((const uint8_t *)k + b * k_sb);
+                         : (const void *)((const uint8_t *)k + b * k_sb); /* bytes */
     decode_index_query(q + (int64_t)r * CSA2REF_HI * CSA2REF_DI, qd);
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < n_cache; ++p) {
@@ -275,7 +292,7 @@ void csa2ref_cand(int B, int Tq, const uint16_t *q, const float *w,
     int64_t nv = csa2ref_n_vis(q_pos[r], n_cache);
     const void *kb = (k_fmt == CSA2REF_BF16)
                          ? (const void *)((const uint16_t *)k + b * k_sb)
-                         : (const void *)((const uint8_t *)k + b * k_sb);
+                         : (const void *)((const uint8_t *)k + b * k_sb); /* bytes */
     decode_index_query(q + (int64_t)r * CSA2REF_HI * CSA2REF_DI, qd);
     for (int j = 0; j < K_b; ++j) {
       int32_t blk = blocks[(int64_t)r * K_b + j];

@@ -52,6 +52,8 @@ extern "C" {
 #define CSA2REF_E4M3 2  /* OCP FP8 E4M3FN bytes                            */
 #define CSA2REF_NVFP4 3 /* E2M1 nibbles + one E4M3 scale per 16 elements   */
 #define CSA2REF_F32 4
+#define CSA2REF_MXFP4 5 /* index keys: E2M1 codes + one E8M0 scale per 32  */
+#define CSA2REF_MXFP4_ROW 68 /* oracle key row: 64 code bytes, 4 scales  */
 
 #define CSA2REF_D 512   /* latent width (one shared KV head)               */
 #define CSA2REF_HQ 64   /* query heads                                     */
@@ -63,6 +65,7 @@ extern "C" {
 double csa2ref_bf16(uint16_t bits);
 double csa2ref_e4m3(uint8_t bits);   /* NaN for S.1111.111                */
 double csa2ref_e2m1(uint8_t nibble); /* low 4 bits used                   */
+double csa2ref_e8m0(uint8_t bits);   /* 2^(bits-127); NaN for 0xFF        */
 uint16_t csa2ref_round_bf16(double x); /* round-to-nearest-even to bf16   */
 
 /* ---- visibility helpers -------------------------------------------- */
@@ -83,6 +86,9 @@ void csa2ref_compress(int B, int T, const uint16_t *kv, int64_t kv_sb,
  * k_fmt (BF16 or E4M3), batch stride k_sb elements; q_pos: [B][Tq].
  * scores (optional): [B*Tq][s_stride], -inf for invisible positions.
  * block_max (optional): [B*Tq][bm_stride], -inf for invisible blocks.     */
+/* Index keys k: [B][N][128] in k_fmt (CSA2REF_BF16, CSA2REF_E4M3 or
+ * CSA2REF_MXFP4 as packed 68-byte rows), batch stride k_sb elements (bytes
+ * for the byte formats). */
 void csa2ref_scan(int B, int Tq, const uint16_t *q, const float *w,
                   const void *k, int k_fmt, int64_t k_sb, int64_t n_cache,
                   const int64_t *q_pos, double *scores, int64_t s_stride,

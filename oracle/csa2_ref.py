@@ -22,7 +22,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libcsa2ref.so")
 
-BF16, E4M3, NVFP4, F32 = 1, 2, 3, 4
+BF16, E4M3, NVFP4, F32, MXFP4 = 1, 2, 3, 4, 5
+MXFP4_ROW = 68
 D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
 _FMT = {"bf16": BF16, "fp8": E4M3, "nvfp4": NVFP4, "f32": F32}
 
@@ -43,6 +44,8 @@ def lib():
         L.csa2ref_e4m3.argtypes = [ctypes.c_uint8]
         L.csa2ref_e2m1.restype = D_
         L.csa2ref_e2m1.argtypes = [ctypes.c_uint8]
+        L.csa2ref_e8m0.restype = D_
+        L.csa2ref_e8m0.argtypes = [ctypes.c_uint8]
         L.csa2ref_round_bf16.restype = ctypes.c_uint16
         L.csa2ref_round_bf16.argtypes = [D_]
         L.csa2ref_n_vis.restype = I64
@@ -86,8 +89,18 @@ def _c(a, dtype):
     return a
 
 
-def _key_fmt(k):
-    return BF16 if k.dtype == np.uint16 else E4M3
+def _keys(k):
+    """Index keys as (array, format, batch stride): uint16 bf16 or uint8 E4M3
+    [B][N][128], or an MXFP4 pair (codes uint8 [B][N][64], E8M0 scales uint8
+    [B][N][4]) packed into the oracle's 68-byte rows."""
+    if isinstance(k, tuple):
+        codes, scales = np.ascontiguousarray(k[0], np.uint8), np.ascontiguousarray(k[1], np.uint8)
+        B, N = codes.shape[:2]
+        assert codes.shape == (B, N, DI // 2) and scales.shape == (B, N, DI // 32)
+        packed = np.ascontiguousarray(np.concatenate([codes, scales], axis=2))
+        return packed, MXFP4, N * MXFP4_ROW
+    k = np.ascontiguousarray(k)
+    return k, (BF16 if k.dtype == np.uint16 else E4M3), k.shape[1] * DI
 
 
 # ---------------------------------------------------------------- decoders
@@ -97,6 +110,10 @@ def bf16(bits) -> float:
 
 def e4m3(bits) -> float:
     return lib().csa2ref_e4m3(int(bits))
+
+
+def e8m0(bits) -> float:
+    return lib().csa2ref_e8m0(int(bits))
 
 
 def e2m1(nibble) -> float:
@@ -142,15 +159,15 @@ def scan(q, w, k, q_pos, want_scores=False):
     uint8 E4M3); q_pos int64 [B][Tq].  Returns (scores [B*Tq][N] or None,
     block_max [B*Tq][ceil(N/8)]), float64 with -inf where invisible."""
     q, w, q_pos = _c(q, np.uint16), _c(w, np.float32), _c(q_pos, np.int64)
-    k = np.ascontiguousarray(k)
+    k, k_fmt, k_sb = _keys(k)
     B, Tq = q.shape[:2]
     N = k.shape[1]
     assert q.shape == (B, Tq, HI, DI) and w.shape == (B, Tq, HI) and q_pos.shape == (B, Tq)
-    assert k.shape == (B, N, DI)
+    assert k.shape[:2] == (B, N)
     nblk = (N + BLK - 1) // BLK
     sc = np.zeros((B * Tq, N), np.float64) if want_scores else None
     bm = np.zeros((B * Tq, nblk), np.float64)
-    lib().csa2ref_scan(B, Tq, _p(q), _p(w), _p(k), _key_fmt(k), N * DI, N, _p(q_pos),
+    lib().csa2ref_scan(B, Tq, _p(q), _p(w), _p(k), k_fmt, k_sb, N, _p(q_pos),
                        _p(sc), N, _p(bm), nblk)
     return sc, bm
 
@@ -172,15 +189,15 @@ def cand(q, w, k, q_pos, blocks):
     blocks int32 [B*Tq][K_b]; returns (scores float64 [B*Tq][8*K_b],
     ids int32 [B*Tq][8*K_b]) with id -1 / score -inf for absent latents."""
     q, w, q_pos, blocks = _c(q, np.uint16), _c(w, np.float32), _c(q_pos, np.int64), _c(blocks, np.int32)
-    k = np.ascontiguousarray(k)
+    k, k_fmt, k_sb = _keys(k)
     B, Tq = q.shape[:2]
     N = k.shape[1]
     K_b = blocks.shape[1]
     assert q.shape == (B, Tq, HI, DI) and w.shape == (B, Tq, HI) and q_pos.shape == (B, Tq)
-    assert k.shape == (B, N, DI) and blocks.shape == (B * Tq, K_b)
+    assert k.shape[:2] == (B, N) and blocks.shape == (B * Tq, K_b)
     sc = np.zeros((B * Tq, K_b * BLK), np.float64)
     ids = np.zeros((B * Tq, K_b * BLK), np.int32)
-    lib().csa2ref_cand(B, Tq, _p(q), _p(w), _p(k), _key_fmt(k), N * DI, N, _p(q_pos),
+    lib().csa2ref_cand(B, Tq, _p(q), _p(w), _p(k), k_fmt, k_sb, N, _p(q_pos),
                        _p(blocks), K_b, _p(sc), _p(ids), K_b * BLK)
     return sc, ids
 
@@ -344,10 +361,12 @@ def decode(inp: dict, K_b: int, K: int, W: int, scale: float, compress_first=Fal
     q_pos = inp["q_pos"]
     B, Tq = q_pos.shape
     N = lat.shape[1]
-    _, bm = scan(inp["qs"], inp["ws"], inp["ks"], q_pos)
+    ks = (inp["ks"], inp["ks_scale"]) if inp.get("ks_scale") is not None else inp["ks"]
+    ki = (inp["ki"], inp["ki_scale"]) if inp.get("ki_scale") is not None else inp["ki"]
+    _, bm = scan(inp["qs"], inp["ws"], ks, q_pos)
     forced = np.array([newest_block(t, N) for t in q_pos.reshape(-1)], np.int32)
     blocks = select(bm, K_b, forced=forced)
-    csc, cid = cand(inp["qi"], inp["wi"], inp["ki"], q_pos, blocks)
+    csc, cid = cand(inp["qi"], inp["wi"], ki, q_pos, blocks)
     sel = select(csc, K, ids=cid)
     out, lse = attn(inp["q"], lat, sel, inp["win"], q_pos, inp["sink"], W, scale,
                     lat_scale=lat_scale, win_scale=inp.get("win_scale"))

@@ -122,6 +122,36 @@ def test_scan_cand_select_stages(name, kw):
     say(f"  blocks, candidates and Sel bit-exact ({(sel_ref >= 0).sum(1).tolist()[:4]} selected)")
 
 
+def test_gather_edge_cases():
+    """Candidate gather from stored scores on the cases the selection rarely
+    produces: block ids of -1, blocks partly or wholly past a query's horizon
+    (t = 0, 1, 2, 17), a cache whose last block is partial (N = 1003), and the
+    matrix read from an oracle scan.  Expected: the oracle's candidate indexer
+    over the same blocks."""
+    cfg = gen.shrink(gen.CONFIGS["tiny"], B=2, Tq=4, N=1003, t_last=2005, K_b=40, seed=90)
+    inp = _inputs(cfg)
+    host = np_subset(inp)
+    q_pos = np.array([[0, 1, 2, 17], [2000, 2003, 2004, 2005]], np.int64)
+    sc_ref, _ = ref.scan(host["qs"], host["ws"], host["ks"], q_pos, want_scores=True)
+    rng = np.random.default_rng(91)
+    nblk = cfg.nblk
+    blocks = np.sort(rng.choice(nblk, (cfg.R, cfg.K_b), replace=True), axis=1).astype(np.int32)
+    blocks[:, -1] = nblk - 1            # the partial last block
+    blocks[:, ::7] = -1                 # absent entries
+    N4 = (cfg.N + 3) // 4 * 4
+    all_s = np.full((cfg.R, N4), np.nan, np.float32)  # padding is never read
+    all_s[:, :cfg.N] = sc_ref
+    out = torch.empty((cfg.R, cfg.K_b * 8), dtype=torch.float32, device="cuda")
+    ids = torch.empty((cfg.R, cfg.K_b * 8), dtype=torch.int32, device="cuda")
+    api.gather_scores(torch.from_numpy(all_s).cuda(), torch.from_numpy(q_pos).cuda(),
+                      torch.from_numpy(blocks).cuda(), out, ids, n_cache=cfg.N)
+    torch.cuda.synchronize()
+    want_s, want_id = ref.cand(host["qs"], host["ws"], host["ks"], q_pos, blocks)
+    assert np.array_equal(ids.cpu().numpy(), want_id)
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), want_s)
+    say(f"  gather: {(want_id >= 0).sum()} present, {(want_id < 0).sum()} absent entries exact")
+
+
 @pytest.mark.parametrize("seed,R,n,k,mode", [
     (40, 5, 300, 17, "ties"), (41, 3, 65536, 2048, "last"), (42, 7, 16384, 512, "ids"),
     (43, 4, 1000, 1200, "plain"), (44, 6, 5000, 64, "forced"), (45, 2, 777, 1, "forced"),
