@@ -36,6 +36,7 @@ METRIC = "CSA2 decode queries/s (64 heads) at 1M ctx; % HBM peak; prefill indexe
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E peak
 MFMA_BF16_PEAK_TFS = 2500.0
 MFMA_FP8_PEAK_TFS = 5000.0  # MI355X dense fp8 MFMA peak
+MFMA_FP4_PEAK_TFS = 10100.0  # MI355X dense fp4 MFMA peak
 D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
 
 
@@ -394,6 +395,18 @@ def main():
             "stages_us_eager": {k: round(v * 1e3, 2) for k, v in fst.items()},
         }
         del finp
+        torch.cuda.empty_cache()
+        xcfg, xinp, xpath, xms, xst = time_config("prefill_mxfp4", 2, 1, torch, gen, api)
+        del xpath
+        xtfs = prefill_indexer_flops(xcfg) / (xst["index_scan"] * 1e-3) / 1e12
+        extra["prefill_mxfp4"] = {
+            "workload": "the same chunked prefill with MXFP4 index keys (FP4 MFMA indexer)",
+            "indexer_TFLOPs": round(xtfs, 2), "indexer_mfma_frac_fp4": round(xtfs / MFMA_FP4_PEAK_TFS, 4),
+            "indexer_mfma_frac_of_bf16_peak": round(xtfs / MFMA_BF16_PEAK_TFS, 4),
+            "tokens_per_s": round(xcfg.R / (xms * 1e-3), 1), "ms_per_step": round(xms, 3),
+            "stages_us_eager": {k: round(v * 1e3, 2) for k, v in xst.items()},
+        }
+        del xinp
         torch.cuda.empty_cache()
         inp = gen.make_inputs(cfg, device="cuda") if not args.no_cpu_baseline else None
     result["extra"] = extra

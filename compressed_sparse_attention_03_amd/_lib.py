@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
 # csa2_dtype
-BF16, FP8_E4M3, NVFP4, F32 = 1, 2, 3, 4
+BF16, FP8_E4M3, NVFP4, F32, MXFP4 = 1, 2, 3, 4, 5
 # csa2_status
 OK, EINVAL, EUNSUPPORTED, ELAUNCH, EWORKSPACE = 0, -1, -2, -3, -4
 SCORES_SCAN, SCORES_CAND = 0, 1
@@ -50,7 +50,7 @@ def lib():
         "csa2_status_string": (ctypes.c_char_p, [I]),
         "csa2_version": (I, []),
         "csa2_compress": (I, [I, I, P, I64, P, I64, P, I64, P]),
-        "csa2_index_scores": (I, [I, I, I, P, I, P, P, I, I64, I64, P, P, I, P, I64, P, P, I64, P]),
+        "csa2_index_scores": (I, [I, I, I, P, I, P, P, I, P, I64, I64, P, P, I, P, I64, P, P, I64, P]),
         "csa2_select_topk": (I, [I, I64, P, I64, P, I64, P, I, I, P, I64, P, SZ, P]),
         "csa2_sparse_attn": (I, [I, I, P, I64, P, I, P, I64, I64, P, I, I64, P, I, P, I, I, I64,
                                  P, P, F, P, I64, P, P, SZ, P]),

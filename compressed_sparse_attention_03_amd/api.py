@@ -12,7 +12,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import BF16, F32, FP8_E4M3, NVFP4, SCORES_CAND, SCORES_SCAN, check, lib
+from ._lib import BF16, F32, FP8_E4M3, MXFP4, NVFP4, SCORES_CAND, SCORES_SCAN, check, lib
 
 D, HQ, HI, DI, BLK = 512, 64, 32, 128, 8
 
@@ -123,17 +123,26 @@ def quant_nvfp4(src: torch.Tensor, packed=None, scales=None, stream=None):
     return packed, scales
 
 
-def index_scan(q, w, k, q_pos, scores=None, block_max=None, stream=None):
+def index_scan(q, w, k, q_pos, scores=None, block_max=None, k_scale=None, stream=None):
     """a2: indexer scores of every latent and/or per-block maxima.
 
     q bf16 [B][Tq][32][128], w f32 [B][Tq][32], k [B][N][128] (bf16 or E4M3
-    bytes), q_pos int64 [B][Tq]; scores f32 [B*Tq][>=N], block_max f32
+    bytes) or, with k_scale (E8M0 bytes [B][N][4]), MXFP4 codes [B][N][64];
+    q_pos int64 [B][Tq]; scores f32 [B*Tq][>=N], block_max f32
     [B*Tq][>=ceil(N/8)]."""
     B, Tq = q.shape[:2]
     N = k.shape[1]
     assert q.is_contiguous() and w.is_contiguous() and q_pos.is_contiguous()
+    if k_scale is not None:
+        if k.dtype != torch.uint8 or k.shape[2] != DI // 2 or tuple(k_scale.shape) != (B, N, DI // 32) \
+                or not k_scale.is_contiguous() or k.stride(0) != 16 * k_scale.stride(0):
+            raise ValueError("index_scan: MXFP4 keys are uint8 codes [B][N][64] with E8M0 "
+                             "scales [B][N][4], scale batch stride = code batch stride / 16")
+        k_dt = MXFP4
+    else:
+        k_dt = _key_dtype(k)
     check("csa2_index_scores", lib().csa2_index_scores(
-        SCORES_SCAN, B, Tq, _p(q), BF16, _p(w), _p(k), _key_dtype(k), _rows_contig(k, DI, "k"), N,
+        SCORES_SCAN, B, Tq, _p(q), BF16, _p(w), _p(k), k_dt, _p(k_scale), _rows_contig(k, DI, "k"), N,
         _p(q_pos), None, 0, _p(scores), scores.stride(0) if scores is not None else 0, None,
         _p(block_max), block_max.stride(0) if block_max is not None else 0, _stream(stream)))
     return scores, block_max
@@ -147,7 +156,7 @@ def index_cand(q, w, k, q_pos, blocks, scores, ids, stream=None):
     assert q.is_contiguous() and w.is_contiguous() and q_pos.is_contiguous() and blocks.is_contiguous()
     assert scores.stride(0) == ids.stride(0)
     check("csa2_index_scores", lib().csa2_index_scores(
-        SCORES_CAND, B, Tq, _p(q), BF16, _p(w), _p(k), _key_dtype(k), _rows_contig(k, DI, "k"), N,
+        SCORES_CAND, B, Tq, _p(q), BF16, _p(w), _p(k), _key_dtype(k), None, _rows_contig(k, DI, "k"), N,
         _p(q_pos), _p(blocks), K_b, _p(scores), scores.stride(0), _p(ids), None, 0, _stream(stream)))
     return scores, ids
 
@@ -279,7 +288,7 @@ class DecodePath:
                           stream=stream)
         mark(1)
         index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,
-                   scores=self.all_scores, stream=stream)
+                   scores=self.all_scores, k_scale=inp.get("ks_scale"), stream=stream)
         mark(2)
         select_topk(self.block_max, self.K_b, self.blocks, force_last=True, ws=self.sel_ws,
                     stream=stream)

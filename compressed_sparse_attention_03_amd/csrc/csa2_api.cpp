@@ -154,23 +154,29 @@ int csa2_quant_nvfp4(const void* src, csa2_dtype src_dt, int64_t rows, int cols,
 }
 
 int csa2_index_scores(int mode, int B, int Tq, const void* q, csa2_dtype q_dt, const float* w,
-                      const void* k, csa2_dtype k_dt, int64_t k_sb, int64_t n_cache,
-                      const int64_t* q_pos, const int32_t* cand_blocks, int K_b, float* scores,
-                      int64_t s_stride, int32_t* ids_out, float* block_max, int64_t bm_stride,
-                      hipStream_t stream) {
+                      const void* k, csa2_dtype k_dt, const uint8_t* k_scale, int64_t k_sb,
+                      int64_t n_cache, const int64_t* q_pos, const int32_t* cand_blocks, int K_b,
+                      float* scores, int64_t s_stride, int32_t* ids_out, float* block_max,
+                      int64_t bm_stride, hipStream_t stream) {
   if (mode != CSA2_SCORES_SCAN && mode != CSA2_SCORES_CAND) return CSA2_EINVAL;
   if (B < 0 || Tq < 0 || n_cache < 0) return CSA2_EINVAL;
   if (q_dt != CSA2_BF16) return CSA2_EUNSUPPORTED;
-  if (k_dt != CSA2_BF16 && k_dt != CSA2_FP8_E4M3) return CSA2_EUNSUPPORTED;
+  if (k_dt != CSA2_BF16 && k_dt != CSA2_FP8_E4M3 && k_dt != CSA2_MXFP4) return CSA2_EUNSUPPORTED;
+  // MXFP4 keys: the many-query scan (prefill) only
+  if (k_dt == CSA2_MXFP4 && (mode != CSA2_SCORES_SCAN || Tq < 64)) return CSA2_EUNSUPPORTED;
   if (n_cache > kMaxN * 8) return CSA2_EUNSUPPORTED;
   const int64_t R = (int64_t)B * Tq;
   if (R == 0) return CSA2_OK;
   if (!q || !w || !q_pos) return CSA2_EINVAL;
   if (!aligned(q, 16) || !aligned(w, 4)) return CSA2_EINVAL;
-  const bool fp8 = k_dt == CSA2_FP8_E4M3;
+  const bool fp8 = k_dt == CSA2_FP8_E4M3, mx = k_dt == CSA2_MXFP4;
+  // key row bytes: bf16 256, FP8 128, MXFP4 64 codes (+ 4 scale bytes apart)
+  const int64_t row_units = mx ? CSA2_DI / 2 : CSA2_DI;
   if (n_cache > 0) {
     if (!k || !aligned(k, 16)) return CSA2_EINVAL;
-    if (k_sb < 0 || (B > 1 && k_sb < n_cache * CSA2_DI) || (k_sb % (fp8 ? 16 : 8))) return CSA2_EINVAL;
+    if (k_sb < 0 || (B > 1 && k_sb < n_cache * row_units) || (k_sb % (fp8 || mx ? 16 : 8)))
+      return CSA2_EINVAL;
+    if (mx && (!k_scale || !aligned(k_scale, 4))) return CSA2_EINVAL;
   }
   if (mode == CSA2_SCORES_SCAN) {
     if (!scores && !block_max) return CSA2_EINVAL;
@@ -180,8 +186,9 @@ int csa2_index_scores(int mode, int B, int Tq, const void* q, csa2_dtype q_dt, c
     if (B > 65535 || (Tq + 3) / 4 > 65535) return CSA2_EUNSUPPORTED;
     if (n_cache == 0) return CSA2_OK;
     clear_stale_error();
-    return launched(csa2::launch_index_scan(B, Tq, q, w, k, fp8, k_sb, n_cache, q_pos, scores,
-                                            s_stride, block_max, bm_stride, stream));
+    const int fmt = mx ? csa2::KEYS_MXFP4 : (fp8 ? csa2::KEYS_FP8 : csa2::KEYS_BF16);
+    return launched(csa2::launch_index_scan(B, Tq, q, w, k, fmt, k_scale, k_sb, n_cache, q_pos,
+                                            scores, s_stride, block_max, bm_stride, stream));
   }
   if (!cand_blocks || !scores || !ids_out || K_b < 1) return CSA2_EINVAL;
   if (K_b > kMaxN / CSA2_BLOCK) return CSA2_EUNSUPPORTED;

@@ -28,6 +28,7 @@ struct ScanArgs {
   float* block_max;
   int64_t bm_stride;
   int tiles_per_wave;
+  const uint8_t* k_scale;  // MXFP4 keys: E8M0 scales [B][N][4], batch stride k_sb / 16
 };
 
 // ---- scan: every latent, block max fused ------------------------------------
@@ -200,23 +201,37 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 // query, 6 tiles in flight, enough key ranges to fill the chip.
 constexpr int TS_TILE = 32;  // keys per tile
 
+// MXFP4 index keys: E2M1 codes (dim 2i in the low nibble of byte i) and one
+// E8M0 scale per 32 dims.  v_mfma_scale_f32_32x32x64_f8f6f4 with both
+// operands in FP4: lane (row / column l % 32, half h) holds 32 values of
+// one K-block of 32 and supplies that block's scale byte, so each lane's 32
+// dims are exactly one MX block of its key (and of the query, whose scale is
+// 1: the bf16 query is rounded to E2M1 once, exact for the small integers
+// index queries take).
+struct KMx4 {};
+
 template <typename KT>
 struct TileKeys;
 template <>
 struct TileKeys<KBf16> {
   static constexpr int ROWB = DI * 2;      // bytes per key row
+  static constexpr int ESZ = 2;            // bytes per unit of the batch stride
   static constexpr int LD = ROWB + 16;     // LDS pitch (padded)
-  static constexpr int NK = 8;             // MFMAs per query and tile
-  typedef bf16x8 Op;                       // one MFMA operand
-  typedef bf16x8 QOp[8];
+  typedef bf16x8 QOp[8];                   // a query's A operands (one per MFMA)
 };
 template <>
 struct TileKeys<KFp8> {
   static constexpr int ROWB = DI;
+  static constexpr int ESZ = 1;
   static constexpr int LD = ROWB + 16;
-  static constexpr int NK = 2;
-  typedef i32x8 Op;
   typedef i32x8 QOp[2];
+};
+template <>
+struct TileKeys<KMx4> {
+  static constexpr int ROWB = DI / 2;
+  static constexpr int ESZ = 1;
+  static constexpr int LD = ROWB + 16;
+  typedef i32x8 QOp[2];  // 4 of the 8 registers carry the 32 E2M1 codes
 };
 
 // this lane's A operands of query row r (32 heads x 128 dims)
@@ -261,6 +276,61 @@ __device__ __forceinline__ void tile_key(const uint8_t* tile, int kn, int half, 
   }
 }
 
+// bf16 -> E2M1 code, nearest with ties to the even code, saturating at +-6
+// (midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; ties at 0.75, 1.75 and 3.5
+// round up, the others down), sign from x < 0
+__device__ __forceinline__ uint32_t bf16_to_e2m1(uint32_t h) {
+  const float x = bf16_to_f32(h), a = fabsf(x);
+  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+  return mag | (x < 0.0f ? 8u : 0u);
+}
+
+// this lane's A operands for MXFP4 keys: dims 32(2c+h) .. +31 as E2M1 codes
+__device__ __forceinline__ void tile_query_mx(const uint16_t* q, int kn, int half, i32x8 (&qa)[2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(q + kn * DI + 32 * (2 * c + half));
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const u32x4 x = p[v];  // 8 bf16 -> 8 codes = one operand word
+      uint32_t wd = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wd |= (bf16_to_e2m1(x[i] & 0xffffu) | (bf16_to_e2m1(x[i] >> 16) << 4)) << (8 * i);
+      qa[c][v] = (int)wd;
+      qa[c][4 + v] = 0;
+    }
+  }
+}
+
+// this lane's B operands and scale bytes for MXFP4 keys (key kn)
+__device__ __forceinline__ void tile_key_mx(const uint8_t* tile, const uint32_t* scales, int kn,
+                                            int half, i32x8 (&kb)[2], int (&ks)[2]) {
+  const uint32_t sc = scales[kn];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + kn * TileKeys<KMx4>::LD + 16 * (2 * c + half));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kb[c][i] = (int)v[i];
+      kb[c][4 + i] = 0;
+    }
+    ks[c] = (int)((sc >> (8 * (2 * c + half))) & 0xffu);
+  }
+}
+
+__device__ __forceinline__ f32x16 tile_mfma_mx(const i32x8 (&qa)[2], const i32x8 (&kb)[2],
+                                               const int (&ks)[2]) {
+  f32x16 acc = {};
+  // format code 4 = FP4 E2M1 for both operands; the query's scale is 2^0
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[c], kb[c], acc, 4, 4, 0, 127, 0, ks[c]);
+  return acc;
+}
+
 __device__ __forceinline__ f32x16 tile_mfma(const bf16x8 (&qa)[8], const bf16x8 (&kb)[8]) {
   f32x16 acc = {};
 #pragma unroll
@@ -279,12 +349,17 @@ __device__ __forceinline__ f32x16 tile_mfma(const i32x8 (&qa)[2], const i32x8 (&
 template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
 __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
   using TK = TileKeys<KT>;
+  constexpr bool MX = std::is_same<KT, KMx4>::value;
   constexpr int NT = NW * 64;
   constexpr int NQ = NW * QW;                   // queries per block
   constexpr int PIECES = TS_TILE * TK::ROWB / 16;  // 16-byte pieces per tile
   constexpr int PPR = TK::ROWB / 16;            // pieces per row
   constexpr int LPT = (PIECES + NT - 1) / NT;   // pieces per thread
+  // MXFP4: the tile's 32 scale words are loaded by the threads after the
+  // code pieces (one 4-byte word per key)
+  static_assert(!MX || (LPT == 1 && PIECES + TS_TILE <= NT), "scale loaders");
   __shared__ __align__(16) uint8_t kt[2][TS_TILE * TK::LD];
+  __shared__ uint32_t kts[MX ? 2 : 1][MX ? TS_TILE : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, kn = lane & 31;
   const int chunk = blockIdx.x;
@@ -293,7 +368,8 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
   // key positions fit in 32 bits (the cache holds at most 2^27 latents)
   const int k0 = (int)(chunk * keys_per_chunk);
   const int k1 = (int)min(a.n_cache, (int64_t)k0 + keys_per_chunk);
-  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + b * a.k_sb * (TK::ROWB / DI);
+  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + b * a.k_sb * TK::ESZ;
+  const uint32_t* ksb = MX ? reinterpret_cast<const uint32_t*>(a.k_scale + b * (a.k_sb / 16)) : nullptr;
 
   // query operands, per-lane head weights and output rows
   typename TK::QOp qa[QW];
@@ -308,7 +384,10 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
     qok[qi] = j < a.Tq;
     const int64_t r = (int64_t)b * a.Tq + (qok[qi] ? j : a.Tq - 1);
     rows[qi] = r;
-    tile_query(a.q + r * (HI * DI), kn, half, qa[qi]);
+    if constexpr (MX)
+      tile_query_mx(a.q + r * (HI * DI), kn, half, qa[qi]);
+    else
+      tile_query(a.q + r * (HI * DI), kn, half, qa[qi]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) wl[qi][i] = a.w[r * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
     nv[qi] = qok[qi] ? (int)n_visible(a.q_pos[r], a.n_cache) : 0;
@@ -333,6 +412,8 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
       const int row = min(t0 + pc / PPR, kend - 1);
       if (pc < PIECES)
         v[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)row * TK::ROWB + 16 * (pc % PPR));
+      else if (MX && pc < PIECES + TS_TILE)  // one key's scale word
+        v[u][0] = ksb[min(t0 + pc - PIECES, kend - 1)];
     }
   };
   auto store_tile = [&](uint8_t* tile, const u32x4 (&v)[LPT]) {
@@ -340,6 +421,7 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
     for (int u = 0; u < LPT; ++u) {
       const int pc = u * NT + tid;
       if (pc < PIECES) *reinterpret_cast<u32x4*>(tile + (pc / PPR) * TK::LD + 16 * (pc % PPR)) = v[u];
+      else if (MX && pc < PIECES + TS_TILE) kts[tile == kt[0] ? 0 : 1][pc - PIECES] = v[u][0];
     }
   };
   struct Accs {
@@ -348,9 +430,16 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
   // the MFMAs of all queries of the wave on one tile
   auto mma = [&](const uint8_t* tile, Accs& A) {
     typename TK::QOp kop;
-    tile_key(tile, kn, half, kop);
+    if constexpr (MX) {
+      int ks[2];
+      tile_key_mx(tile, kts[tile == kt[0] ? 0 : 1], kn, half, kop, ks);
 #pragma unroll
-    for (int qi = 0; qi < QW; ++qi) A.v[qi] = tile_mfma(qa[qi], kop);
+      for (int qi = 0; qi < QW; ++qi) A.v[qi] = tile_mfma_mx(qa[qi], kop, ks);
+    } else {
+      tile_key(tile, kn, half, kop);
+#pragma unroll
+      for (int qi = 0; qi < QW; ++qi) A.v[qi] = tile_mfma(qa[qi], kop);
+    }
   };
   // the epilogue of one tile: ReLU . w . head sum, causal mask, block max
   auto epi = [&](int t0, const Accs& A) {
@@ -488,11 +577,12 @@ hipError_t launch_scan_t(const ScanArgs& a, int B, dim3 grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const void* k,
-                             bool k_fp8, int64_t k_sb, int64_t n_cache, const int64_t* q_pos,
-                             float* scores, int64_t s_stride, float* block_max,
-                             int64_t bm_stride, hipStream_t s) {
+                             int k_fmt, const uint8_t* k_scale, int64_t k_sb, int64_t n_cache,
+                             const int64_t* q_pos, float* scores, int64_t s_stride,
+                             float* block_max, int64_t bm_stride, hipStream_t s) {
   ScanArgs a{(const uint16_t*)q, w, k, k_sb, n_cache, q_pos, Tq,
-             scores, s_stride, block_max, bm_stride, 1};
+             scores, s_stride, block_max, bm_stride, 1, k_scale};
+  const bool k_fp8 = k_fmt == KEYS_FP8;
   if (Tq >= 64) {
     // many queries: MFMA-bound.  8 key ranges, tile-aligned (so block-aligned).
     constexpr int CH = 8;
@@ -500,12 +590,15 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
     kpc = (kpc + TS_TILE - 1) / TS_TILE * TS_TILE;
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
     dim3 grid(nchunks, (unsigned)((Tq + 15) / 16), (unsigned)B);
-    if (k_fp8)
+    if (k_fmt == KEYS_MXFP4)
+      hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KMx4>), grid, dim3(512), 0, s, a, kpc);
+    else if (k_fp8)
       hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KFp8>), grid, dim3(512), 0, s, a, kpc);
     else
       hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KBf16>), grid, dim3(512), 0, s, a, kpc);
     return hipGetLastError();
   }
+  if (k_fmt == KEYS_MXFP4) return hipErrorInvalidValue;  // rejected before launch
   if (!k_fp8 && Tq >= 2) {
     // a few queries per sequence (speculative verification): HBM-bound, the
     // keys are read once per 8 queries; ranges of whole tiles, ~1024 blocks

@@ -22,10 +22,11 @@ hipError_t launch_compress_step(int B, const void* kv, int64_t kv_sb, const void
 hipError_t launch_quant_nvfp4(const void* src, bool f32_in, int64_t rows, int cols,
                               uint8_t* packed, uint8_t* scales, hipStream_t s);
 
+enum { KEYS_BF16 = 0, KEYS_FP8 = 1, KEYS_MXFP4 = 2 };
 hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const void* k,
-                             bool k_fp8, int64_t k_sb, int64_t n_cache, const int64_t* q_pos,
-                             float* scores, int64_t s_stride, float* block_max,
-                             int64_t bm_stride, hipStream_t s);
+                             int k_fmt, const uint8_t* k_scale, int64_t k_sb, int64_t n_cache,
+                             const int64_t* q_pos, float* scores, int64_t s_stride,
+                             float* block_max, int64_t bm_stride, hipStream_t s);
 
 hipError_t launch_index_cand(int B, int Tq, const void* q, const float* w, const void* k,
                              bool k_fp8, int64_t k_sb, int64_t n_cache, const int64_t* q_pos,

@@ -16,7 +16,9 @@ Layout of one input set (all torch tensors on ``device``):
   q      bf16 [B][Tq][64][512]   attention queries
   sink   f32  [64]               per-head sink logit
   qs/ws/ks   candidate-source indexer: bf16 [B][Tq][32][128], f32 [B][Tq][32],
-             keys [B][N][128] (bf16, or uint8 E4M3 codes)
+             keys [B][N][128] (bf16, or uint8 E4M3 codes), or MXFP4 keys as
+             uint8 E2M1 codes [B][N][64] with ks_scale E8M0 bytes [B][N][4]
+             (ks_scale None otherwise; ki_scale likewise)
   qi/wi/ki   current-layer indexer, same shapes (the same tensors when the
              config uses one shared indexer)
   lat    latent cache: bf16 [B][N][512], or uint8 NVFP4 [B][N][256] with
@@ -53,7 +55,7 @@ class Config:
     K: int = 512
     W: int = 128
     W_cap: int = 128
-    key_fmt: str = "bf16"  # "bf16" | "fp8"
+    key_fmt: str = "bf16"  # "bf16" | "fp8" | "mxfp4"
     lat_fmt: str = "bf16"  # "bf16" | "nvfp4"
     win_fmt: str = "bf16"  # "bf16" | "fp8"
     shared_indexer: bool = False
@@ -104,7 +106,9 @@ def _configs():
              "1,048,576 raw tokens, bf16 caches")
     c7 = replace(c3, name="prefill_fp8", key_fmt="fp8", seed=6,
                  desc="the chunked prefill with FP8 E4M3 index keys (integer-valued, exact)")
-    return {c.name: c for c in (c1, c2, c3, c4, c5, c6, c7)}
+    c8 = replace(c3, name="prefill_mxfp4", key_fmt="mxfp4", seed=7,
+                 desc="the chunked prefill with MXFP4 index keys (E2M1 x E8M0, exact scores)")
+    return {c.name: c for c in (c1, c2, c3, c4, c5, c6, c7, c8)}
 
 
 CONFIGS = _configs()
@@ -134,6 +138,19 @@ def _int_fp8(shape, g, device):
     return x.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+def _mx_keys(shape, g, device):
+    """MXFP4 index keys: uniform random E2M1 codes (every code, values up to
+    +-6) and E8M0 block scales 2^-1 or 2^0, so every key is a multiple of
+    1/4 and every score stays exact in fp32.  Returns (codes [B][N][64],
+    scales [B][N][4])."""
+    B, N, _ = shape
+    codes = torch.randint(0, 256, (B, N, DI // 2), generator=g, device=device,
+                          dtype=torch.int32).to(torch.uint8)
+    scales = torch.randint(126, 128, (B, N, DI // 32), generator=g, device=device,
+                           dtype=torch.int32).to(torch.uint8)
+    return codes, scales
+
+
 def _head_weights(shape, g, device):
     return torch.randint(1, 17, shape, generator=g, device=device, dtype=torch.int32).to(torch.float32) / 16.0
 
@@ -148,16 +165,22 @@ def make_inputs(cfg: Config, device="cpu", seed: Optional[int] = None) -> dict:
     out["q_pos"] = q_positions(cfg).to(dev)
     out["q"] = _normal_bf16((B, Tq, HQ, D), g, dev)
     out["sink"] = torch.randn((HQ,), generator=g, device=dev, dtype=torch.float32)
-    kmake = _int_fp8 if cfg.key_fmt == "fp8" else _int_bf16
     out["qs"] = _int_bf16((B, Tq, HI, DI), g, dev)
     out["ws"] = _head_weights((B, Tq, HI), g, dev)
-    out["ks"] = kmake((B, N, DI), g, dev)
-    if cfg.shared_indexer:
-        out["qi"], out["wi"], out["ki"] = out["qs"], out["ws"], out["ks"]
+    if cfg.key_fmt == "mxfp4":
+        out["ks"], out["ks_scale"] = _mx_keys((B, N, DI), g, dev)
     else:
+        out["ks"] = (_int_fp8 if cfg.key_fmt == "fp8" else _int_bf16)((B, N, DI), g, dev)
+        out["ks_scale"] = None
+    if cfg.shared_indexer:
+        out["qi"], out["wi"], out["ki"], out["ki_scale"] = out["qs"], out["ws"], out["ks"], out["ks_scale"]
+    else:
+        assert cfg.key_fmt != "mxfp4", "MXFP4 keys serve the one-indexer prefill"
+        kmake = _int_fp8 if cfg.key_fmt == "fp8" else _int_bf16
         out["qi"] = _int_bf16((B, Tq, HI, DI), g, dev)
         out["wi"] = _head_weights((B, Tq, HI), g, dev)
         out["ki"] = kmake((B, N, DI), g, dev)
+        out["ki_scale"] = None
     if cfg.lat_fmt == "nvfp4":
         out["lat"] = torch.randint(0, 256, (B, N, D // 2), generator=g, device=dev,
                                    dtype=torch.int32).to(torch.uint8)

@@ -64,7 +64,9 @@ typedef enum csa2_dtype {
   CSA2_FP8_E4M3 = 2, /* OCP FP8 E4M3FN (bias 7, max 448, S.1111.111 = NaN) */
   CSA2_NVFP4 = 3,    /* E2M1 codes, 2 per byte (element 2i in the low      */
                      /* nibble of byte i), one E4M3 scale per 16 elements  */
-  CSA2_F32 = 4
+  CSA2_F32 = 4,
+  CSA2_MXFP4 = 5     /* index keys: E2M1 codes, 2 per byte (dim 2i in the  */
+                     /* low nibble of byte i), one E8M0 scale per 32 dims  */
 } csa2_dtype;
 
 typedef enum csa2_status {
@@ -171,7 +173,16 @@ int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
  *           small integers index queries take)
  *   w     : f32  [B][Tq][32] per-query, per-head weights
  *   k     : [B][n_cache][128] in k_dt (CSA2_BF16 or CSA2_FP8_E4M3), batch
- *           stride k_sb elements
+ *           stride k_sb elements; or CSA2_MXFP4 ([NVFP4] section 3.3 keeps
+ *           the index keys in FP4; section 4 describes MXFP4): k holds the
+ *           E2M1 codes [B][n_cache][64] bytes, batch stride k_sb bytes
+ *           (a multiple of 16), and k_scale the E8M0 scales
+ *           [B][n_cache][4] (dims 0-31, 32-63, 64-95, 96-127), batch stride
+ *           k_sb/16 bytes, 4-byte aligned; the query is rounded to E2M1
+ *           (exact for the small integers index queries take).  MXFP4 keys
+ *           are supported by the many-query scan (SCAN mode, Tq >= 64, the
+ *           chunked prefill) and return CSA2_EUNSUPPORTED elsewhere.
+ *   k_scale : MXFP4 only, else ignored (may be NULL)
  *   q_pos : int64 [B][Tq]
  *
  * mode CSA2_SCORES_SCAN: every latent p < n_cache is scored;
@@ -195,7 +206,8 @@ int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
 #define CSA2_SCORES_CAND 1
 int csa2_index_scores(int mode, int B, int Tq, const void *q, csa2_dtype q_dt,
                       const float *w, const void *k, csa2_dtype k_dt,
-                      int64_t k_sb, int64_t n_cache, const int64_t *q_pos,
+                      const uint8_t *k_scale, int64_t k_sb, int64_t n_cache,
+                      const int64_t *q_pos,
                       const int32_t *cand_blocks, int K_b, float *scores,
                       int64_t s_stride, int32_t *ids_out, float *block_max,
                       int64_t bm_stride, hipStream_t stream);

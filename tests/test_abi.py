@@ -63,8 +63,8 @@ def test_compress_validation(L):
 
 def _scores(L, mode=0, B=1, Tq=1, q=FAKE, q_dt=_lib.BF16, w=FAKE, k=FAKE, k_dt=_lib.BF16,
             k_sb=0, n=64, qp=FAKE, blocks=NULL, K_b=0, sc=FAKE, s_stride=64, ids=NULL, bm=NULL,
-            bm_stride=0):
-    return L.csa2_index_scores(mode, B, Tq, q, q_dt, w, k, k_dt, k_sb, n, qp, blocks, K_b, sc,
+            bm_stride=0, k_scale=NULL):
+    return L.csa2_index_scores(mode, B, Tq, q, q_dt, w, k, k_dt, k_scale, k_sb, n, qp, blocks, K_b, sc,
                                s_stride, ids, bm, bm_stride, None)
 
 
@@ -85,6 +85,14 @@ def test_index_scores_validation(L):
     assert _scores(L, mode=1, blocks=FAKE, K_b=0, ids=FAKE) == _lib.EINVAL
     assert _scores(L, mode=1, blocks=FAKE, K_b=16, ids=FAKE, s_stride=100) == _lib.EINVAL
     assert _scores(L, mode=1, blocks=FAKE, K_b=4, ids=NULL) == _lib.EINVAL
+    # MXFP4 keys: the many-query scan only, with its scales
+    mx = dict(k_dt=_lib.MXFP4, Tq=64, k_scale=ctypes.c_void_p(0x300000))
+    assert _scores(L, k_dt=_lib.MXFP4, Tq=1, k_scale=FAKE) == _lib.EUNSUPPORTED   # decode scan
+    assert _scores(L, mode=1, blocks=FAKE, K_b=4, ids=FAKE, **mx) == _lib.EUNSUPPORTED
+    assert _scores(L, **dict(mx, k_scale=NULL)) == _lib.EINVAL
+    assert _scores(L, **dict(mx, k_scale=ctypes.c_void_p(0x300002))) == _lib.EINVAL
+    assert _scores(L, B=2, k_sb=64 * 64 - 16, **mx) == _lib.EINVAL              # overlapping batches
+    assert _scores(L, B=2, k_sb=64 * 64 + 8, **mx) == _lib.EINVAL               # rows not 16-aligned
 
 
 def _select(L, R=1, n=16, sc=FAKE, s_stride=16, ids=NULL, id_stride=0, forced=NULL, last=0, k=4,

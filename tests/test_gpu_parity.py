@@ -71,18 +71,24 @@ def test_compress_stage_tiny():
     ("prefill_fp8", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=42)),
     ("prefill_fp8", dict(B=2, Tq=70, N=3001, t_last=6001, K_b=32, K=64, comp_T=0,
                          shared_indexer=False, seed=43)),
+    # MXFP4 keys (E2M1 x E8M0 scales 2^-1, 2^0), the FP4 MFMA; ragged tiles
+    ("prefill_mxfp4", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=44)),
+    ("prefill_mxfp4", dict(B=2, Tq=70, N=3001, t_last=6001, K_b=32, K=64, comp_T=0, seed=45)),
 ])
 def test_scan_cand_select_stages(name, kw):
     cfg = gen.shrink(gen.CONFIGS[name], **kw)
     inp = _inputs(cfg)
     host = np_subset(inp)
     R, nblk = cfg.R, cfg.nblk
+    mx = cfg.key_fmt == "mxfp4"  # keys as (codes, scales); the prefill pairs them with the gather
+    ks_h = (host["ks"], host["ks_scale"]) if mx else host["ks"]
     # rows padded to a multiple of 4 floats, as the score gather needs
     scores = torch.empty((R, (cfg.N + 3) // 4 * 4), dtype=torch.float32, device="cuda")[:, :cfg.N]
     bm = torch.empty((R, nblk), dtype=torch.float32, device="cuda")
-    api.index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], scores=scores, block_max=bm)
+    api.index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], scores=scores, block_max=bm,
+                   k_scale=inp["ks_scale"])
     torch.cuda.synchronize()
-    sc_ref, bm_ref = ref.scan(host["qs"], host["ws"], host["ks"], host["q_pos"], want_scores=True)
+    sc_ref, bm_ref = ref.scan(host["qs"], host["ws"], ks_h, host["q_pos"], want_scores=True)
     got_sc, got_bm = scores.cpu().numpy(), bm.cpu().numpy()
     assert np.array_equal(got_sc.astype(np.float64), sc_ref), "scan scores"
     assert np.array_equal(got_bm.astype(np.float64), bm_ref), "block max"
@@ -95,14 +101,16 @@ def test_scan_cand_select_stages(name, kw):
     blk_ref = ref.select(bm_ref, cfg.K_b, forced=forced)
     assert np.array_equal(blocks.cpu().numpy(), blk_ref), "block selection"
 
-    # candidate scoring on identical block lists
+    # candidate scoring on identical block lists (MXFP4 keys: the gather only)
     csc = torch.empty((R, cfg.K_b * 8), dtype=torch.float32, device="cuda")
     cid = torch.empty((R, cfg.K_b * 8), dtype=torch.int32, device="cuda")
-    api.index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], blocks, csc, cid)
-    torch.cuda.synchronize()
-    csc_ref, cid_ref = ref.cand(host["qi"], host["wi"], host["ki"], host["q_pos"], blk_ref)
-    assert np.array_equal(cid.cpu().numpy(), cid_ref), "candidate ids"
-    assert np.array_equal(csc.cpu().numpy().astype(np.float64), csc_ref), "candidate scores"
+    ki_h = (host["ki"], host["ki_scale"]) if mx else host["ki"]
+    csc_ref, cid_ref = ref.cand(host["qi"], host["wi"], ki_h, host["q_pos"], blk_ref)
+    if not mx:
+        api.index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], blocks, csc, cid)
+        torch.cuda.synchronize()
+        assert np.array_equal(cid.cpu().numpy(), cid_ref), "candidate ids"
+        assert np.array_equal(csc.cpu().numpy().astype(np.float64), csc_ref), "candidate scores"
 
     # the same candidates' entries gathered from the scan's own scores equal
     # the candidate indexer run with the scan's (q, w, k)
@@ -111,9 +119,11 @@ def test_scan_cand_select_stages(name, kw):
     api.gather_scores(scores, inp["q_pos"], blocks, gsc, gid, n_cache=cfg.N)
     torch.cuda.synchronize()
     gsc_ref, gid_ref = (csc_ref, cid_ref) if cfg.shared_indexer else \
-        ref.cand(host["qs"], host["ws"], host["ks"], host["q_pos"], blk_ref)
+        ref.cand(host["qs"], host["ws"], ks_h, host["q_pos"], blk_ref)
     assert np.array_equal(gid.cpu().numpy(), gid_ref), "gathered candidate ids"
     assert np.array_equal(gsc.cpu().numpy().astype(np.float64), gsc_ref), "gathered candidate scores"
+    if mx:
+        csc, cid = gsc, gid
 
     sel = torch.empty((R, cfg.K), dtype=torch.int32, device="cuda")
     api.select_topk(csc, cfg.K, sel, ids=cid)
@@ -311,6 +321,11 @@ def test_full_prefill_sampled_queries():
 def test_full_prefill_fp8_sampled_queries():
     Tq = gen.CONFIGS["prefill_fp8"].Tq
     _full("prefill_fp8", seqs=[0], queries=[0, 5, 300, 4097, Tq - 1])
+
+
+def test_full_prefill_mxfp4_sampled_queries():
+    Tq = gen.CONFIGS["prefill_mxfp4"].Tq
+    _full("prefill_mxfp4", seqs=[0], queries=[0, 7, 2048, 4099, Tq - 1])
 
 
 def test_full_1m():
