@@ -77,10 +77,16 @@ struct AttnArgs {
 };
 
 constexpr int kMaxDevices = 64;
-constexpr float RESCALE_TAU = 8.0f;  // largest log-weight above the reference point
+// The softmax runs in base 2: logits are pre-multiplied by log2(e) and the
+// weights are exp2 of them (one v_exp_f32 each), which is the same
+// distribution; the sink enters as sink * log2(e) and lse is converted back.
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float RESCALE_TAU = 11.5f;  // largest log2-weight above the reference point
 constexpr int SEL_CAP = 2048;       // largest K: a split's sel entries are cached in LDS
 
 struct Smem {
+  uint16_t q[HQ][KV_LD];  // the query's 64 heads (the S^T contraction's B operand)
   uint16_t kv[TILE][KV_LD];
   uint16_t vt[D][VT_LD];
   float rscale[TILE];
@@ -121,8 +127,9 @@ __device__ __forceinline__ u32x4 nvfp4_piece(uint32_t codes, uint32_t scale_byte
   return v;
 }
 
-// One wave per SIMD: the 64 heads x 512 fp32 accumulators, the query
-// operand and the next tile's rows take more than half of the register file.
+// One wave per SIMD: the 64 heads x 512 fp32 accumulators and the next
+// tile's rows take more than half of the register file; the query is read
+// from LDS for each tile.
 template <int LF, int WF>
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -149,17 +156,31 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     sv[m] = idx < n_lat ? selrow[lat_beg + idx] : -1;
   }
 
-  // Q^T operand of this wave's 16 heads: lane holds head 16w + l%16,
-  // dims 32c + 8g .. +7 for c = 0..15
-  const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + ((int64_t)j * HQ + 16 * wave + hl) * D;
-  bf16x8 qop[16];
+  // the query's 64 x 512 bf16 into LDS: thread tid moves 16 pieces of 16 B
+  {
+    const uint16_t* qb = a.q + (int64_t)b * a.q_sb + (int64_t)j * HQ * D;
+    u32x4 qv[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g);
+    for (int m = 0; m < 16; ++m) {
+      const int piece = tid + 256 * m;  // head piece / 64, dims 8 (piece % 64)
+      qv[m] = *reinterpret_cast<const u32x4*>(qb + (piece >> 6) * D + 8 * (piece & 63));
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int piece = tid + 256 * m;
+      *reinterpret_cast<u32x4*>(&sm.q[piece >> 6][8 * (piece & 63)]) = qv[m];
+    }
+  }
 
 #pragma unroll
   for (int m = 0; m < SEL_CAP / 256; ++m)
     if (tid + 256 * m < n_lat) sm.selc[tid + 256 * m] = sv[m];
   __syncthreads();
+  const float scale2 = a.scale * LOG2E;
+  // first window slot: raw position t - W + 1 modulo W_cap (later rows of
+  // the window follow it, wrapping once at most since W <= W_cap)
+  const int64_t w0 = t - (a.W - 1);
+  const int wslot0 = (int)(((w0 % a.W_cap) + a.W_cap) % a.W_cap);
 
   f32x4 o[32];
 #pragma unroll
@@ -214,9 +235,10 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         const int jw = TILE * (tt - a.tiles_lat) + 4 * rq + x;
-        const int64_t pos = t - (a.W - 1) + jw;
-        st.ok[x] = jw < a.W && pos >= 0;
-        slot[x] = (int64_t)b * a.win_sb + (st.ok[x] ? pos % a.W_cap : 0);
+        st.ok[x] = jw < a.W && w0 + jw >= 0;
+        int sl = wslot0 + jw;
+        sl = sl >= a.W_cap ? sl - a.W_cap : sl;
+        slot[x] = (int64_t)b * a.win_sb + (st.ok[x] ? sl : 0);
         st.rs[x] = WF == FMT_FP8 ? a.win_scale[slot[x]] : 1.0f;
       }
 #pragma unroll
@@ -283,7 +305,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int c = 0; c < 16; c += 2) {
-      bf16x8 kop[2][2];
+      // Q^T operand of this wave's 16 heads: lane holds head 16w + l%16,
+      // dims 32c + 8g .. +7
+      bf16x8 kop[2][2], qop[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        qop[u] = *reinterpret_cast<const bf16x8*>(&sm.q[16 * wave + hl][32 * (c + u) + 8 * g]);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -293,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-          s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st][u], qop[c + u], s[st], 0, 0, 0);
+          s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st][u], qop[u], s[st], 0, 0, 0);
     }
     // logits of rows 16st + 4g + i for head l%16
     float lg[2][4], rs[2][4];
@@ -304,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * st + 4 * g + i;
         rs[st][i] = sm.rscale[row];
-        lg[st][i] = sm.rvalid[row] ? s[st][i] * a.scale * rs[st][i] : -INFINITY;
+        lg[st][i] = sm.rvalid[row] ? s[st][i] * scale2 * rs[st][i] : -INFINITY;
         mt = fmaxf(mt, lg[st][i]);
       }
     mt = max_across_rows(mt);
@@ -326,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     const bool grow = mt > m_run + RESCALE_TAU;
     const bool scale_acc = grow && m_run != -INFINITY;
     if (__ballot(scale_acc) != 0) {
-      const float alpha = scale_acc ? expf(m_run - mt) : 1.0f;
+      const float alpha = scale_acc ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
       l_run *= alpha;
 #pragma unroll
       for (int i = 0; i < 32; ++i) o[i] *= alpha;
@@ -338,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = expf(lg[st][i] - m_run);
+        const float p = __builtin_amdgcn_exp2f(lg[st][i] - m_run);
         psum += p;
         pop[4 * st + i] = (__bf16)(p * rs[st][i]);
       }
@@ -375,10 +402,10 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     }
     return;
   }
-  const float sk = a.sink[h];
+  const float sk = a.sink[h] * LOG2E;
   const float M = fmaxf(m_run, sk);
-  const float em = m_run == -INFINITY ? 0.f : expf(m_run - M);
-  const float Z = l_run * em + expf(sk - M);
+  const float em = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  const float Z = l_run * em + __builtin_amdgcn_exp2f(sk - M);
   const float f = em / Z;
   uint16_t* orow = a.out + r * a.out_sb + (int64_t)h * D;
 #pragma unroll
@@ -388,7 +415,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     pk[1] = pack_bf16x2(o[T][2] * f, o[T][3] * f);
     *reinterpret_cast<u32x2*>(orow + 16 * T + 4 * g) = pk;
   }
-  if (a.lse && g == 0) a.lse[r * HQ + h] = M + logf(Z);
+  if (a.lse && g == 0) a.lse[r * HQ + h] = (M + __log2f(Z)) * LN2;
 }
 
 // merge the split partials of one query: grid (R, 16), 256 threads =
@@ -401,7 +428,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t r = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int d0 = (threadIdx.x & 63) * 8;
-  const float sk = a.sink[h];
+  const float sk = a.sink[h] * LOG2E;  // the partials' references are base 2
   const float* part = a.part + (r * a.splits * HQ + h) * PART;  // split s at + s * HQ * PART
   float ms[MAX_SPLITS], ls[MAX_SPLITS];
 #pragma unroll
@@ -416,7 +443,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   float M = sk;
 #pragma unroll
   for (int s = 0; s < MAX_SPLITS; ++s) M = fmaxf(M, ms[s]);
-  float Z = expf(sk - M);
+  float Z = __builtin_amdgcn_exp2f(sk - M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s0 = 0; s0 < MAX_SPLITS; s0 += MERGE_BATCH) {
@@ -435,7 +462,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < MERGE_BATCH; ++u) {
       const int s = s0 + u;
-      const float e = ms[s] == -INFINITY ? 0.f : expf(ms[s] - M);
+      const float e = ms[s] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
       Z += ls[s] * e;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -449,7 +476,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) pk[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   *reinterpret_cast<u32x4*>(a.out + r * a.out_sb + (int64_t)h * D + d0) = pk;
-  if (a.lse && (threadIdx.x & 63) == 0) a.lse[r * HQ + h] = M + logf(Z);
+  if (a.lse && (threadIdx.x & 63) == 0) a.lse[r * HQ + h] = (M + __log2f(Z)) * LN2;
 }
 
 }  // namespace
