@@ -40,7 +40,11 @@ namespace {
 
 constexpr int TILE = 32;            // rows per tile
 constexpr int KV_LD = D + 8;        // bf16 per row-major LDS row (1040 B)
-constexpr int VT_LD = TILE + 4;     // bf16 per transposed LDS row (72 B)
+// Transposed (V) tile: dim-major, the 32 rows of a dim in the order the PV
+// contraction's k-slots want them (column 8g + 4st + i holds row
+// 16st + 4g + i), 40 bf16 per dim: a lane's 8 k-slots are one 16-byte read,
+// and the 16 dims read together land in 16 distinct 4-bank groups.
+constexpr int VT_LD = TILE + 8;
 constexpr int PART = D + 4;         // floats per (query, split, head) partial (16-B multiple)
 
 enum { FMT_BF16 = 1, FMT_FP8 = 2, FMT_NVFP4 = 3 };
@@ -188,9 +192,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   bool seen = false;  // any valid row so far (wave-uniform)
 
-  // staging map: lane -> row quad rq (rows 4rq..4rq+3) and pieces p0, p0+32
-  const int rq = lane & 7;
-  const int p0 = (lane >> 3) + 8 * wave;
+  // staging map: lane -> row quad rq (rows 4rq..4rq+3) and pieces p0, p0+32;
+  // four consecutive lanes take four consecutive pieces of the same rows
+  // (64 contiguous bytes per row), and the 16 lanes of one LDS store phase
+  // cover 16 distinct bank groups (row-major pitch 260 words = 4 mod 64)
+  const int rq = (lane >> 2) & 7;
+  const int p0 = (lane & 3) + 4 * (lane >> 5) + 8 * wave;
 
   // A tile's rows are gathered into registers one tile ahead: the loads of
   // tile i+1 are in flight while tile i is computed from LDS.
@@ -281,10 +288,10 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
         u32x2 pr;
         pr[0] = ((v[0][w32] >> sh) & 0xffffu) | (((v[1][w32] >> sh) & 0xffffu) << 16);
         pr[1] = ((v[2][w32] >> sh) & 0xffffu) | (((v[3][w32] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&sm.vt[8 * p + d][4 * rq]) = pr;
+        *reinterpret_cast<u32x2*>(&sm.vt[8 * p + d][8 * (rq & 3) + 4 * (rq >> 2)]) = pr;
       }
     }
-    if (wave == 0 && (lane >> 3) == 0) {
+    if (wave == 0 && lane < 32 && (lane & 3) == 0) {  // one lane per row quad (rq = 0..7)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
         sm.rscale[4 * rq + x] = st.ok[x] ? st.rs[x] : 1.0f;
@@ -376,13 +383,8 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     for (int T0 = 0; T0 < 32; T0 += 4) {
       bf16x8 vop[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int T = T0 + u;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[16 * T + hl][4 * g]);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[16 * T + hl][16 + 4 * g]);
-        const u32x4 vv = {lo[0], lo[1], hi[0], hi[1]};
-        vop[u] = __builtin_bit_cast(bf16x8, vv);
-      }
+      for (int u = 0; u < 4; ++u)
+        vop[u] = *reinterpret_cast<const bf16x8*>(&sm.vt[16 * (T0 + u) + hl][8 * g]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         o[T0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[u], pop, o[T0 + u], 0, 0, 0);
