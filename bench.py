@@ -18,7 +18,10 @@ region starts.  Prints ONE JSON line: the headline metric with its roofline
 secondary workloads under "extra".
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                  [--only-main] [--calib]
+                  [--only-main] [--calib] [--only CONFIG]
+
+--only CONFIG times one workload's step alone and prints its stage times
+instead (used for the counter runs behind the committed profiles).
 """
 from __future__ import annotations
 
@@ -261,6 +264,29 @@ def calib_copy(torch, nbytes=1 << 30):
     torch.cuda.synchronize()
 
 
+def hbm_ceiling(torch, nbytes=1 << 30, iters=10):
+    """Practical HBM ceiling for context (never the roofline's denominator):
+    torch's own elementwise copy (reads and writes nbytes) and sum (reads
+    nbytes) over 1 GiB, timed with events on the current stream."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("sum", lambda: torch.sum(src), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(iters):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out[f"torch_{name}_GBs"] = round(moved * iters / (s.elapsed_time(e) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +295,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-main", action="store_true", help="skip the low-precision and prefill extras")
     ap.add_argument("--calib", action="store_true", help="also run a 1 GiB plain copy (counter scaling)")
+    ap.add_argument("--only", metavar="CONFIG", default=None,
+                    help="time only this workload's step (e.g. prefill) and print its stage times "
+                         "instead of the benchmark line (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the CSA2 path here is built and timed on a single "
@@ -282,6 +311,14 @@ def main():
     api.lib()  # fail loudly if the HIP library is not built
     if args.calib:
         calib_copy(torch)
+    if args.only is not None:
+        if args.only not in gen.CONFIGS:
+            print(f"unknown workload {args.only!r}; one of {sorted(gen.CONFIGS)}", file=sys.stderr)
+            sys.exit(2)
+        ocfg, _, _, oms, ost = time_config(args.only, args.steps, args.warmup, torch, gen, api)
+        print(json.dumps({"workload": args.only, "ms_per_step": round(oms, 4),
+                          "stages_us_eager": {k: round(v * 1e3, 2) for k, v in ost.items()}}), flush=True)
+        return
 
     cfg, inp, path, ms, stage_ms = time_config("1m", args.steps, args.warmup, torch, gen, api)
     sb = step_bytes(cfg)
@@ -335,6 +372,15 @@ def main():
     }
 
     extra = {}
+    # secondary view: the stages a layer runs when it reuses the block stage
+    # of an earlier layer (candidate indexer, position top-k, attention)
+    amort = stage_ms["index_cand"] + stage_ms["select_positions"] + stage_ms["sparse_attn"]
+    extra["amortized_layer_1m"] = {
+        "workload": "the 1M decode's candidate indexer + position top-512 + sparse attention only "
+                    "(eager stage times, launch gaps included); secondary",
+        "us": round(amort * 1e3, 2), "queries_per_s": round(cfg.R / (amort * 1e-3), 1),
+    }
+    extra["hbm_ceiling_context"] = hbm_ceiling(torch)
     if not args.only_main:
         del inp
         torch.cuda.empty_cache()
