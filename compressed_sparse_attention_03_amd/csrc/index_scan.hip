@@ -15,6 +15,8 @@ namespace {
 
 using namespace indexer;
 
+constexpr int MAX_TPW = 32;  // tiles per wave of the decode scan (launcher's cap)
+
 struct ScanArgs {
   const uint16_t* q;
   const float* w;
@@ -52,19 +54,42 @@ struct KRaw<KFp8> {
   u32x4 r[LOADS];
 };
 
+// A block's keys as one buffer resource: based at the block's first row and
+// clipped to the cache, so a row at or past n_cache reads as zeros (its
+// scores are masked like every invisible key's) and every offset is a small
+// 32-bit value: a lane-constant part (row within the tile, swizzled chunk)
+// and a wave-uniform part (the tile), which lives in a scalar register.
 template <typename KT>
-__device__ __forceinline__ void load_key_coalesced(const void* kbase, int64_t tile, int64_t n_cache,
-                                                   int lane, KRaw<KT>& R) {
+struct KeyRange {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t off[KRaw<KT>::LOADS];
+};
+
+constexpr int BUF_DWORD3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+template <typename KT>
+__device__ __forceinline__ KeyRange<KT> key_range(const void* kbase, int64_t row0, int64_t rows,
+                                                  int lane) {
   constexpr int ROW = KRaw<KT>::ROW, C = ROW / 16, RPL = 64 / C;  // chunks per row, rows per load
+  KeyRange<KT> kr;
+  const uint8_t* base = static_cast<const uint8_t*>(kbase) + row0 * ROW;
+  kr.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                              (int)(rows * ROW), BUF_DWORD3);
 #pragma unroll
   for (int c = 0; c < KRaw<KT>::LOADS; ++c) {
     const int rl = lane / C + RPL * c;  // tile row
-    int64_t row = tile * 16 + rl;
-    row = row < n_cache ? row : n_cache - 1;
-    const int chunk = (lane % C) ^ (rl % C);
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(kbase) + row * ROW) + chunk;
-    R.r[c] = __builtin_nontemporal_load(p);
+    kr.off[c] = (uint32_t)(rl * ROW + (((lane % C) ^ (rl % C)) << 4));
   }
+  return kr;
+}
+
+// tile_off: byte offset of the tile from the block's first row
+template <typename KT>
+__device__ __forceinline__ void load_key_coalesced(const KeyRange<KT>& kr, uint32_t tile_off,
+                                                   KRaw<KT>& R) {
+#pragma unroll
+  for (int c = 0; c < KRaw<KT>::LOADS; ++c)
+    R.r[c] = __builtin_amdgcn_raw_buffer_load_b128(kr.rsrc, kr.off[c], tile_off, 2 /* nt */);
 }
 
 // stage the tile into the wave's LDS buffer and read this lane's operand
@@ -93,7 +118,9 @@ __device__ __forceinline__ void relayout_key(const KRaw<KFp8>& R, uint8_t* kst, 
 template <int QPB, typename QT, typename KT>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   using KL = KRaw<KT>;  // what a fetch holds
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through a scalar register: the compiler then keeps the
+  // tile bookkeeping (indices, horizons, loop control) in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.y;
   const int j0 = blockIdx.z * QPB;
   const int nq = min(QPB, a.Tq - j0);
@@ -102,6 +129,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
   __shared__ __align__(16) uint8_t qstage[HI * DI];
   __shared__ __align__(16) uint8_t kstage[WAVES][16 * KRaw<KT>::ROW];
+  // the block's block maxima, written out as one contiguous run at the end
+  // (2 per tile, at most 32 tiles per wave)
+  __shared__ float bmst[QPB][WAVES * MAX_TPW * 2];
   QT Q[QPB];
   int64_t nv[QPB];
   int64_t max_nv = 0;
@@ -110,7 +140,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const int j = j0 + (qi < nq ? qi : 0);
     const int64_t r = (int64_t)b * a.Tq + j;
     load_query(a.q + r * (HI * DI), a.w + r * HI, Q[qi], lane, qstage);
-    nv[qi] = qi < nq ? n_visible(a.q_pos[r], a.n_cache) : 0;
+    // the same in every lane: kept in scalar registers
+    const int64_t v = qi < nq ? n_visible(a.q_pos[r], a.n_cache) : 0;
+    nv[qi] = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
     max_nv = nv[qi] > max_nv ? nv[qi] : max_nv;
   }
   const void* kb = (const void*)((const char*)a.k + b * a.k_sb * key_elem_bytes<KT>());
@@ -122,13 +155,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int64_t blk0 = (int64_t)blockIdx.x * WAVES * a.tiles_per_wave;
   int64_t t = blk0 + wave;
   const int64_t t_end = min(blk0 + (int64_t)WAVES * a.tiles_per_wave, n_tiles);
-  if (t >= t_end) return;
+  // a wave past the end of the block's stretch has no tile (it still joins
+  // the final barrier)
+  const int64_t row0 = blk0 * 16;
+  const KeyRange<KT> kr = key_range<KT>(kb, row0, min(a.n_cache, t_end * 16) - row0, lane);
 
   // The first DEPTH tiles are fetched without waiting for the queries'
   // positions (any tile of the cache is readable; invisible keys are masked
   // when scored); later fetches skip tiles past every query's horizon.
   auto fetch = [&](int64_t tile, KL& K, int64_t horizon) {
-    if (tile * 16 < horizon) load_key_coalesced<KT>(kb, tile, a.n_cache, lane, K);
+    if (tile * 16 < horizon) load_key_coalesced<KT>(kr, (uint32_t)((tile - blk0) * 16 * KL::ROW), K);
   };
   auto process = [&](int64_t tile, const KL& KLd) {
     const int64_t p = tile * 16 + kl;
@@ -147,8 +183,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       if (a.scores && g == 0 && p < a.n_cache) a.scores[r * a.s_stride + p] = s;
       if (a.block_max) {
         const float m = max_of_8_lanes(s);
-        const int64_t blk = p >> 3;
-        if (g == 0 && (kl & 7) == 0 && blk < nblk) a.block_max[r * a.bm_stride + blk] = m;
+        if (g == 0 && (kl & 7) == 0) bmst[qi][(tile - blk0) * 2 + (kl >> 3)] = m;
       }
     }
   };
@@ -169,6 +204,17 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         process(tt, buf[d]);
         if (tt + DEPTH * WAVES < t_end) fetch(tt + DEPTH * WAVES, buf[d], max_nv);
       }
+    }
+  }
+  if (a.block_max) {
+    // every tile of [blk0, t_end) was processed by one of the waves
+    __syncthreads();
+    const int64_t nb = min(2 * (t_end - blk0), nblk - 2 * blk0);
+#pragma unroll
+    for (int qi = 0; qi < QPB; ++qi) {
+      if (qi >= nq) break;
+      float* dst = a.block_max + ((int64_t)b * a.Tq + j0 + qi) * a.bm_stride + 2 * blk0;
+      for (int i = threadIdx.x; i < nb; i += WAVES * 64) dst[i] = bmst[qi][i];
     }
   }
 }
@@ -624,7 +670,7 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
   const int64_t target_waves = 8192;
   int64_t tpw = (n_tiles * B * nz + target_waves - 1) / target_waves;
   if (tpw < 1) tpw = 1;
-  if (tpw > 32) tpw = 32;
+  if (tpw > MAX_TPW) tpw = MAX_TPW;
   a.tiles_per_wave = (int)tpw;
   const int64_t per_block = tpw * WAVES;
   dim3 grid((unsigned)((n_tiles + per_block - 1) / per_block), (unsigned)B, (unsigned)nz);

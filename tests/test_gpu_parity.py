@@ -58,6 +58,10 @@ def test_compress_stage_tiny():
     ("tiny", {}),
     ("tiny", dict(N=2051, t_last=4101, seed=31)),            # ragged tiles / blocks
     ("1m_lowp", dict(B=2, N=4096, t_last=8191, Tq=3, seed=32)),  # FP8 keys, 3 queries
+    # one query per sequence (the decode scan's single-query kernel), ragged:
+    # a 3-key last tile and a last block whose stretch has 1 tile for 4 waves
+    ("1m", dict(B=3, N=2051, t_last=4101, K_b=64, K=128, seed=33)),
+    ("1m_lowp", dict(B=2, N=2051, t_last=4101, K_b=64, K=128, seed=34)),
     # many queries: the prefill scan kernel; ragged query groups, key chunks
     # and tiles, visibility changing inside a block of queries
     ("prefill", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=39)),
