@@ -26,9 +26,18 @@ FLAGS = [
 ]
 
 
+# per-source extra flags
+SOURCE_FLAGS = {
+    # the attention's accumulators stay in vector registers (VGPR-form MFMA):
+    # with them in the matrix-core registers the compiler copied all 128 of
+    # them out on every tile for the rare softmax rescale
+    "sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

@@ -19,8 +19,9 @@
 //   * every row is gathered from HBM once (1 KiB bf16, or 256 B NVFP4 codes +
 //     32 B scales, or 512 B FP8 + a row scale), dequantised in registers to
 //     bf16 (exact: E2M1 x E4M3 and E4M3 values are all bf16 values) and
-//     stored to LDS twice: row-major (the K operand) and transposed (the V
-//     operand), so the same bytes feed both contractions;
+//     stored to LDS once, row-major: the K operand is read from it directly
+//     and the V operand through the LDS transpose read (ds_read_b64_tr_b16),
+//     so the same bytes feed both contractions;
 //   * wave w handles heads 16w..16w+15:
 //       S^T = KV . Q^T  (v_mfma_f32_16x16x32_bf16, rows x heads, K = 512)
 //     which leaves each lane with a single head (l%16) and 8 of the rows,
@@ -40,11 +41,6 @@ namespace {
 
 constexpr int TILE = 32;            // rows per tile
 constexpr int KV_LD = D + 8;        // bf16 per row-major LDS row (1040 B)
-// Transposed (V) tile: dim-major, the 32 rows of a dim in the order the PV
-// contraction's k-slots want them (column 8g + 4st + i holds row
-// 16st + 4g + i), 40 bf16 per dim: a lane's 8 k-slots are one 16-byte read,
-// and the 16 dims read together land in 16 distinct 4-bank groups.
-constexpr int VT_LD = TILE + 8;
 constexpr int PART = D + 4;         // floats per (query, split, head) partial (16-B multiple)
 
 enum { FMT_BF16 = 1, FMT_FP8 = 2, FMT_NVFP4 = 3 };
@@ -89,10 +85,20 @@ constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_TAU = 11.5f;  // largest log2-weight above the reference point
 constexpr int SEL_CAP = 2048;       // largest K: a split's sel entries are cached in LDS
 
+// 8 bf16 of the PV contraction's A operand from two LDS transpose reads
+// (4 values each) of the row-major tile.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ bf16x8 pv_operand(const uint16_t* lo, const uint16_t* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)lo);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)hi);
+  const u32x2 a2 = __builtin_bit_cast(u32x2, a), b2 = __builtin_bit_cast(u32x2, b);
+  return __builtin_bit_cast(bf16x8, (u32x4){a2[0], a2[1], b2[0], b2[1]});
+}
+
 struct Smem {
   uint16_t q[HQ][KV_LD];  // the query's 64 heads (the S^T contraction's B operand)
-  uint16_t kv[TILE][KV_LD];
-  uint16_t vt[D][VT_LD];
+  uint16_t kv[TILE][KV_LD];  // the tile, row-major: QK operand, and PV operand via transpose reads
   float rscale[TILE];
   int rvalid[TILE];
   int32_t selc[SEL_CAP];  // sel[lat_beg ..] of this workgroup's latent rows
@@ -275,21 +281,9 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int pp = 0; pp < 2; ++pp) {
       const int p = p0 + 32 * pp;
-      u32x4 v[4];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        v[x] = decoded(st, pp, x);
-        *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = v[x];
-      }
-      // transpose: dim 8p+d gets the four rows' values side by side
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const int w32 = d >> 1, sh = 16 * (d & 1);
-        u32x2 pr;
-        pr[0] = ((v[0][w32] >> sh) & 0xffffu) | (((v[1][w32] >> sh) & 0xffffu) << 16);
-        pr[1] = ((v[2][w32] >> sh) & 0xffffu) | (((v[3][w32] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<u32x2*>(&sm.vt[8 * p + d][8 * (rq & 3) + 4 * (rq >> 2)]) = pr;
-      }
+      for (int x = 0; x < 4; ++x)
+        *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = decoded(st, pp, x);
     }
     if (wave == 0 && lane < 32 && (lane & 3) == 0) {  // one lane per row quad (rq = 0..7)
 #pragma unroll
@@ -299,6 +293,15 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       }
     }
   };
+
+  // PV operand addresses: ds_read_b64_tr_b16 works on 16-lane groups, lane
+  // 4a + b of a group receiving, as its value j, element b of the four
+  // 16-bit values addressed by lane 4j + a.  Lane (group g, 4j + a) therefore
+  // addresses dims 16T + 4a .. +3 of row 4g + j (k-slots 0-3) and of row
+  // 16 + 4g + j (k-slots 4-7), and every lane gets its dim's 8 rows.
+  const int trj = (lane & 15) >> 2, tra = lane & 3;
+  const uint16_t* tr_lo = &sm.kv[4 * g + trj][4 * tra];
+  const uint16_t* tr_hi = &sm.kv[16 + 4 * g + trj][4 * tra];
 
   if (tile_beg < tile_end) gather(tile_beg, nxt);
   for (int tt = tile_beg; tt < tile_end; ++tt) {
@@ -377,14 +380,14 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
         pop[4 * st + i] = (__bf16)(p * rs[st][i]);
       }
     l_run += psum;
-    // O^T += V^T . P^T ; A lane: dim 16T + l%16, k-slots = rows 4g..4g+3, 16+4g..16+4g+3
+    // O^T += V^T . P^T ; A lane: dim 16T + l%16, k-slots = rows 4g..4g+3, 16+4g..16+4g+3,
+    // read from the row-major tile by two LDS transpose reads (tr_lo, tr_hi);
     // operands read 4 MFMAs ahead so that LDS latency overlaps the MFMAs
 #pragma unroll
     for (int T0 = 0; T0 < 32; T0 += 4) {
       bf16x8 vop[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        vop[u] = *reinterpret_cast<const bf16x8*>(&sm.vt[16 * (T0 + u) + hl][8 * g]);
+      for (int u = 0; u < 4; ++u) vop[u] = pv_operand(tr_lo + 16 * (T0 + u), tr_hi + 16 * (T0 + u));
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         o[T0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[u], pop, o[T0 + u], 0, 0, 0);

@@ -241,6 +241,71 @@ def test_attention_stage(name, kw, tol):
     assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3
 
 
+@pytest.mark.parametrize("name,kw,tol", [
+    ("tiny", dict(Tq=300, K_b=16, K=128, W_cap=512, seed=51), BF16_TOL),
+    ("1m_lowp", dict(B=2, Tq=100, N=4096, t_last=8191, K_b=64, K=256, seed=52), LOWP_TOL),
+])
+def test_attention_rescale(name, kw, tol):
+    """Logits that keep growing from tile to tile: latent rows scaled up with
+    their position (bf16 rows by up to 6x, NVFP4 group scales from 2^-4 to
+    1.875) and enough queries that each workgroup walks all of a query's
+    tiles.  The running softmax reference then moves several times per head,
+    so the accumulators are rescaled; the result must match the oracle's
+    one-pass softmax all the same."""
+    cfg = gen.shrink(gen.CONFIGS[name], **kw)
+    inp = _inputs(cfg)
+    N = cfg.N
+    ramp = torch.linspace(0.0, 1.0, N, device="cuda")
+    if inp["lat_scale"] is None:
+        inp["lat"] = (inp["lat"].float() * (1.0 + 5.0 * ramp)[None, :, None]).bfloat16()
+    else:
+        codes = (0x18 + torch.round(ramp * (0x3F - 0x18))).to(torch.uint8)
+        inp["lat_scale"] = codes[None, :, None].expand_as(inp["lat_scale"]).contiguous()
+    host = np_subset(inp)
+    R, K = cfg.R, cfg.K
+    # K latents spread evenly over the visible ones, ascending: later tiles
+    # hold larger rows; a softmax scale 8x the usual one
+    scale = 8.0 * cfg.scale
+    sel = np.full((R, K), -1, np.int32)
+    for r in range(R):
+        nv = ref.n_vis(int(host["q_pos"].reshape(-1)[r]), N)
+        picks = np.unique(np.linspace(0, nv - 1, min(K, nv)).astype(np.int64))
+        sel[r, :len(picks)] = picks
+    # the lazy-rescale condition (a tile's max logit above the reference by
+    # more than 11.5 in log2 units) must actually occur for most heads
+    lat = host["lat"] if host["lat_scale"] is None else None
+    lat_f = (ref.bf16_array(lat) if lat is not None
+             else ref.dequant_nvfp4(host["lat"].reshape(-1, 256), host["lat_scale"].reshape(-1, 32))
+             .reshape(cfg.B, N, 512))
+    q = ref.bf16_array(host["q"]).reshape(R, 64, 512)
+    moved = 0
+    for r in range(0, R, 7):
+        rows = lat_f[r // cfg.Tq][sel[r][sel[r] >= 0]]
+        lg = q[r] @ rows.T * scale / np.log(2.0)  # log2 units, [64, rows]
+        tmax = np.stack([lg[:, i:i + 32].max(1) for i in range(0, lg.shape[1], 32)], 1)
+        ref_pt = tmax[:, 0].copy()
+        for t in range(1, tmax.shape[1]):
+            up = tmax[:, t] > ref_pt + 11.5
+            moved += int(up.sum())
+            ref_pt = np.where(up, tmax[:, t], ref_pt)
+    assert moved >= (R // 7) * 64 // 2, f"rescale condition met only {moved} times"
+    sel_t = torch.from_numpy(sel).cuda()
+    out = torch.empty((R, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, 64), dtype=torch.float32, device="cuda")
+    wsb = api.workspace_bytes(2, R, K, cfg.W)
+    ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device="cuda")
+    say(f"  rescale condition met {moved} times over {(R + 6) // 7} sampled queries x 64 heads")
+    api.sparse_attn(inp["q"], inp["lat"], sel_t, inp["win"], inp["q_pos"], inp["sink"], cfg.W,
+                    scale, out, lat_scale=inp["lat_scale"], win_scale=inp["win_scale"],
+                    lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref.attn(host["q"], host["lat"], sel, host["win"], host["q_pos"], host["sink"],
+                              cfg.W, scale, lat_scale=host["lat_scale"],
+                              win_scale=host["win_scale"])
+    check_close("attention out (rescaled)", bf16_to_np(out).reshape(o_ref.shape), o_ref, tol)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3 * max(1.0, np.abs(lse_ref).max())
+
+
 # ------------------------------------------------------ chained, small
 @pytest.mark.parametrize("name,kw", [
     ("tiny", {}),
