@@ -987,11 +987,19 @@ __global__ __launch_bounds__(THREADS) void select_finish_kernel(SelArgs a, const
 //     valid entry holding the forced id) by block reductions; the forced key
 //     is set aside (0) and k_rem = k - 1 others are wanted;
 //  2. E > 8: a bracket [Bt, A] from 2048 of the register keys, as in the
-//     sampled paths; "in" = key > A, candidates = Bt <= key <= A.  When the
-//     counts show that it missed, every valid entry is a candidate instead, so
-//     the result never depends on the sample.  E = 8: all are candidates;
-//  3. the exact key threshold over the candidates (radix on the registers);
-//  4. ballots into the chosen and tie bitmaps, ordered read-back.
+//     sampled paths; "in" = key > A, candidates = Bt <= key <= A, both
+//     counted by one block scan.  When the bracket holds and the candidates
+//     fit ROW_LIST, they are compacted into an LDS list of (key, column)
+//     composites, two per thread at most, and steps 3-4 work on the list;
+//     when the counts show that it missed, every valid entry is a candidate
+//     instead (in registers), so the result never depends on the sample.
+//     E = 8: all are candidates;
+//  3. the exact key threshold over the candidates (radix on the list, or on
+//     the registers);
+//  4. ballots into the chosen and tie bitmaps (list candidates: bit sets),
+//     ordered read-back.
+constexpr int ROW_LIST = 2048;  // compacted candidate capacity of the register-row path
+
 template <int E>
 struct RowsSmem {
   Shared sh;
@@ -999,6 +1007,7 @@ struct RowsSmem {
   ThreshSmem ts;
   uint64_t bitmap[E * 16];  // 64 columns per entry: the two words of one ballot
   uint64_t tiemap[E * 16];
+  uint64_t list[E > 8 ? ROW_LIST : 1];  // (key << 32) | ~column of each candidate
 };
 
 template <int E, bool IDS>
@@ -1085,6 +1094,8 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
   uint32_t A = 0u, Bt = 1u, m = 0u;  // A = 0: every valid key is in
   CandStats st{0u, 0u, 0u, 0u, 0u, 0u};
   bool have_st = false;
+  int listed = 0;            // candidates compacted into sm.list (block-uniform)
+  uint32_t n_list = 0;
   if (n_rest > k_rem) {
     A = 0xffffffffu;  // nothing in, every valid key a candidate
     m = k_rem;
@@ -1102,33 +1113,75 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
       // every column of [0, 1024 E) is sampled with probability 2 / E
       uint32_t A2, B2;
       bracket_core<THREADS, 2>(v, (float)k_rem * 2.0f / (float)E, sm.ss, sm.sh, &A2, &B2);
-      // one reduction: the counts that check the bracket and the statistics
-      // of its candidates
-      const CandStats s2 = cand_stats<E, 0>(key, B2, A2, sm.sh);
-      if (s2.above <= k_rem && k_rem <= s2.above + s2.count) {
+      // keys above the bracket and inside it, counted by one scan of both
+      // (packed: 16 bits each, totals at most 16384 below 2^16)
+      uint32_t c_in = 0, c_cand = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        c_in += key[i] > A2 ? 1u : 0u;
+        c_cand += (key[i] >= B2 && key[i] <= A2) ? 1u : 0u;
+      }
+      uint32_t tot;
+      const uint32_t before = block_exclusive_scan((c_in << 16) | c_cand, sm.sh, &tot);
+      const uint32_t n_in = tot >> 16, n_cand = tot & 0xffffu;
+      if (n_in <= k_rem && k_rem <= n_in + n_cand) {
         A = A2;
         Bt = B2;
-        m = k_rem - s2.above;
-        st = s2;
-        have_st = true;
+        m = k_rem - n_in;
+        if (n_cand <= (uint32_t)ROW_LIST) {
+          listed = 1;
+          n_list = n_cand;
+          uint32_t pos = before & 0xffffu;
+#pragma unroll
+          for (int i = 0; i < E; ++i)
+            if (key[i] >= B2 && key[i] <= A2)
+              sm.list[pos++] = ((uint64_t)key[i] << 32) | (uint64_t)(0xffffffffu - (uint32_t)(i * THREADS + tid));
+        } else {
+          st = cand_stats<E, 0>(key, Bt, A, sm.sh);
+          have_st = true;
+        }
       }
     }
-    if (!have_st && m > 0) st = cand_stats<E, 0>(key, Bt, A, sm.sh);
+    if (!listed && !have_st && m > 0) st = cand_stats<E, 0>(key, Bt, A, sm.sh);
   }
 
   // ---- 3 -------------------------------------------------------------------
   KeyThreshold th{0u, 0u, 0, 0, true, 0u};
-  if (m > 0) th = key_threshold<E, 0>(key, Bt, A, m, st, sm.ts);
+  constexpr int LP = ROW_LIST / THREADS;  // list entries per thread
+  uint32_t lkey[LP], lcol[LP];
+#pragma unroll
+  for (int u = 0; u < LP; ++u) {
+    lkey[u] = 0u;
+    lcol[u] = 0u;
+  }
+  if (listed) {
+    __syncthreads();  // the list is written
+#pragma unroll
+    for (int u = 0; u < LP; ++u) {
+      const uint32_t idx = tid + u * THREADS;
+      const uint64_t c = idx < n_list ? sm.list[idx] : 0ull;
+      lkey[u] = (uint32_t)(c >> 32);
+      lcol[u] = 0xffffffffu - (uint32_t)c;
+    }
+    if (m > 0) {
+      const CandStats ls = cand_stats<LP, 0>(lkey, 1u, 0xffffffffu, sm.sh);
+      th = key_threshold<LP, 0>(lkey, 1u, 0xffffffffu, m, ls, sm.ts);
+    }
+  } else if (m > 0) {
+    th = key_threshold<E, 0>(key, Bt, A, m, st, sm.ts);
+  }
 
   // ---- 4 -------------------------------------------------------------------
-  // lane i of each wave keeps the ballots of element i: one store per lane
+  // lane i of each wave keeps the ballots of element i: one store per lane.
+  // Listed candidates are not in the ballots (their key <= A); they are set
+  // in the bitmaps afterwards.
   uint64_t my_cb = 0ull, my_tb = 0ull;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
     const uint32_t k = key[i];
     bool chosen = k > A || i * THREADS + tid == fcol;
     bool tie = false;
-    if (m > 0 && k >= Bt && k <= A) {
+    if (!listed && m > 0 && k >= Bt && k <= A) {
       const int cmp = th_cmp(th, k);
       chosen = chosen || cmp > 0 || (cmp == 0 && th.take_all);
       tie = cmp == 0 && !th.take_all;
@@ -1142,6 +1195,19 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
   if (lane < E) {
     sm.bitmap[lane * NWAVES + wave] = my_cb;
     sm.tiemap[lane * NWAVES + wave] = my_tb;
+  }
+  if (listed && m > 0) {
+    __syncthreads();  // ballot words stored
+    uint32_t* bm32 = reinterpret_cast<uint32_t*>(sm.bitmap);
+    uint32_t* tm32 = reinterpret_cast<uint32_t*>(sm.tiemap);
+#pragma unroll
+    for (int u = 0; u < LP; ++u) {
+      if (!lkey[u]) continue;
+      const int cmp = th_cmp(th, lkey[u]);
+      const uint32_t c = lcol[u];
+      if (cmp > 0 || (cmp == 0 && th.take_all)) atomicOr(&bm32[c >> 5], 1u << (c & 31));
+      else if (cmp == 0) atomicOr(&tm32[c >> 5], 1u << (c & 31));
+    }
   }
   __syncthreads();
   read_back(a, row, th, (int)((a.n + 31) / 32), reinterpret_cast<uint32_t*>(sm.bitmap),

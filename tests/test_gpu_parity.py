@@ -178,10 +178,16 @@ def test_gather_edge_cases():
     # longer rows: few rows take the split path, else one workgroup per row from memory
     (60, 2, 100000, 2048, "allequal"), (61, 3, 131072, 2048, "forced"),
     (62, 2, 140000, 300, "last"), (63, 2, 100000, 1500, "ids"),
+    # continuous scores (few ties): rows of 8K-16K entries take the compacted
+    # candidate list; k from 64 to 2048, with and without a forced id
+    (64, 9, 16384, 512, "cont"), (65, 4, 12000, 1500, "cont"), (66, 5, 16384, 64, "cont_forced"),
+    (67, 3, 9000, 2048, "cont"),
 ])
 def test_select_edge_cases(seed, R, n, k, mode):
     rng = np.random.default_rng(seed)
     scores = rng.integers(0, 40, (R, n)).astype(np.float32) / 16
+    if mode.startswith("cont"):
+        scores = rng.standard_normal((R, n)).astype(np.float32)
     if mode == "allequal":
         scores[:] = 1.5
     scores[rng.random((R, n)) < 0.07] = -np.inf
@@ -191,7 +197,7 @@ def test_select_edge_cases(seed, R, n, k, mode):
         ids = np.tile((np.arange(n) * 2 + 1).astype(np.int32), (R, 1))
         ids[rng.random((R, n)) < 0.05] = -1
     forced = None
-    if mode == "forced":
+    if mode in ("forced", "cont_forced"):
         forced = rng.integers(0, n, R).astype(np.int32)
         forced[0] = -1
     out = torch.empty((R, k), dtype=torch.int32, device="cuda")
