@@ -303,6 +303,14 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   const uint16_t* tr_lo = &sm.kv[4 * g + trj][4 * tra];
   const uint16_t* tr_hi = &sm.kv[16 + 4 * g + trj][4 * tra];
 
+  // this wave's 16 heads of the query as QK operands, held in registers for
+  // all tiles (lane: head 16w + l%16, dims 32c + 8g .. +7); read from the
+  // staged query once instead of once per tile
+  bf16x8 qreg[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    qreg[c] = *reinterpret_cast<const bf16x8*>(&sm.q[16 * wave + hl][32 * c + 8 * g]);
+
   if (tile_beg < tile_end) gather(tile_beg, nxt);
   for (int tt = tile_beg; tt < tile_end; ++tt) {
     __syncthreads();  // previous tile fully consumed
@@ -315,12 +323,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int c = 0; c < 16; c += 2) {
-      // Q^T operand of this wave's 16 heads: lane holds head 16w + l%16,
-      // dims 32c + 8g .. +7
-      bf16x8 kop[2][2], qop[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        qop[u] = *reinterpret_cast<const bf16x8*>(&sm.q[16 * wave + hl][32 * (c + u) + 8 * g]);
+      bf16x8 kop[2][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-          s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st][u], qop[u], s[st], 0, 0, 0);
+          s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[st][u], qreg[c + u], s[st], 0, 0, 0);
     }
     // logits of rows 16st + 4g + i for head l%16
     float lg[2][4], rs[2][4];
