@@ -40,7 +40,12 @@ namespace csa2 {
 namespace {
 
 constexpr int TILE = 32;            // rows per tile
-constexpr int KV_LD = D + 8;        // bf16 per row-major LDS row (1040 B)
+// Row-major LDS tile: 528 bf16 per row (264 words, 8 mod 64 banks), which
+// makes the PV transpose reads conflict-free (the 4 consecutive rows x 4
+// half-pieces a 16-lane group reads land on 16 distinct bank pairs).
+// Measured against 520, 536 and 552 (and 528 with a piece swizzle for the
+// QK operand reads): 528 is fastest.
+constexpr int KV_LD = D + 16;
 constexpr int PART = D + 4;         // floats per (query, split, head) partial (16-B multiple)
 
 enum { FMT_BF16 = 1, FMT_FP8 = 2, FMT_NVFP4 = 3 };
@@ -200,8 +205,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 
   // staging map: lane -> row quad rq (rows 4rq..4rq+3) and pieces p0, p0+32;
   // four consecutive lanes take four consecutive pieces of the same rows
-  // (64 contiguous bytes per row), and the 16 lanes of one LDS store phase
-  // cover 16 distinct bank groups (row-major pitch 260 words = 4 mod 64)
+  // (64 contiguous bytes per row)
   const int rq = (lane >> 2) & 7;
   const int p0 = (lane & 3) + 4 * (lane >> 5) + 8 * wave;
 
