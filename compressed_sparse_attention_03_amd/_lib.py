@@ -22,7 +22,7 @@ EXPORTS = (
     "csa2_status_string", "csa2_version", "csa2_compress", "csa2_index_scores",
     "csa2_select_topk", "csa2_sparse_attn", "csa2_dequant_fp8", "csa2_dequant_nvfp4",
     "csa2_workspace_bytes", "csa2_compress_nvfp4", "csa2_compress_step", "csa2_quant_nvfp4",
-    "csa2_gather_scores",
+    "csa2_gather_scores", "csa2_gather_select",
 )
 
 _lib = None
@@ -61,6 +61,7 @@ def lib():
         "csa2_compress_step": (I, [I, P, I64, P, I64, P, P, I, P, P, I64, I64, P]),
         "csa2_quant_nvfp4": (I, [P, I, I64, I, P, P, P]),
         "csa2_gather_scores": (I, [I, I, P, I64, I64, P, P, I, P, P, I64, P]),
+        "csa2_gather_select": (I, [I, I, P, I64, I64, P, P, I, I, P, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -174,6 +174,21 @@ def gather_scores(all_scores, q_pos, blocks, scores, ids, n_cache=None, stream=N
         _p(ids), scores.stride(0), _stream(stream)))
     return scores, ids
 
+def gather_select(all_scores, q_pos, blocks, k: int, out, n_cache=None, stream=None):
+    """a4 from stored scores and a5 in one pass: the position top-k of the
+    candidates of ``blocks`` gathered from the scan's score matrix, equal to
+    gather_scores followed by select_topk.  out int32 [B*Tq][>=k]."""
+    B, Tq = q_pos.shape
+    K_b = blocks.shape[1]
+    N = all_scores.shape[1] if n_cache is None else n_cache
+    assert blocks.is_contiguous() and q_pos.is_contiguous() and all_scores.stride(1) == 1
+    assert out.stride(1) == 1
+    check("csa2_gather_select", lib().csa2_gather_select(
+        B, Tq, _p(all_scores), all_scores.stride(0), N, _p(q_pos), _p(blocks), K_b, k, _p(out),
+        out.stride(0), _stream(stream)))
+    return out
+
+
 def select_topk(scores, k: int, out, ids=None, forced=None, force_last=False, ws=None,
                 stream=None):
     """a3 / a5: top-k ids per row (ascending, -1 padded).  ``ws``: scratch of
@@ -253,6 +268,10 @@ class DecodePath:
         nblk = (N + BLK - 1) // BLK
         dev = torch.device(device)
         self.one_indexer = one_indexer
+        # one indexer: gather + position top-k in one call when a row of
+        # 8 * K_b candidates fits one workgroup's registers
+        R8 = K_b * BLK
+        self.fused_gather = one_indexer and (R8 <= 16384 or (R >= 256 and R8 <= 32768))
         # row stride a multiple of 4 floats (16-byte rows for the gather)
         self.all_scores = (torch.empty((R, (N + 3) // 4 * 4), dtype=torch.float32, device=dev)
                            if one_indexer else None)
@@ -296,14 +315,22 @@ class DecodePath:
         if self.one_indexer:
             if not (inp["qi"] is inp["qs"] and inp["wi"] is inp["ws"] and inp["ki"] is inp["ks"]):
                 raise ValueError("one_indexer path needs the same indexer for both stages")
-            gather_scores(self.all_scores, inp["q_pos"], self.blocks, self.cand_scores,
-                          self.cand_ids, n_cache=self.N, stream=stream)
+            mark(4)
+            if self.fused_gather:
+                # the candidates gathered inside the position top-k (one pass)
+                gather_select(self.all_scores, inp["q_pos"], self.blocks, self.K, self.sel,
+                              n_cache=self.N, stream=stream)
+            else:
+                gather_scores(self.all_scores, inp["q_pos"], self.blocks, self.cand_scores,
+                              self.cand_ids, n_cache=self.N, stream=stream)
+                select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids,
+                            ws=self.sel_ws, stream=stream)
         else:
             index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], self.blocks,
                        self.cand_scores, self.cand_ids, stream=stream)
-        mark(4)
-        select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids, ws=self.sel_ws,
-                    stream=stream)
+            mark(4)
+            select_topk(self.cand_scores, self.K, self.sel, ids=self.cand_ids, ws=self.sel_ws,
+                        stream=stream)
         mark(5)
         sparse_attn(inp["q"], inp["lat"], self.sel, inp["win"], inp["q_pos"], inp["sink"], self.W,
                     scale, self.out, lat_scale=inp.get("lat_scale"), win_scale=inp.get("win_scale"),

@@ -43,7 +43,7 @@ const char* csa2_status_string(int status) {
   }
 }
 
-int csa2_version(void) { return (1 << 16) | 1; }
+int csa2_version(void) { return (1 << 16) | 2; }
 
 size_t csa2_workspace_bytes(int op, int64_t R, int64_t n, int64_t k) {
   if (R <= 0) return 0;
@@ -225,6 +225,29 @@ int csa2_gather_scores(int B, int Tq, const float* all, int64_t a_stride, int64_
   clear_stale_error();
   return launched(csa2::launch_gather_cand(R, all, a_stride, n_cache, q_pos, cand_blocks, K_b,
                                            scores, ids_out, s_stride, stream));
+}
+
+int csa2_gather_select(int B, int Tq, const float* all, int64_t a_stride, int64_t n_cache,
+                       const int64_t* q_pos, const int32_t* cand_blocks, int K_b, int k,
+                       int32_t* out, int64_t o_stride, hipStream_t stream) {
+  if (B < 0 || Tq < 0 || n_cache < 0 || k < 1) return CSA2_EINVAL;
+  if (n_cache > kMaxN * 8) return CSA2_EUNSUPPORTED;
+  const int64_t R = (int64_t)B * Tq;
+  if (R == 0) return CSA2_OK;
+  if (!q_pos || !cand_blocks || !out || K_b < 1) return CSA2_EINVAL;
+  if (K_b > kMaxN / CSA2_BLOCK || k > kMaxN) return CSA2_EUNSUPPORTED;
+  if (R > INT32_MAX || !csa2::gather_select_supported(R, (int64_t)K_b * CSA2_BLOCK))
+    return CSA2_EUNSUPPORTED;
+  if (o_stride < k || !aligned(out, 4)) return CSA2_EINVAL;
+  if (n_cache > 0 && (!all || !aligned(all, 4) || a_stride < n_cache)) return CSA2_EINVAL;
+  if (n_cache > 0) {
+    const int64_t a_bytes = ((R - 1) * a_stride + n_cache) * 4;
+    const int64_t o_bytes = ((R - 1) * o_stride + k) * 4;
+    if (overlap(out, o_bytes, all, a_bytes)) return CSA2_EINVAL;
+  }
+  clear_stale_error();
+  return launched(csa2::launch_gather_select((int)R, all, a_stride, n_cache, q_pos, cand_blocks,
+                                             K_b, k, out, o_stride, stream));
 }
 
 int csa2_select_topk(int R, int64_t n, const float* scores, int64_t s_stride, const int32_t* ids,

@@ -42,6 +42,12 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
                               const int32_t* ids, int64_t id_stride, const int32_t* forced,
                               int force_last, int k, int32_t* out, int64_t o_stride, void* ws,
                               hipStream_t s);
+// candidate gather + position top-k in one pass (rows of 8 * K_b entries
+// taking the register-row path only)
+bool gather_select_supported(int64_t R, int64_t n);
+hipError_t launch_gather_select(int R, const float* all, int64_t a_stride, int64_t n_cache,
+                                const int64_t* q_pos, const int32_t* blocks, int K_b, int k,
+                                int32_t* out, int64_t o_stride, hipStream_t s);
 
 int attn_splits(int64_t R, int K, int W);
 size_t attn_workspace_bytes(int64_t R, int K, int W);

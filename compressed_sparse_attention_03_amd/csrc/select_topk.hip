@@ -52,6 +52,19 @@ struct SelArgs {
   int64_t o_stride;
 };
 
+// Candidates gathered on the fly (one indexer for both stages): entry j of
+// row r is latent p = 8 * blocks[r][j / 8] + j % 8 of the scan's score
+// matrix, valid when the block id is >= 0 and p < n_vis(q_pos[r]); its id is
+// p.  Used by the register-row kernel only.
+struct GatherSrc {
+  const float* all;  // [R][a_stride] scan scores
+  int64_t a_stride;
+  const int32_t* blocks;  // [R][K_b], ascending, -1 padded
+  int K_b;
+  const int64_t* q_pos;  // [R]
+  int64_t n_cache;
+};
+
 __device__ __forceinline__ uint32_t order_key(float s) {
   const uint32_t u = __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -673,7 +686,8 @@ __device__ KeyThreshold key_threshold(const T (&vals)[P], uint32_t lo_key, uint3
 // chosen ones; the ids of the chosen columns are written in column order and
 // the row is padded with -1 up to k.  1024 threads.
 __device__ __forceinline__ void read_back(const SelArgs& a, int64_t row, const KeyThreshold& th, int words,
-                          uint32_t* bitmap, const uint32_t* tiemap, Shared& sh) {
+                          uint32_t* bitmap, const uint32_t* tiemap, Shared& sh,
+                          const GatherSrc* gs = nullptr) {
   const int tid = threadIdx.x;
   // thread t owns a contiguous run of words
   const int wpt = (words + THREADS - 1) / THREADS;
@@ -708,7 +722,9 @@ __device__ __forceinline__ void read_back(const SelArgs& a, int64_t row, const K
       const int b = __ffs(bits) - 1;
       bits &= bits - 1u;
       const int64_t c = (int64_t)wi * 32 + b;
-      if (pos < (uint32_t)a.k) orow[pos] = a.ids ? a.ids[row * a.id_stride + c] : (int32_t)c;
+      if (pos < (uint32_t)a.k)
+        orow[pos] = gs ? gs->blocks[row * gs->K_b + (c >> 3)] * BLK + (int32_t)(c & 7)
+                       : (a.ids ? a.ids[row * a.id_stride + c] : (int32_t)c);
       ++pos;
     }
   }
@@ -1049,8 +1065,51 @@ __device__ __forceinline__ void load_row_keys(const SelArgs& a, int64_t row, int
   *n_valid = nv;
 }
 
+// The row's keys from the scan's score matrix through its block list (see
+// GatherSrc): the block ids first, then the scores of the visible latents,
+// 16 entries at a time.  No forced entry in this mode.
 template <int E>
-__global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
+__device__ __forceinline__ void load_row_keys_gather(const SelArgs& a, const GatherSrc& gs,
+                                                     int64_t row, uint32_t (&key)[E],
+                                                     int32_t* last_valid, uint32_t* n_valid) {
+  const int tid = threadIdx.x;
+  const int n = (int)a.n;
+  const int64_t t = gs.q_pos[row];
+  const int64_t nvis = t < 0 ? 0 : min((t + 1) >> 1, gs.n_cache);
+  const int32_t* brow = gs.blocks + row * gs.K_b;
+  const float* srow = gs.all + row * gs.a_stride;
+  constexpr int G = E > 16 ? 16 : E;
+  int32_t lv = -1;
+  uint32_t nv = 0;
+#pragma unroll
+  for (int g = 0; g < E; g += G) {
+    int64_t p[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = (g + u) * THREADS + tid;
+      const int32_t blk = j < n ? brow[j >> 3] : -1;
+      p[u] = blk >= 0 ? (int64_t)blk * BLK + (j & 7) : -1;
+    }
+    float sc[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) sc[u] = (p[u] >= 0 && p[u] < nvis) ? srow[p[u]] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int j = (g + u) * THREADS + tid;
+      const bool ok = !(sc[u] != sc[u]) && sc[u] != -INFINITY;
+      key[g + u] = ok ? order_key(sc[u]) : 0u;
+      if (ok) {
+        lv = j;
+        ++nv;
+      }
+    }
+  }
+  *last_valid = lv;
+  *n_valid = nv;
+}
+
+template <int E, bool GATHER>
+__global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a, GatherSrc gs) {
   __shared__ RowsSmem<E> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -1058,9 +1117,10 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
 
   // ---- 1 -------------------------------------------------------------------
   uint32_t key[E];
-  int32_t lv, ff;
+  int32_t lv, ff = 0x7fffffff;
   uint32_t nv;
-  if (a.ids) load_row_keys<E, true>(a, row, fid, key, &lv, &ff, &nv);
+  if (GATHER) load_row_keys_gather<E>(a, gs, row, key, &lv, &nv);
+  else if (a.ids) load_row_keys<E, true>(a, row, fid, key, &lv, &ff, &nv);
   else load_row_keys<E, false>(a, row, fid, key, &lv, &ff, &nv);
   lv = wave_max_i(lv);
   ff = wave_min_i(ff);
@@ -1211,7 +1271,7 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a) {
   }
   __syncthreads();
   read_back(a, row, th, (int)((a.n + 31) / 32), reinterpret_cast<uint32_t*>(sm.bitmap),
-            reinterpret_cast<const uint32_t*>(sm.tiemap), sm.sh);
+            reinterpret_cast<const uint32_t*>(sm.tiemap), sm.sh, GATHER ? &gs : nullptr);
 }
 
 
@@ -1232,6 +1292,22 @@ size_t select_workspace_bytes(int64_t R, int64_t n, int64_t k) {
   return (size_t)(R * nchunks) * sizeof(Slot);
 }
 
+bool gather_select_supported(int64_t R, int64_t n) { return rows_path(R, n); }
+
+hipError_t launch_gather_select(int R, const float* all, int64_t a_stride, int64_t n_cache,
+                                const int64_t* q_pos, const int32_t* blocks, int K_b, int k,
+                                int32_t* out, int64_t o_stride, hipStream_t s) {
+  const int64_t n = (int64_t)K_b * BLK;
+  if (!rows_path(R, n)) return hipErrorInvalidValue;  // rejected before launch
+  SelArgs a{nullptr, 0, nullptr, 0, nullptr, 0, n, k, out, o_stride};
+  const GatherSrc gs{all, a_stride, blocks, K_b, q_pos, n_cache};
+  const dim3 grid((unsigned)R), block(THREADS);
+  if (n <= 8 * THREADS) hipLaunchKernelGGL((select_rows_kernel<8, true>), grid, block, 0, s, a, gs);
+  else if (n <= 16 * THREADS) hipLaunchKernelGGL((select_rows_kernel<16, true>), grid, block, 0, s, a, gs);
+  else hipLaunchKernelGGL((select_rows_kernel<32, true>), grid, block, 0, s, a, gs);
+  return hipGetLastError();
+}
+
 hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_stride,
                               const int32_t* ids, int64_t id_stride, const int32_t* forced,
                               int force_last, int k, int32_t* out, int64_t o_stride, void* ws,
@@ -1239,9 +1315,10 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
   SelArgs a{scores, s_stride, ids, id_stride, forced, force_last, n, k, out, o_stride};
   if (rows_path(R, n)) {
     const dim3 grid((unsigned)R), block(THREADS);
-    if (n <= 8 * THREADS) hipLaunchKernelGGL(select_rows_kernel<8>, grid, block, 0, s, a);
-    else if (n <= 16 * THREADS) hipLaunchKernelGGL(select_rows_kernel<16>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(select_rows_kernel<32>, grid, block, 0, s, a);
+    const GatherSrc none{};
+    if (n <= 8 * THREADS) hipLaunchKernelGGL((select_rows_kernel<8, false>), grid, block, 0, s, a, none);
+    else if (n <= 16 * THREADS) hipLaunchKernelGGL((select_rows_kernel<16, false>), grid, block, 0, s, a, none);
+    else hipLaunchKernelGGL((select_rows_kernel<32, false>), grid, block, 0, s, a, none);
     return hipGetLastError();
   }
   if (split_path(R, n, k)) {

@@ -236,6 +236,27 @@ int csa2_gather_scores(int B, int Tq, const float *all, int64_t a_stride,
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * a4 from stored scores and a5 in one pass ([NVFP4] section 3.3, as for
+ * csa2_gather_scores): the position top-k of the candidates gathered from
+ * the scan's score matrix, without materialising the candidate scores.
+ * The result equals
+ *   csa2_gather_scores(B, Tq, all, a_stride, n_cache, q_pos, cand_blocks,
+ *                      K_b, scores, ids, ...)
+ *   csa2_select_topk(B*Tq, 8*K_b, scores, .., ids, .., NULL, 0, k, out, ..)
+ * bit for bit: out int32 [B*Tq][o_stride >= k], the kept latent indices in
+ * ascending order, then -1.  all, q_pos, cand_blocks as for
+ * csa2_gather_scores (all 4-byte aligned here); out must not overlap all.
+ * Supported when a row of 8*K_b candidates is held in registers by one
+ * workgroup: 8*K_b <= 16384, or up to 32768 with B*Tq >= 256; else
+ * CSA2_EUNSUPPORTED (use the two calls above).  Precondition: block ids are
+ * -1 or < ceil(n_cache/8), a row's valid ids ascending.
+ * ---------------------------------------------------------------------- */
+int csa2_gather_select(int B, int Tq, const float *all, int64_t a_stride,
+                       int64_t n_cache, const int64_t *q_pos,
+                       const int32_t *cand_blocks, int K_b, int k, int32_t *out,
+                       int64_t o_stride, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * a3 / a5. Top-k selection  ([NVFP4] section 3.3).
  *
  * Per row r < R over entries j < n: an entry is valid when its id is >= 0

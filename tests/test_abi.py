@@ -222,6 +222,22 @@ def test_quant_nvfp4_validation(L):
     assert L.csa2_quant_nvfp4(A, _lib.F32, 4, 32, ctypes.c_void_p(0x100010), S, s) == _lib.EINVAL
 
 
+def test_gather_select_validation(L):
+    s = None
+    A, Q, BL, O = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000))
+    assert L.csa2_gather_select(0, 4, NULL, 0, 10, NULL, NULL, 1, 5, NULL, 8, s) == _lib.OK   # no rows
+    assert L.csa2_gather_select(1, 1, A, 64, 64, Q, BL, 0, 5, O, 8, s) == _lib.EINVAL         # K_b < 1
+    assert L.csa2_gather_select(1, 1, A, 64, 64, Q, BL, 2, 0, O, 8, s) == _lib.EINVAL         # k < 1
+    assert L.csa2_gather_select(1, 1, A, 64, 64, Q, BL, 2, 9, O, 8, s) == _lib.EINVAL         # o_stride < k
+    assert L.csa2_gather_select(1, 1, A, 32, 64, Q, BL, 2, 5, O, 8, s) == _lib.EINVAL         # a_stride < n
+    assert L.csa2_gather_select(1, 1, A, 64, 64, NULL, BL, 2, 5, O, 8, s) == _lib.EINVAL      # no q_pos
+    assert L.csa2_gather_select(1, 1, A, 64, 64, Q, BL, 2, 5, ctypes.c_void_p(0x400002), 8, s) == _lib.EINVAL
+    assert L.csa2_gather_select(1, 1, A, 64, 64, Q, BL, 2, 5, ctypes.c_void_p(0x100010), 8, s) == _lib.EINVAL  # overlap
+    # rows longer than one workgroup's registers: the two-call path instead
+    assert L.csa2_gather_select(1, 1, A, 64, 64, Q, BL, 2049, 5, O, 8, s) == _lib.EUNSUPPORTED
+    assert L.csa2_gather_select(1, 255, A, 64, 64, Q, BL, 4096, 5, O, 8, s) == _lib.EUNSUPPORTED
+
+
 def test_gather_scores_validation(L):
     s = None
     A, Q, BL, S, I = (ctypes.c_void_p(a) for a in (0x100000, 0x200000, 0x300000, 0x400000, 0x500000))

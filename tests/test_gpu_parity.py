@@ -166,6 +166,53 @@ def test_gather_edge_cases():
     say(f"  gather: {(want_id >= 0).sum()} present, {(want_id < 0).sum()} absent entries exact")
 
 
+@pytest.mark.parametrize("seed,R,N,K_b,k,cont", [
+    (70, 300, 40000, 2048, 512, False),   # the prefill shape: 16,384 candidates, ties
+    (71, 300, 40000, 2048, 512, True),
+    (72, 260, 30000, 3000, 700, True),    # 24,000 candidates (R >= 256: registers)
+    (73, 9, 3000, 100, 1000, False),      # fewer valid candidates than k
+    (74, 5, 20000, 2048, 64, True),
+])
+def test_gather_select_fused(seed, R, N, K_b, k, cont):
+    """The one-pass gather + position top-k equals gather_scores followed by
+    select_topk (bit for bit) and the oracle's selection over the same
+    gathered candidates: absent blocks (-1), blocks partly and wholly past a
+    query's visibility, tied and continuous scores."""
+    rng = np.random.default_rng(seed)
+    all_s = (rng.standard_normal((R, N)) if cont else rng.integers(0, 60, (R, N)) / 16.0)
+    all_s = all_s.astype(np.float32)
+    nblk = (N + 7) // 8
+    q_pos = rng.integers(2 * 8 * 40, 2 * N + 4, R).astype(np.int64)  # n_vis from 320 to N
+    blocks = np.full((R, K_b), -1, np.int32)
+    for r in range(R):
+        m = int(rng.integers(K_b // 2, K_b + 1))
+        pick = np.sort(rng.choice(nblk, min(m, nblk), replace=False))
+        blocks[r, :len(pick)] = pick
+    B = 1
+    qp = torch.from_numpy(q_pos.reshape(B, R)).cuda()
+    a_t = torch.from_numpy(all_s).cuda()
+    b_t = torch.from_numpy(blocks).cuda()
+    fused = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    api.gather_select(a_t, qp, b_t, k, fused, n_cache=N)
+    sc = torch.empty((R, K_b * 8), dtype=torch.float32, device="cuda")
+    ids = torch.empty((R, K_b * 8), dtype=torch.int32, device="cuda")
+    api.gather_scores(a_t, qp, b_t, sc, ids, n_cache=N)
+    two = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    api.select_topk(sc, k, two, ids=ids)
+    torch.cuda.synchronize()
+    got = fused.cpu().numpy()
+    assert np.array_equal(got, two.cpu().numpy()), "fused != gather + select"
+    # oracle: the same candidates gathered on the host, then the oracle's top-k
+    nv = np.minimum((q_pos + 1) // 2, N)
+    pos = blocks[:, :, None].astype(np.int64) * 8 + np.arange(8)
+    ok = (blocks[:, :, None] >= 0) & (pos < nv[:, None, None])
+    cs = np.where(ok, np.take_along_axis(all_s, np.clip(pos, 0, N - 1).reshape(R, -1), 1)
+                  .reshape(R, K_b, 8), -np.inf).reshape(R, -1).astype(np.float64)
+    cid = np.where(ok, pos, -1).reshape(R, -1).astype(np.int32)
+    assert np.array_equal(got, ref.select(cs, k, ids=cid)), "fused != oracle selection"
+    say(f"  gather+select fused: {R} rows x {K_b * 8} candidates, k={k}, bit-exact")
+
+
 @pytest.mark.parametrize("seed,R,n,k,mode", [
     (40, 5, 300, 17, "ties"), (41, 3, 65536, 2048, "last"), (42, 7, 16384, 512, "ids"),
     (43, 4, 1000, 1200, "plain"), (44, 6, 5000, 64, "forced"), (45, 2, 777, 1, "forced"),
@@ -337,9 +384,10 @@ def _compare_chain(cfg, path, res, rows):
     bm = path.block_max.cpu().numpy()[rows].astype(np.float64)
     assert np.array_equal(bm, res["block_max"]), "block max"
     assert np.array_equal(path.blocks.cpu().numpy()[rows], res["blocks"]), "blocks"
-    assert np.array_equal(path.cand_ids.cpu().numpy()[rows], res["cand_ids"]), "candidate ids"
-    assert np.array_equal(path.cand_scores.cpu().numpy()[rows].astype(np.float64),
-                          res["cand_scores"]), "candidate scores"
+    if not path.fused_gather:  # else the candidates are gathered inside the top-k
+        assert np.array_equal(path.cand_ids.cpu().numpy()[rows], res["cand_ids"]), "candidate ids"
+        assert np.array_equal(path.cand_scores.cpu().numpy()[rows].astype(np.float64),
+                              res["cand_scores"]), "candidate scores"
     assert np.array_equal(path.sel.cpu().numpy()[rows], res["sel"]), "Sel"
     check_close("chained out", bf16_to_np(path.out)[rows], res["out"], tol)
     assert np.abs(path.lse.cpu().numpy()[rows] - res["lse"]).max() < 2e-3
