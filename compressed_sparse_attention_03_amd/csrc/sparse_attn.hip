@@ -102,7 +102,6 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint16_t* lo, const uint16_t*
 }
 
 struct Smem {
-  uint16_t q[HQ][KV_LD];  // the query's 64 heads (the S^T contraction's B operand)
   uint16_t kv[TILE][KV_LD];  // the tile, row-major: QK operand, and PV operand via transpose reads
   float rscale[TILE];
   int rvalid[TILE];
@@ -142,9 +141,8 @@ __device__ __forceinline__ u32x4 nvfp4_piece(uint32_t codes, uint32_t scale_byte
   return v;
 }
 
-// One wave per SIMD: the 64 heads x 512 fp32 accumulators and the next
-// tile's rows take more than half of the register file; the query is read
-// from LDS for each tile.
+// One wave per SIMD: a wave's 16 heads x 512 fp32 accumulators, its 16 query
+// heads (QK operands) and the next tile's rows take the register file.
 template <int LF, int WF>
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -171,20 +169,14 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     sv[m] = idx < n_lat ? selrow[lat_beg + idx] : -1;
   }
 
-  // the query's 64 x 512 bf16 into LDS: thread tid moves 16 pieces of 16 B
+  // this wave's 16 heads of the query as QK operands, held in registers for
+  // all tiles (lane: head 16w + l%16, dims 32c + 8g .. +7), loaded straight
+  // from memory (every lane 16 contiguous bytes of one head)
+  bf16x8 qreg[16];
   {
-    const uint16_t* qb = a.q + (int64_t)b * a.q_sb + (int64_t)j * HQ * D;
-    u32x4 qv[16];
+    const uint16_t* qh = a.q + (int64_t)b * a.q_sb + ((int64_t)j * HQ + 16 * wave + hl) * D + 8 * g;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int piece = tid + 256 * m;  // head piece / 64, dims 8 (piece % 64)
-      qv[m] = *reinterpret_cast<const u32x4*>(qb + (piece >> 6) * D + 8 * (piece & 63));
-    }
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      const int piece = tid + 256 * m;
-      *reinterpret_cast<u32x4*>(&sm.q[piece >> 6][8 * (piece & 63)]) = qv[m];
-    }
+    for (int c = 0; c < 16; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(qh + 32 * c);
   }
 
 #pragma unroll
@@ -306,14 +298,6 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   const int trj = (lane & 15) >> 2, tra = lane & 3;
   const uint16_t* tr_lo = &sm.kv[4 * g + trj][4 * tra];
   const uint16_t* tr_hi = &sm.kv[16 + 4 * g + trj][4 * tra];
-
-  // this wave's 16 heads of the query as QK operands, held in registers for
-  // all tiles (lane: head 16w + l%16, dims 32c + 8g .. +7); read from the
-  // staged query once instead of once per tile
-  bf16x8 qreg[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c)
-    qreg[c] = *reinterpret_cast<const bf16x8*>(&sm.q[16 * wave + hl][32 * c + 8 * g]);
 
   if (tile_beg < tile_end) gather(tile_beg, nxt);
   for (int tt = tile_beg; tt < tile_end; ++tt) {
