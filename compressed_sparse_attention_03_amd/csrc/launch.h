@@ -49,7 +49,7 @@ hipError_t launch_gather_select(int R, const float* all, int64_t a_stride, int64
                                 const int64_t* q_pos, const int32_t* blocks, int K_b, int k,
                                 int32_t* out, int64_t o_stride, hipStream_t s);
 
-int attn_splits(int64_t R, int K, int W);
+int attn_splits(int64_t R, int K, int W, int lat_fmt);
 size_t attn_workspace_bytes(int64_t R, int K, int W);
 hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
                               int lat_fmt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,

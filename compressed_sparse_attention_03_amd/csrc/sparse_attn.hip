@@ -30,6 +30,7 @@
 //     whose B operand is exactly the P values the lane already holds.
 // FP8 window rows keep their per-token scale out of the MFMA: it multiplies
 // the logit of that row and its P weight.
+#include <algorithm>
 #include <atomic>
 
 #include "device_common.h"
@@ -481,29 +482,34 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 static int attn_tiles(int K, int W) { return (K + TILE - 1) / TILE + (W + TILE - 1) / TILE; }
 
 // Tiles handled by one workgroup: many query rows -> one workgroup per
-// query (no merge); few -> split the tiles so that roughly 256+ workgroups
-// run, down to one tile each (each split costs a 128 KiB fp32 partial that
-// the merge reads back, but a workgroup's gathers all start at once, and
-// one gather round is 2-4 us of latency on random latent rows).
-static int attn_tiles_per_split(int64_t R, int K, int W) {
+// query (no merge); few -> split the tiles so that roughly TARGET
+// workgroups run, down to one tile each (each split costs a 128 KiB fp32
+// partial that the merge reads back, but a workgroup's gathers all start at
+// once, and one gather round is 2-4 us of latency on random latent rows).
+// Measured: bf16 latents are fastest at ~128 workgroups (1M decode, 8
+// queries: 10 splits of 2 tiles beat 20 of 1; 40 queries: 4 splits beat 7),
+// NVFP4 latents, whose rows cost more to decode, at ~256.
+static int attn_tiles_per_split(int64_t R, int K, int W, int lat_fmt) {
   const int tiles = attn_tiles(K, W);
   if (R >= 192 || tiles <= 1) return tiles > 0 ? tiles : 1;
-  const int64_t want = (256 + R - 1) / R;  // splits wanted per query
+  const int64_t target = lat_fmt == FMT_NVFP4 ? 256 : 128;
+  const int64_t want = (target + R - 1) / R;  // splits wanted per query
   int tps = (int)((tiles + want - 1) / want);
   if (tps < 1) tps = 1;
   if ((tiles + tps - 1) / tps > MAX_SPLITS) tps = (tiles + MAX_SPLITS - 1) / MAX_SPLITS;
   return tps;
 }
 
-int attn_splits(int64_t R, int K, int W) {
+int attn_splits(int64_t R, int K, int W, int lat_fmt) {
   const int tiles = attn_tiles(K, W);
-  const int tps = attn_tiles_per_split(R, K, W);
+  const int tps = attn_tiles_per_split(R, K, W, lat_fmt);
   const int s = (tiles + tps - 1) / tps;
   return s < 1 ? 1 : s;
 }
 
+// the larger of the two formats' needs: the workspace query has no format
 size_t attn_workspace_bytes(int64_t R, int K, int W) {
-  const int s = attn_splits(R, K, W);
+  const int s = std::max(attn_splits(R, K, W, FMT_BF16), attn_splits(R, K, W, FMT_NVFP4));
   if (s <= 1) return 0;
   return (size_t)R * s * HQ * PART * sizeof(float);
 }
@@ -516,8 +522,8 @@ hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const 
                               float scale, void* out, int64_t out_sb, float* lse, void* ws,
                               hipStream_t s) {
   const int64_t R = (int64_t)B * Tq;
-  const int splits = attn_splits(R, K, W);
-  const int tiles_per_split = attn_tiles_per_split(R, K, W);
+  const int splits = attn_splits(R, K, W, lat_fmt);
+  const int tiles_per_split = attn_tiles_per_split(R, K, W, lat_fmt);
   // with an empty cache no latent row exists: its tiles are dropped (they
   // would only be masked rows, and the cache pointer may be null)
   const int tiles_lat = n_cache > 0 ? (K + TILE - 1) / TILE : 0;
