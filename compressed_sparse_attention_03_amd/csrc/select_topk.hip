@@ -19,6 +19,11 @@
 // path, so the result never depends on the sample.  Few rows: the pass is
 // spread over many workgroups (bracket / classify / finish kernels).
 //
+// Many rows (>= 1024 rows of <= 16,384 entries: the chunked prefill).  A
+// 256/512-thread workgroup per row, several per CU: exact radix threshold
+// over the bits the row's keys differ in, column bitmaps by ballot, one
+// block scan for the ordered output (select_many_kernel).
+//
 // Radix path (any n, k).  A stats pass finds the valid count, the forced
 // entry and the min / max key; radix select finds the k-th largest key T,
 // 8 bits per pass below the bits all keys share; histograms live in LDS and
@@ -1275,6 +1280,275 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a, GatherS
 }
 
 
+// ---- many rows: one 256- or 512-thread workgroup per row -------------------
+// For thousands of rows (the chunked prefill's two stages, 8192 rows) the
+// register-row kernel's latency chain (16 waves, a dozen barrier-separated
+// phases per row) leaves the CUs waiting; a smaller workgroup per row lets
+// several rows share a CU and keeps the instruction count per entry low:
+//  1. the row in registers, entry c = e * MT + t of thread t (coalesced; in
+//     gather mode the block list is staged in LDS first, so all score loads
+//     of the row go out in one round through a buffer resource);
+//  2. the k-th key exactly by radix over the bits in which the valid keys
+//     differ (AND / OR of the keys first), 11-bit digits counted in an LDS
+//     histogram: with integer-valued scores ~16 bits differ, two passes;
+//  3. one ballot per (entry, wave) writes the "above" and "tied" bits of 64
+//     consecutive columns; each thread then owns one 64-column word, one
+//     block scan of the packed (above, tied) counts gives its output offset
+//     and how many ties precede it, and it writes its chosen ids in column
+//     order (ties go to the smaller columns).
+constexpr int MBIN = 2048;                   // radix digit bins (11 bits)
+constexpr int SEL_BUF_DWORD3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+
+template <int MT, int E, bool GATHER>
+struct ManySmem {
+  Shared sh;
+  uint32_t hist[MBIN];
+  uint64_t above[E * (MT / 64)];  // word e * NW + wave: columns e * MT + 64 * wave + [0, 64)
+  uint64_t tied[E * (MT / 64)];
+  uint32_t fb[4];                 // wave_find_bin result
+  int32_t blk[GATHER ? E * MT / BLK : 1];  // the row's block list (gather mode)
+};
+
+template <int MT, int E, bool GATHER, bool IDS>
+__global__ __launch_bounds__(MT) void select_many_kernel(SelArgs a, GatherSrc gs) {
+  __shared__ ManySmem<MT, E, GATHER> sm;
+  constexpr int NW = MT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int n = (int)a.n;
+  const int32_t fid = (!GATHER && a.forced) ? a.forced[row] : -1;
+
+  // ---- 1: keys --------------------------------------------------------------
+  uint32_t key[E];
+  int32_t lv = -1, ff = 0x7fffffff;
+  uint32_t nv = 0;
+  if (GATHER) {
+    // the block list to LDS first, so that every score load of the row is
+    // issued in one round (positions from LDS, no dependent global loads)
+    const int64_t t = gs.q_pos[row];
+    const int32_t nvis = (int32_t)(t < 0 ? 0 : min((t + 1) >> 1, gs.n_cache));
+    const int32_t* brow = gs.blocks + row * gs.K_b;
+    const float* srow = gs.all + row * gs.a_stride;
+    const int nb = (n + BLK - 1) / BLK;  // <= K_b
+    for (int i = tid; i < nb; i += MT) sm.blk[i] = brow[i];
+    __syncthreads();
+    // the row's visible scores as one buffer resource: 32-bit lane offsets
+    // (one register per load instead of a 64-bit address), clipped to n_vis
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(srow), (short)0, (int)(nvis * 4), SEL_BUF_DWORD3);
+    uint64_t okm = 0ull;  // entry e visible: bit e (one register pair, not E flags)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = e * MT + tid;
+      const int32_t blk = c < n ? sm.blk[c >> 3] : -1;
+      const bool ok = blk >= 0 && (int64_t)blk * BLK + (c & 7) < nvis;  // any caller block id is safe
+      const uint32_t off = ok ? ((uint32_t)blk * (uint32_t)BLK + (uint32_t)(c & 7)) << 2 : 0u;
+      key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+      okm |= (uint64_t)ok << e;
+    }
+    // branch-free (a branch per entry made the compiler copy the whole key
+    // array around each one)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t u = key[e];
+      const bool ok = ((okm >> e) & 1ull) && u != 0xff800000u && (u & 0x7fffffffu) <= 0x7f800000u;
+      key[e] = ok ? order_key(__uint_as_float(u)) : 0u;
+      lv = ok ? e * MT + tid : lv;
+      nv += ok ? 1u : 0u;
+    }
+  } else {
+    const float* srow = a.scores + row * a.s_stride;
+    const int32_t* irow = IDS ? a.ids + row * a.id_stride : nullptr;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(srow), (short)0, n * 4, SEL_BUF_DWORD3);
+    // (without ids the row's own scores stand in, never read)
+    const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+        IDS ? (void*)const_cast<int32_t*>(irow) : (void*)const_cast<float*>(srow), (short)0, n * 4,
+        SEL_BUF_DWORD3);
+    constexpr int G = (IDS && E > 16) ? 16 : E;
+#pragma unroll
+    for (int g = 0; g < E; g += G) {
+      float sc[G];
+      int32_t id[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int c = (g + u) * MT + tid;
+        const uint32_t off = (uint32_t)c << 2;  // past the row: reads as 0, masked here
+        const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+        sc[u] = c < n ? v : -INFINITY;
+        if (IDS) {
+          const int32_t x = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0);
+          id[u] = c < n ? x : -1;
+        } else {
+          id[u] = c;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int c = (g + u) * MT + tid;
+        const bool ok = id[u] >= 0 && !(sc[u] != sc[u]) && sc[u] != -INFINITY;
+        key[g + u] = ok ? order_key(sc[u]) : 0u;
+        lv = ok ? c : lv;  // c grows with g + u
+        nv += ok ? 1u : 0u;
+        ff = (ok && fid >= 0 && id[u] == fid && c < ff) ? c : ff;
+      }
+    }
+  }
+  lv = wave_max_i(lv);
+  ff = wave_min_i(ff);
+  nv = wave_sum(nv);
+  if (lane == 0) {
+    sm.sh.wred[0 * NW + wave] = (uint32_t)lv;
+    sm.sh.wred[1 * NW + wave] = (uint32_t)ff;
+    sm.sh.wred[2 * NW + wave] = nv;
+  }
+  __syncthreads();
+  lv = (int32_t)waves_combine(sm.sh.wred + 0 * NW, NW, 0xffffffffu, [](uint32_t x, uint32_t y) {
+    return (int32_t)x > (int32_t)y ? x : y;
+  });
+  ff = (int32_t)waves_combine(sm.sh.wred + 1 * NW, NW, 0x7fffffffu, [](uint32_t x, uint32_t y) {
+    return (int32_t)x < (int32_t)y ? x : y;
+  });
+  nv = waves_combine(sm.sh.wred + 2 * NW, NW, 0u, [](uint32_t x, uint32_t y) { return x + y; });
+  int32_t fcol = -1;
+  if (a.force_last) fcol = lv;
+  else if (fid >= 0 && ff != 0x7fffffff) fcol = ff;
+  // the forced entry leaves the ranking and comes back as an "above" bit
+#pragma unroll
+  for (int e = 0; e < E; ++e) key[e] = (e * MT + tid == fcol) ? 0u : key[e];
+  const uint32_t k_rem = (uint32_t)a.k - (fcol >= 0 ? 1u : 0u);
+  const uint32_t n_rest = nv - (fcol >= 0 ? 1u : 0u);
+
+  // ---- 2: threshold key T and the number of ties at T to take --------------
+  uint32_t T = 0u, need = 0u;  // T = 0, need = 0: every valid key (key > 0)
+  if (n_rest > k_rem && k_rem == 0u) {
+    T = 0xffffffffu;  // above every key: only the forced entry
+  } else if (n_rest > k_rem) {
+    uint32_t kand = 0xffffffffu, kor = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (key[e] != 0u) {
+        kand &= key[e];
+        kor |= key[e];
+      }
+    kand = wave_and(kand);
+    kor = wave_or(kor);
+    __syncthreads();  // wred reused
+    if (lane == 0) {
+      sm.sh.wred[0 * NW + wave] = kand;
+      sm.sh.wred[1 * NW + wave] = kor;
+    }
+    __syncthreads();
+    kand = waves_combine(sm.sh.wred + 0 * NW, NW, 0xffffffffu, [](uint32_t x, uint32_t y) { return x & y; });
+    kor = waves_combine(sm.sh.wred + 1 * NW, NW, 0u, [](uint32_t x, uint32_t y) { return x | y; });
+    const uint32_t diff = kand ^ kor;
+    if (diff == 0u) {  // every valid key equal
+      T = kand;
+      need = k_rem;
+    } else {
+      const int hb = 31 - __clz(diff), lb = __ffs(diff) - 1;
+      uint32_t prefix = hb == 31 ? 0u : (kand & ~((2u << hb) - 1u));
+      uint32_t rem = k_rem;
+      int hi = hb, lo;
+      while (true) {
+        lo = hi - 10 > 0 ? hi - 10 : 0;
+        const uint32_t dmask = (2u << (hi - lo)) - 1u;  // hi - lo <= 10
+        for (int i = tid; i < MBIN; i += MT) sm.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool match = key[e] != 0u && (hi == 31 || (key[e] >> (hi + 1)) == (prefix >> (hi + 1)));
+          if (match) atomicAdd(&sm.hist[(key[e] >> lo) & dmask], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) wave_find_bin<MBIN>(sm.hist, rem, sm.fb);
+        __syncthreads();
+        const uint32_t d = sm.fb[0], above = sm.fb[1];
+        prefix |= d << lo;
+        rem -= above;
+        if (lo <= lb) break;
+        hi = lo - 1;
+      }
+      // bits below the last digit are the same in every valid key
+      prefix |= kand & ((1u << lo) - 1u);
+      T = prefix;
+      need = rem;
+    }
+  }
+
+  // ---- 3: column bitmaps, ordered output -------------------------------------
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool up = key[e] > T || e * MT + tid == fcol;
+    const bool tie = need > 0u && key[e] == T;
+    const uint64_t mu = __ballot(up), mt = __ballot(tie);
+    if (lane == 0) {
+      sm.above[e * NW + wave] = mu;
+      sm.tied[e * NW + wave] = mt;
+    }
+  }
+  __syncthreads();
+  const int nwords = (n + 63) >> 6;  // <= E * NW = MT * E / 64
+  static_assert(E * NW <= MT, "one bitmap word per thread");
+  const int w = tid;
+  uint64_t mu = 0ull, mt = 0ull;
+  if (w < nwords) {
+    mu = sm.above[w];
+    mt = sm.tied[w];
+  }
+  const uint32_t cu = (uint32_t)__popcll(mu), ct = (uint32_t)__popcll(mt);
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan((cu << 16) | ct, sm.sh, &tot);
+  const uint32_t t_before = before & 0xffffu;
+  uint32_t take = need > t_before ? need - t_before : 0u;
+  uint64_t chosen = mu;
+  for (uint64_t m = mt; m && take; --take) {
+    const uint64_t low = m & (~m + 1ull);  // lowest set bit: smallest tied column
+    chosen |= low;
+    m ^= low;
+  }
+  uint32_t pos = (before >> 16) + (t_before < need ? t_before : need);
+  int32_t* orow = a.out + row * a.o_stride;
+  if (chosen) {
+    const int32_t* irow = IDS ? a.ids + row * a.id_stride : nullptr;
+    for (uint64_t m = chosen; m; m &= m - 1ull) {
+      const int b = __ffsll((unsigned long long)m) - 1;
+      const int word_col = 64 * (w & (NW - 1)) + MT * (w / NW);  // first column of word w
+      const int c = word_col + b;
+      int32_t id;
+      if (GATHER) id = sm.blk[c >> 3] * BLK + (c & 7);
+      else if (IDS) id = irow[c];
+      else id = c;
+      if (pos < (uint32_t)a.k) orow[pos] = id;  // never more than k (bounds guard)
+      ++pos;
+    }
+  }
+  const uint32_t total = (tot >> 16) + ((tot & 0xffffu) < need ? (tot & 0xffffu) : need);
+  for (int j = (int)total + tid; j < a.k; j += MT) orow[j] = -1;
+}
+
+template <int MT, int E, bool GATHER, bool IDS>
+void launch_many_cfg(int R, const SelArgs& a, const GatherSrc& gs, hipStream_t s) {
+  hipLaunchKernelGGL((select_many_kernel<MT, E, GATHER, IDS>), dim3((unsigned)R), dim3(MT), 0, s, a, gs);
+}
+
+// (threads, entries per thread) by row length on the many-rows path.  Measured
+// on the 8192-row prefill stages: 512 threads beat 256 (fewer entries per
+// thread, 4 workgroups per CU at n = 4608, 2 at n = 16,384) and 1024.
+template <bool GATHER, bool IDS>
+void launch_many(int R, int64_t n, const SelArgs& a, const GatherSrc& gs, hipStream_t s) {
+  if (n <= 2048) launch_many_cfg<256, 8, GATHER, IDS>(R, a, gs, s);
+  else if (n <= 4096) launch_many_cfg<256, 16, GATHER, IDS>(R, a, gs, s);
+  else if (n <= 6144) launch_many_cfg<512, 12, GATHER, IDS>(R, a, gs, s);
+  else if (n <= 8192) launch_many_cfg<512, 16, GATHER, IDS>(R, a, gs, s);
+  else if (n <= 12288) launch_many_cfg<512, 24, GATHER, IDS>(R, a, gs, s);
+  else launch_many_cfg<512, 32, GATHER, IDS>(R, a, gs, s);
+}
+
+// Rows enough to give every CU several workgroups of the many-rows kernel.
+constexpr int MANY_ROWS = 1024;
+bool many_path(int64_t R, int64_t n) { return R >= MANY_ROWS && n <= 16384; }
+
 // Path choice.  One CU works through a register-held row at a few entries
 // per lane-cycle, so a row of more than 16K entries is faster spread over
 // many workgroups (split path) when there are too few rows to fill the chip.
@@ -1301,6 +1575,10 @@ hipError_t launch_gather_select(int R, const float* all, int64_t a_stride, int64
   if (!rows_path(R, n)) return hipErrorInvalidValue;  // rejected before launch
   SelArgs a{nullptr, 0, nullptr, 0, nullptr, 0, n, k, out, o_stride};
   const GatherSrc gs{all, a_stride, blocks, K_b, q_pos, n_cache};
+  if (many_path(R, n)) {
+    launch_many<true, false>(R, n, a, gs, s);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)R), block(THREADS);
   if (n <= 8 * THREADS) hipLaunchKernelGGL((select_rows_kernel<8, true>), grid, block, 0, s, a, gs);
   else if (n <= 16 * THREADS) hipLaunchKernelGGL((select_rows_kernel<16, true>), grid, block, 0, s, a, gs);
@@ -1313,6 +1591,12 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
                               int force_last, int k, int32_t* out, int64_t o_stride, void* ws,
                               hipStream_t s) {
   SelArgs a{scores, s_stride, ids, id_stride, forced, force_last, n, k, out, o_stride};
+  if (many_path(R, n)) {
+    const GatherSrc none{};
+    if (ids) launch_many<false, true>(R, n, a, none, s);
+    else launch_many<false, false>(R, n, a, none, s);
+    return hipGetLastError();
+  }
   if (rows_path(R, n)) {
     const dim3 grid((unsigned)R), block(THREADS);
     const GatherSrc none{};

@@ -172,12 +172,14 @@ def test_gather_edge_cases():
     (72, 260, 30000, 3000, 700, True),    # 24,000 candidates (R >= 256: registers)
     (73, 9, 3000, 100, 1000, False),      # fewer valid candidates than k
     (74, 5, 20000, 2048, 64, True),
+    (75, 1100, 40000, 2048, 512, False),  # 1024+ rows: the many-rows kernel
+    (76, 1100, 37000, 1000, 300, True),
 ])
 def test_gather_select_fused(seed, R, N, K_b, k, cont):
     """The one-pass gather + position top-k equals gather_scores followed by
     select_topk (bit for bit) and the oracle's selection over the same
     gathered candidates: absent blocks (-1), blocks partly and wholly past a
-    query's visibility, tied and continuous scores."""
+    query's visibility (ids up to INT32_MAX), tied and continuous scores."""
     rng = np.random.default_rng(seed)
     all_s = (rng.standard_normal((R, N)) if cont else rng.integers(0, 60, (R, N)) / 16.0)
     all_s = all_s.astype(np.float32)
@@ -188,6 +190,9 @@ def test_gather_select_fused(seed, R, N, K_b, k, cont):
         m = int(rng.integers(K_b // 2, K_b + 1))
         pick = np.sort(rng.choice(nblk, min(m, nblk), replace=False))
         blocks[r, :len(pick)] = pick
+        if len(pick) + 3 <= K_b:
+            # ids past the cache, up to INT32_MAX (latent ids beyond 2^31): never read
+            blocks[r, len(pick):len(pick) + 3] = [1 << 28, 1 << 30, 2**31 - 1]
     B = 1
     qp = torch.from_numpy(q_pos.reshape(B, R)).cuda()
     a_t = torch.from_numpy(all_s).cuda()
@@ -258,6 +263,56 @@ def test_select_edge_cases(seed, R, n, k, mode):
                            for r in range(R)], np.int32)
     exp = ref.select(scores.astype(np.float64), k, ids=ids, forced=forced)
     assert np.array_equal(out.cpu().numpy(), exp)
+
+
+@pytest.mark.parametrize("seed,n,k,mode", [
+    # 1024+ rows take the 256-thread many-rows kernel (8 to 64 entries per
+    # thread): integer ties, signed scores, continuous scores, all keys equal,
+    # forced ids (k = 1 keeps only the forced one), the last valid entry kept,
+    # fewer valid entries than k, ids
+    (80, 4608, 2048, "last"), (81, 16384, 512, "ties"), (82, 16384, 512, "ids"),
+    (83, 2000, 64, "signed"), (84, 3000, 1, "forced"), (85, 6000, 700, "cont_forced"),
+    (86, 12000, 2048, "allequal"), (87, 700, 900, "plain"), (88, 1, 1, "plain"),
+    (89, 257, 256, "last"), (90, 8192, 2048, "cont"), (91, 5000, 4999, "signed"),
+])
+def test_select_many_rows(seed, n, k, mode):
+    """Thousands of rows (the chunked prefill's shape) against the oracle's
+    selection, bit for bit."""
+    R = 1100
+    rng = np.random.default_rng(seed)
+    scores = rng.integers(0, 40, (R, n)).astype(np.float32) / 16
+    if mode.startswith("cont"):
+        scores = rng.standard_normal((R, n)).astype(np.float32)
+    if mode == "signed":
+        scores = rng.integers(-20, 21, (R, n)).astype(np.float32) / 16
+    if mode == "allequal":
+        scores[:] = 1.5
+    scores[rng.random((R, n)) < 0.07] = -np.inf
+    scores[0, :5] = np.nan
+    scores[1, :] = -np.inf                       # a row with nothing valid
+    scores[2, rng.random(n) < 0.9] = -np.inf     # a row with few valid entries
+    ids = None
+    if mode == "ids":
+        ids = np.tile((np.arange(n) * 2 + 1).astype(np.int32), (R, 1))
+        ids[rng.random((R, n)) < 0.05] = -1
+    forced = None
+    if mode in ("forced", "cont_forced"):
+        forced = rng.integers(0, n, R).astype(np.int32)
+        forced[0] = -1
+    out = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    api.select_topk(torch.from_numpy(scores).cuda(), k, out,
+                    ids=None if ids is None else torch.from_numpy(ids).cuda(),
+                    forced=None if forced is None else torch.from_numpy(forced).cuda(),
+                    force_last=(mode == "last"))
+    torch.cuda.synchronize()
+    if mode == "last":
+        fin = np.isfinite(scores)
+        forced = np.where(fin.any(1), n - 1 - np.argmax(fin[:, ::-1], 1), -1).astype(np.int32)
+    exp = ref.select(scores.astype(np.float64), k, ids=ids, forced=forced)
+    got = out.cpu().numpy()
+    bad = np.nonzero((got != exp).any(1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first {bad[:5].tolist()}"
+    say(f"  many-rows select: {R} rows x {n}, k={k} ({mode}) bit-exact")
 
 
 @pytest.mark.parametrize("name,kw,tol", [
