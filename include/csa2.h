@@ -192,8 +192,9 @@ int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
  *             of the block's visible scores, -inf for blocks with none
  *   cand_blocks, K_b, ids_out are ignored.  At least one output is needed.
  * mode CSA2_SCORES_CAND: only the latents of the chosen blocks are scored;
- *   cand_blocks : int32 [B*Tq][K_b] block ids, -1 = none.  Precondition:
- *             ids are -1 or < ceil(n_cache/8).
+ *   cand_blocks : int32 [B*Tq][K_b] block ids, -1 = none; an id at or
+ *             past ceil(n_cache/8) names latents that are not visible
+ *             (score -inf, id -1; nothing past the cache is read).
  *   scores    : f32 [B*Tq][s_stride >= 8*K_b]; column 8j+i scores latent
  *             8*cand_blocks[j]+i;
  *   ids_out   : int32 [B*Tq][s_stride], that latent's index, or -1 (score
@@ -227,7 +228,7 @@ int csa2_index_scores(int mode, int B, int Tq, const void *q, csa2_dtype q_dt,
  *                latent is not visible (n_vis of the query's position)
  *   ids_out    : int32, same shape, that latent's index or -1
  *   scores and ids_out 16-byte aligned, s_stride % 4 == 0, no overlap.
- * Precondition: block ids are -1 or < ceil(n_cache/8).
+ * Block ids at or past ceil(n_cache/8) count as not visible (never read).
  * ---------------------------------------------------------------------- */
 int csa2_gather_scores(int B, int Tq, const float *all, int64_t a_stride,
                        int64_t n_cache, const int64_t *q_pos,
@@ -248,8 +249,9 @@ int csa2_gather_scores(int B, int Tq, const float *all, int64_t a_stride,
  * csa2_gather_scores (all 4-byte aligned here); out must not overlap all.
  * Supported when a row of 8*K_b candidates is held in registers by one
  * workgroup: 8*K_b <= 16384, or up to 32768 with B*Tq >= 256; else
- * CSA2_EUNSUPPORTED (use the two calls above).  Precondition: block ids are
- * -1 or < ceil(n_cache/8), a row's valid ids ascending.
+ * CSA2_EUNSUPPORTED (use the two calls above).  Block ids at or past
+ * ceil(n_cache/8) count as not visible (never read).  Precondition: a row's
+ * valid block ids ascending.
  * ---------------------------------------------------------------------- */
 int csa2_gather_select(int B, int Tq, const float *all, int64_t a_stride,
                        int64_t n_cache, const int64_t *q_pos,

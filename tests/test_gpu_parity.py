@@ -137,8 +137,9 @@ def test_scan_cand_select_stages(name, kw):
 
 
 def test_gather_edge_cases():
-    """Candidate gather from stored scores on the cases the selection rarely
-    produces: block ids of -1, blocks partly or wholly past a query's horizon
+    """Candidate gather from stored scores, and the candidate indexer, on the
+    cases the selection rarely produces: block ids of -1, ids past the cache
+    (up to INT32_MAX), blocks partly or wholly past a query's horizon
     (t = 0, 1, 2, 17), a cache whose last block is partial (N = 1003), and the
     matrix read from an oracle scan.  Expected: the oracle's candidate indexer
     over the same blocks."""
@@ -152,6 +153,8 @@ def test_gather_edge_cases():
     blocks = np.sort(rng.choice(nblk, (cfg.R, cfg.K_b), replace=True), axis=1).astype(np.int32)
     blocks[:, -1] = nblk - 1            # the partial last block
     blocks[:, ::7] = -1                 # absent entries
+    blocks[:, 3] = 2**31 - 1            # ids past the cache: never read
+    blocks[:, 5] = nblk + 1000
     N4 = (cfg.N + 3) // 4 * 4
     all_s = np.full((cfg.R, N4), np.nan, np.float32)  # padding is never read
     all_s[:, :cfg.N] = sc_ref
@@ -163,6 +166,13 @@ def test_gather_edge_cases():
     want_s, want_id = ref.cand(host["qs"], host["ws"], host["ks"], q_pos, blocks)
     assert np.array_equal(ids.cpu().numpy(), want_id)
     assert np.array_equal(out.cpu().numpy().astype(np.float64), want_s)
+    # the candidate indexer scoring the same blocks itself (CAND mode)
+    out2, ids2 = torch.empty_like(out), torch.empty_like(ids)
+    api.index_cand(inp["qs"], inp["ws"], inp["ks"], torch.from_numpy(q_pos).cuda(),
+                   torch.from_numpy(blocks).cuda(), out2, ids2)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids2.cpu().numpy(), want_id)
+    assert np.array_equal(out2.cpu().numpy().astype(np.float64), want_s)
     say(f"  gather: {(want_id >= 0).sum()} present, {(want_id < 0).sum()} absent entries exact")
 
 
