@@ -19,11 +19,11 @@
 // path, so the result never depends on the sample.  Few rows: the pass is
 // spread over many workgroups (bracket / classify / finish kernels).
 //
-// Many rows (>= 1024 rows of <= 16,384 entries: the chunked prefill), and
-// fewer rows of 8K-16K entries (1024 threads, one row per CU).  A
-// 256/512-thread workgroup per row, several per CU: exact radix threshold
-// over the bits the row's keys differ in, column bitmaps by ballot, one
-// block scan for the ordered output (select_many_kernel).
+// Radix rows (>= 1024 rows of <= 16,384 entries: the chunked prefill, a
+// 256/512-thread workgroup per row, several per CU; fewer rows of 8K-16K
+// entries: 1024 threads, one row per CU): exact radix threshold over the
+// bits the row's keys differ in, column bitmaps by ballot, one block scan
+// for the ordered output (select_many_kernel).
 //
 // Radix path (any n, k).  A stats pass finds the valid count, the forced
 // entry and the min / max key; radix select finds the k-th largest key T,
@@ -1281,11 +1281,13 @@ __global__ __launch_bounds__(THREADS) void select_rows_kernel(SelArgs a, GatherS
 }
 
 
-// ---- many rows: one 256- or 512-thread workgroup per row -------------------
+// ---- radix rows: one 256-, 512- or 1024-thread workgroup per row -----------
 // For thousands of rows (the chunked prefill's two stages, 8192 rows) the
 // register-row kernel's latency chain (16 waves, a dozen barrier-separated
 // phases per row) leaves the CUs waiting; a smaller workgroup per row lets
-// several rows share a CU and keeps the instruction count per entry low:
+// several rows share a CU and keeps the instruction count per entry low.
+// With 1024 threads it also serves few rows of 8K-16K entries (the decodes'
+// position stage), one row per CU, where it beats the sampled bracket:
 //  1. the row in registers, entry c = e * MT + t of thread t (coalesced; in
 //     gather mode the block list is staged in LDS first, so all score loads
 //     of the row go out in one round through a buffer resource);
