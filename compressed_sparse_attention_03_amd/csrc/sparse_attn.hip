@@ -487,7 +487,8 @@ static int attn_tiles(int K, int W) { return (K + TILE - 1) / TILE + (W + TILE -
 // partial that the merge reads back, but a workgroup's gathers all start at
 // once, and one gather round is 2-4 us of latency on random latent rows).
 // Measured: bf16 latents are fastest at ~128 workgroups (1M decode, 8
-// queries: 10 splits of 2 tiles beat 20 of 1; 40 queries: 4 splits beat 7),
+// queries: 10 splits of 2 tiles beat 20 of 1, 7 of 3 and 5 of 4; 40
+// queries: 4 splits beat 7 and 2),
 // NVFP4 latents, whose rows cost more to decode, at ~256.
 static int attn_tiles_per_split(int64_t R, int K, int W, int lat_fmt) {
   const int tiles = attn_tiles(K, W);
