@@ -90,6 +90,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_TAU = 11.5f;  // largest log2-weight above the reference point
 constexpr int SEL_CAP = 2048;       // largest K: a split's sel entries are cached in LDS
+constexpr int DIRECT_MIN_TILES = 10;  // tiles per workgroup from which bf16 rows go straight to LDS
 
 // 8 bf16 of the PV contraction's A operand from two LDS transpose reads
 // (4 values each) of the row-major tile.
@@ -103,9 +104,12 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint16_t* lo, const uint16_t*
 }
 
 struct Smem {
-  uint16_t kv[TILE][KV_LD];  // the tile, row-major: QK operand, and PV operand via transpose reads
-  float rscale[TILE];
-  int rvalid[TILE];
+  // the tile, row-major: QK operand, and PV operand via transpose reads;
+  // two buffers when rows move straight from memory into LDS (bf16 caches),
+  // else only the first is used
+  uint16_t kv[2][TILE][KV_LD];
+  float rscale[2][TILE];
+  int rvalid[2][TILE];
   int32_t selc[SEL_CAP];  // sel[lat_beg ..] of this workgroup's latent rows
 };
 
@@ -144,11 +148,23 @@ __device__ __forceinline__ u32x4 nvfp4_piece(uint32_t codes, uint32_t scale_byte
 
 // One wave per SIMD: a wave's 16 heads x 512 fp32 accumulators, its 16 query
 // heads (QK operands) and the next tile's rows take the register file.
-template <int LF, int WF>
+// DIRECT (bf16 latents and window only): rows move straight from memory
+// into a double-buffered LDS tile instead of through registers.  The
+// compiler cannot tell the two buffers apart and waits for the next tile's
+// loads before reading the current one, so the next tile's gather does not
+// overlap the current tile's compute; what it saves (the staging registers,
+// the masking and LDS stores, one barrier per tile) pays off when a
+// workgroup walks many tiles (prefill, 20 per query: 1.38 -> 1.16 ms), not
+// when it walks a few (1M decode, 2: 18.5 -> 20.4 us; 128K and
+// verification decodes, 5: 25.9 -> 29.8 and 29.5 -> 33.2 us), so the
+// launcher picks by tiles per split.
+template <int LF, int WF, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
+  static_assert(!DIRECT || (LF == FMT_BF16 && WF == FMT_BF16), "direct rows are bf16 rows");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane & 15, g = lane >> 4;
   const int64_t r = blockIdx.x;  // query row b*Tq + j
   const int split = blockIdx.y;
@@ -280,13 +296,49 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       const int p = p0 + 32 * pp;
 #pragma unroll
       for (int x = 0; x < 4; ++x)
-        *reinterpret_cast<u32x4*>(&sm.kv[4 * rq + x][8 * p]) = decoded(st, pp, x);
+        *reinterpret_cast<u32x4*>(&sm.kv[0][4 * rq + x][8 * p]) = decoded(st, pp, x);
     }
     if (wave == 0 && lane < 32 && (lane & 3) == 0) {  // one lane per row quad (rq = 0..7)
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        sm.rscale[4 * rq + x] = st.ok[x] ? st.rs[x] : 1.0f;
-        sm.rvalid[4 * rq + x] = st.ok[x];
+        sm.rscale[0][4 * rq + x] = st.ok[x] ? st.rs[x] : 1.0f;
+        sm.rvalid[0][4 * rq + x] = st.ok[x];
+      }
+    }
+  };
+  // bf16 caches: wave w moves rows 8w .. 8w+7 of tile tt straight from
+  // memory into LDS buffer buf, one global_load_lds_dwordx4 per row (lane l
+  // carries bytes 16l .. 16l+15 of the 1 KiB row, measured), with no
+  // register staging; rows that do not exist are zero-filled by LDS stores.
+  // A row's source is the same for the whole wave (scalar registers).
+  auto gather_direct = [&](int tt, int buf) {
+    const bool lat_tile = tt < a.tiles_lat;
+#pragma unroll
+    for (int x = 0; x < TILE / 4; ++x) {
+      const int rl = (TILE / 4) * wave + x;
+      const uint16_t* src;
+      bool ok;
+      if (lat_tile) {
+        const int i = TILE * tt + rl;
+        const int32_t gidx = __builtin_amdgcn_readfirstlane(i < a.K ? sm.selc[i - lat_beg] : -1);
+        ok = gidx >= 0 && gidx < a.n_cache;
+        src = static_cast<const uint16_t*>(a.lat) + ((int64_t)b * a.lat_sb + (ok ? gidx : 0)) * D;
+      } else {
+        const int jw = TILE * (tt - a.tiles_lat) + rl;
+        ok = jw < a.W && w0 + jw >= 0;
+        int sl = wslot0 + jw;
+        sl = sl >= a.W_cap ? sl - a.W_cap : sl;
+        src = static_cast<const uint16_t*>(a.win) + ((int64_t)b * a.win_sb + (ok ? sl : 0)) * D;
+      }
+      uint16_t* dst = &sm.kv[buf][rl][0];
+      if (ok)
+        __builtin_amdgcn_global_load_lds(src + 8 * lane, (__attribute__((address_space(3))) void*)dst,
+                                         16, 0, 0);
+      else
+        *reinterpret_cast<u32x4*>(dst + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
+      if (lane == 0) {
+        sm.rvalid[buf][rl] = ok;
+        sm.rscale[buf][rl] = 1.0f;
       }
     }
   };
@@ -297,15 +349,29 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // addresses dims 16T + 4a .. +3 of row 4g + j (k-slots 0-3) and of row
   // 16 + 4g + j (k-slots 4-7), and every lane gets its dim's 8 rows.
   const int trj = (lane & 15) >> 2, tra = lane & 3;
-  const uint16_t* tr_lo = &sm.kv[4 * g + trj][4 * tra];
-  const uint16_t* tr_hi = &sm.kv[16 + 4 * g + trj][4 * tra];
 
-  if (tile_beg < tile_end) gather(tile_beg, nxt);
+  if (tile_beg < tile_end) {
+    if constexpr (DIRECT) gather_direct(tile_beg, 0);
+    else gather(tile_beg, nxt);
+  }
   for (int tt = tile_beg; tt < tile_end; ++tt) {
-    __syncthreads();  // previous tile fully consumed
-    stage(nxt);
-    __syncthreads();
-    if (tt + 1 < tile_end) gather(tt + 1, nxt);
+    int buf = 0;
+    if constexpr (DIRECT) {
+      buf = (tt - tile_beg) & 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of the tile are in LDS
+      __syncthreads();  // every wave's rows are in; the other buffer's readers (tile tt-1) are done
+      if (tt + 1 < tile_end) gather_direct(tt + 1, buf ^ 1);
+    } else {
+      __syncthreads();  // previous tile fully consumed
+      stage(nxt);
+      __syncthreads();
+      if (tt + 1 < tile_end) gather(tt + 1, nxt);
+    }
+    const uint16_t(*kv)[KV_LD] = sm.kv[buf];
+    const float* rscale = sm.rscale[buf];
+    const int* rvalid = sm.rvalid[buf];
+    const uint16_t* tr_lo = &kv[4 * g + trj][4 * tra];
+    const uint16_t* tr_hi = &kv[16 + 4 * g + trj][4 * tra];
 
     // S^T = KV . Q^T for rows [16st, 16st+16): the two row halves are
     // independent accumulation chains; their K operands are read in pairs
@@ -317,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-          kop[st][u] = *reinterpret_cast<const bf16x8*>(&sm.kv[16 * st + hl][32 * (c + u) + 8 * g]);
+          kop[st][u] = *reinterpret_cast<const bf16x8*>(&kv[16 * st + hl][32 * (c + u) + 8 * g]);
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -332,8 +398,8 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * st + 4 * g + i;
-        rs[st][i] = sm.rscale[row];
-        lg[st][i] = sm.rvalid[row] ? s[st][i] * scale2 * rs[st][i] : -INFINITY;
+        rs[st][i] = rscale[row];
+        lg[st][i] = rvalid[row] ? s[st][i] * scale2 * rs[st][i] : -INFINITY;
         mt = fmaxf(mt, lg[st][i]);
       }
     mt = max_across_rows(mt);
@@ -343,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mine |= sm.rvalid[16 * st + 4 * g + i] != 0;
+      for (int i = 0; i < 4; ++i) mine |= rvalid[16 * st + 4 * g + i] != 0;
     seen |= __ballot(mine) != 0;
     if (!seen) continue;
     // Lazy rescaling: m_run is a reference point, not necessarily the
@@ -539,10 +605,11 @@ hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const 
   hipError_t e0 = hipGetDevice(&dev);
   if (e0 != hipSuccess) return e0;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  const void* kernels[4] = {(const void*)sparse_attn_kernel<FMT_BF16, FMT_BF16>,
-                            (const void*)sparse_attn_kernel<FMT_BF16, FMT_FP8>,
-                            (const void*)sparse_attn_kernel<FMT_NVFP4, FMT_BF16>,
-                            (const void*)sparse_attn_kernel<FMT_NVFP4, FMT_FP8>};
+  const void* kernels[5] = {(const void*)sparse_attn_kernel<FMT_BF16, FMT_BF16, true>,
+                            (const void*)sparse_attn_kernel<FMT_BF16, FMT_BF16, false>,
+                            (const void*)sparse_attn_kernel<FMT_BF16, FMT_FP8, false>,
+                            (const void*)sparse_attn_kernel<FMT_NVFP4, FMT_BF16, false>,
+                            (const void*)sparse_attn_kernel<FMT_NVFP4, FMT_FP8, false>};
   if (!attr_set[dev].load(std::memory_order_acquire)) {
     for (const void* k : kernels) {
       e0 = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(Smem));
@@ -552,14 +619,16 @@ hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const 
   }
   const dim3 grid((unsigned)R, (unsigned)splits), block(256);
   const bool lat4 = lat_fmt == FMT_NVFP4, win8 = win_fmt == FMT_FP8;
-  if (!lat4 && !win8)
-    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_BF16>), grid, block, sizeof(Smem), s, a);
+  if (!lat4 && !win8 && tiles_per_split >= DIRECT_MIN_TILES)
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_BF16, true>), grid, block, sizeof(Smem), s, a);
+  else if (!lat4 && !win8)
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_BF16, false>), grid, block, sizeof(Smem), s, a);
   else if (!lat4)
-    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_FP8>), grid, block, sizeof(Smem), s, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_BF16, FMT_FP8, false>), grid, block, sizeof(Smem), s, a);
   else if (!win8)
-    hipLaunchKernelGGL((sparse_attn_kernel<FMT_NVFP4, FMT_BF16>), grid, block, sizeof(Smem), s, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_NVFP4, FMT_BF16, false>), grid, block, sizeof(Smem), s, a);
   else
-    hipLaunchKernelGGL((sparse_attn_kernel<FMT_NVFP4, FMT_FP8>), grid, block, sizeof(Smem), s, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<FMT_NVFP4, FMT_FP8, false>), grid, block, sizeof(Smem), s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)R, HQ / 4), dim3(256), 0, s, a);
