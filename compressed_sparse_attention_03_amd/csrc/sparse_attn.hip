@@ -103,11 +103,9 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint16_t* lo, const uint16_t*
   return __builtin_bit_cast(bf16x8, (u32x4){a2[0], a2[1], b2[0], b2[1]});
 }
 
+// The tile buffers themselves are two static LDS arrays of the kernel (see
+// the direct row loads); these are the per-tile row data and the Sel cache.
 struct Smem {
-  // the tile, row-major: QK operand, and PV operand via transpose reads;
-  // two buffers when rows move straight from memory into LDS (bf16 caches),
-  // else only the first is used
-  uint16_t kv[2][TILE][KV_LD];
   float rscale[2][TILE];
   int rvalid[2][TILE];
   int32_t selc[SEL_CAP];  // sel[lat_beg ..] of this workgroup's latent rows
@@ -149,20 +147,29 @@ __device__ __forceinline__ u32x4 nvfp4_piece(uint32_t codes, uint32_t scale_byte
 // One wave per SIMD: a wave's 16 heads x 512 fp32 accumulators, its 16 query
 // heads (QK operands) and the next tile's rows take the register file.
 // DIRECT (bf16 latents and window only): rows move straight from memory
-// into a double-buffered LDS tile instead of through registers.  The
-// compiler cannot tell the two buffers apart and waits for the next tile's
-// loads before reading the current one, so the next tile's gather does not
-// overlap the current tile's compute; what it saves (the staging registers,
-// the masking and LDS stores, one barrier per tile) pays off when a
-// workgroup walks many tiles (prefill, 20 per query: 1.38 -> 1.16 ms), not
-// when it walks a few (1M decode, 2: 18.5 -> 20.4 us; 128K and
-// verification decodes, 5: 25.9 -> 29.8 and 29.5 -> 33.2 us), so the
-// launcher picks by tiles per split.
+// into a double-buffered LDS tile instead of through registers.  The two
+// buffers are separate static arrays and the tile loop alternates between
+// them at compile time, so the compiler can see that the rows loading into
+// one are not the rows read from the other and does not wait for the next
+// tile's loads before the current tile's reads (with one indexed array it
+// did).  What it saves (the staging registers, the masking and LDS stores,
+// one barrier per tile) pays off when a workgroup walks many tiles
+// (prefill, 20 per query: 1.38 -> 1.13 ms), not when it walks a few (the
+// row addresses come from the Sel cache one scalar read at a time: 1M
+// decode, 2 tiles: 18.4 -> 20.4 us; 128K and verification decodes, 5:
+// 25.7 -> 30.2 and 29.0 -> 32.8 us), so the launcher picks by tiles per
+// split.
 template <int LF, int WF, bool DIRECT>
 __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   static_assert(!DIRECT || (LF == FMT_BF16 && WF == FMT_BF16), "direct rows are bf16 rows");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+  // the tile, row-major: QK operand, and PV operand via transpose reads.
+  // Two separate arrays, so that the compiler can tell that the rows being
+  // loaded straight into one (direct path) are not the rows read from the
+  // other; the register path uses the first only.
+  __shared__ __align__(16) uint16_t kvA[TILE][KV_LD];
+  __shared__ __align__(16) uint16_t kvB[TILE][KV_LD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane & 15, g = lane >> 4;
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       const int p = p0 + 32 * pp;
 #pragma unroll
       for (int x = 0; x < 4; ++x)
-        *reinterpret_cast<u32x4*>(&sm.kv[0][4 * rq + x][8 * p]) = decoded(st, pp, x);
+        *reinterpret_cast<u32x4*>(&kvA[4 * rq + x][8 * p]) = decoded(st, pp, x);
     }
     if (wave == 0 && lane < 32 && (lane & 3) == 0) {  // one lane per row quad (rq = 0..7)
 #pragma unroll
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // carries bytes 16l .. 16l+15 of the 1 KiB row, measured), with no
   // register staging; rows that do not exist are zero-filled by LDS stores.
   // A row's source is the same for the whole wave (scalar registers).
-  auto gather_direct = [&](int tt, int buf) {
+  auto gather_direct = [&](int tt, uint16_t (*kvd)[KV_LD], int buf) {
     const bool lat_tile = tt < a.tiles_lat;
 #pragma unroll
     for (int x = 0; x < TILE / 4; ++x) {
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
         sl = sl >= a.W_cap ? sl - a.W_cap : sl;
         src = static_cast<const uint16_t*>(a.win) + ((int64_t)b * a.win_sb + (ok ? sl : 0)) * D;
       }
-      uint16_t* dst = &sm.kv[buf][rl][0];
+      uint16_t* dst = &kvd[rl][0];
       if (ok)
         __builtin_amdgcn_global_load_lds(src + 8 * lane, (__attribute__((address_space(3))) void*)dst,
                                          16, 0, 0);
@@ -350,26 +357,8 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // 16 + 4g + j (k-slots 4-7), and every lane gets its dim's 8 rows.
   const int trj = (lane & 15) >> 2, tra = lane & 3;
 
-  if (tile_beg < tile_end) {
-    if constexpr (DIRECT) gather_direct(tile_beg, 0);
-    else gather(tile_beg, nxt);
-  }
-  for (int tt = tile_beg; tt < tile_end; ++tt) {
-    int buf = 0;
-    if constexpr (DIRECT) {
-      buf = (tt - tile_beg) & 1;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of the tile are in LDS
-      __syncthreads();  // every wave's rows are in; the other buffer's readers (tile tt-1) are done
-      if (tt + 1 < tile_end) gather_direct(tt + 1, buf ^ 1);
-    } else {
-      __syncthreads();  // previous tile fully consumed
-      stage(nxt);
-      __syncthreads();
-      if (tt + 1 < tile_end) gather(tt + 1, nxt);
-    }
-    const uint16_t(*kv)[KV_LD] = sm.kv[buf];
-    const float* rscale = sm.rscale[buf];
-    const int* rvalid = sm.rvalid[buf];
+  // one tile from LDS (kv, and its rows' scales and validity)
+  auto tile_body = [&](const uint16_t (*kv)[KV_LD], const float* rscale, const int* rvalid) {
     const uint16_t* tr_lo = &kv[4 * g + trj][4 * tra];
     const uint16_t* tr_hi = &kv[16 + 4 * g + trj][4 * tra];
 
@@ -411,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mine |= rvalid[16 * st + 4 * g + i] != 0;
     seen |= __ballot(mine) != 0;
-    if (!seen) continue;
+    if (!seen) return;
     // Lazy rescaling: m_run is a reference point, not necessarily the
     // running max; it moves only when a logit exceeds it by more than
     // RESCALE_TAU, so the weights stay below e^RESCALE_TAU and the
@@ -449,6 +438,32 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         o[T0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[u], pop, o[T0 + u], 0, 0, 0);
+    }
+  };
+
+  if constexpr (DIRECT) {
+    // two tiles per trip, one per buffer: each half reads a buffer that is
+    // known at compile time while the next tile's rows load into the other
+    if (tile_beg < tile_end) gather_direct(tile_beg, kvA, 0);
+    for (int tt = tile_beg; tt < tile_end; tt += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of tile tt are in
+      __syncthreads();  // every wave's rows are in; kvB's readers (tile tt-1) are done
+      if (tt + 1 < tile_end) gather_direct(tt + 1, kvB, 1);
+      tile_body(kvA, sm.rscale[0], sm.rvalid[0]);
+      if (tt + 1 >= tile_end) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();  // tile tt+1 is in; kvA's readers (tile tt) are done
+      if (tt + 2 < tile_end) gather_direct(tt + 2, kvA, 0);
+      tile_body(kvB, sm.rscale[1], sm.rvalid[1]);
+    }
+  } else {
+    if (tile_beg < tile_end) gather(tile_beg, nxt);
+    for (int tt = tile_beg; tt < tile_end; ++tt) {
+      __syncthreads();  // previous tile fully consumed
+      stage(nxt);
+      __syncthreads();
+      if (tt + 1 < tile_end) gather(tt + 1, nxt);
+      tile_body(kvA, sm.rscale[0], sm.rvalid[0]);
     }
   }
 
