@@ -168,9 +168,13 @@ int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
  *   score(p) = sum_{h<32} w[h] * max(0, q[h] . k[p])
  *
  * Row r = b*Tq + j is the query (b, j) at raw position q_pos[b][j].
- *   q     : bf16 [B][Tq][32][128] (q_dt must be CSA2_BF16; with FP8 keys
- *           the query is rounded to E4M3 inside the kernel, exact for the
- *           small integers index queries take)
+ *   q     : bf16 [B][Tq][32][128] (q_dt must be CSA2_BF16).  The query
+ *           meets the keys in their format ([NVFP4] section 3.3 runs the
+ *           indexer on FP4 index queries): with CSA2_FP8_E4M3 keys every
+ *           query value is first rounded to the nearest E4M3 value (ties to
+ *           even, saturating at +-448), with CSA2_MXFP4 keys to the nearest
+ *           E2M1 value (ties to even, saturating at +-6); bf16 keys use it as
+ *           is.  Small integers are exact in every format.
  *   w     : f32  [B][Tq][32] per-query, per-head weights
  *   k     : [B][n_cache][128] in k_dt (CSA2_BF16 or CSA2_FP8_E4M3), batch
  *           stride k_sb elements; or CSA2_MXFP4 ([NVFP4] section 3.3 keeps
@@ -178,8 +182,8 @@ int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
  *           E2M1 codes [B][n_cache][64] bytes, batch stride k_sb bytes
  *           (a multiple of 16), and k_scale the E8M0 scales
  *           [B][n_cache][4] (dims 0-31, 32-63, 64-95, 96-127), batch stride
- *           k_sb/16 bytes, 4-byte aligned; the query is rounded to E2M1
- *           (exact for the small integers index queries take).  MXFP4 keys
+ *           k_sb/16 bytes, 4-byte aligned (the query rounded to E2M1, as
+ *           above).  MXFP4 keys
  *           are supported by the many-query scan (SCAN mode, Tq >= 64, the
  *           chunked prefill) and return CSA2_EUNSUPPORTED elsewhere.
  *   k_scale : MXFP4 only, else ignored (may be NULL)
@@ -201,7 +205,10 @@ int csa2_quant_nvfp4(const void *src, csa2_dtype src_dt, int64_t rows,
  *             -inf) when the block id is -1 or the latent is not visible.
  *   block_max, bm_stride are ignored.
  * With integer-valued q, k (|q|,|k| <= 3) and weights that are multiples of
- * 1/16 every score is exact in fp32, whatever the summation order.
+ * 1/16 every score is exact in fp32, whatever the summation order.  For other
+ * queries each head's dot product is exact whenever its terms fit fp32 (E4M3
+ * or E2M1 query against E4M3 or MXFP4 keys of moderate size), and the
+ * weighted sum of the 32 non-negative head terms is rounded in fp32.
  * ---------------------------------------------------------------------- */
 #define CSA2_SCORES_SCAN 0
 #define CSA2_SCORES_CAND 1

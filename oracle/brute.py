@@ -5,7 +5,9 @@ a deliberately different form from ``csa2_ref.c`` so that a slip in either
 (dropped term, wrong index, transposed operand) shows up as a mismatch:
 
 * decoding uses torch's dtype conversions (bf16, float8_e4m3fn) and the OCP
-  E2M1 value list, not the bit-field formulas;
+  E2M1 value list, not the bit-field formulas; the index query's rounding to
+  the key format uses torch's float8_e4m3fn cast and a neighbour search in
+  the E2M1 value list, not a scan over codes;
 * the compressor uses the two-token closed form y = x1 + sigmoid(l0-l1)(x0-x1);
 * indexer scores are one dense einsum over all latents;
 * the block stage ranks every block with ``np.lexsort`` and then swaps the
@@ -54,6 +56,30 @@ def dec_keys(k):
     return dec_bf16(k) if k.dtype == np.uint16 else dec_e4m3(k)
 
 
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Values to the nearest E4M3 value by torch's float8_e4m3fn cast (which
+    rounds to nearest even and saturates to 448 only below 464: callers keep
+    |x| < 464)."""
+    x = np.asarray(x, np.float64)
+    assert np.all(np.abs(x) < 464.0)
+    return torch.from_numpy(x).float().to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def round_e2m1(x: np.ndarray) -> np.ndarray:
+    """Values to the nearest E2M1 value, ties to the even code, saturating at
+    6: the neighbours of |x| in the sorted magnitude list, the closer one, or
+    the one with an even code on a tie."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(E2M1_MAG, a, side="left"), 0, 7)
+    lo = np.clip(hi - 1, 0, 7)
+    dlo, dhi = a - E2M1_MAG[lo], E2M1_MAG[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= 6.0, 7, pick)
+    mag = E2M1_MAG[pick]
+    return np.where(x < 0, -mag, mag)
+
+
 def compress(raw, gate):
     x = dec_bf16(raw)
     l = dec_bf16(gate)
@@ -67,10 +93,17 @@ def visible(t, N):
     return min(N, (int(t) + 1) // 2) if t >= 0 else 0
 
 
-def index_scores(q, w, k):
-    """q [32][128] bits, w [32], k [N][128] -> dense scores [N]."""
+def index_scores(q, w, k, kd=None):
+    """q [32][128] bits, w [32], k [N][128] -> dense scores [N].  The query
+    meets E4M3 keys rounded to E4M3; ``kd`` (decoded keys) stands for MXFP4
+    keys, which meet the query rounded to E2M1."""
     qd = dec_bf16(q)
-    kd = dec_keys(k)
+    if kd is not None:
+        qd = round_e2m1(qd)
+    else:
+        if k.dtype != np.uint16:
+            qd = round_e4m3(qd)
+        kd = dec_keys(k)
     dots = np.einsum("hd,nd->hn", qd, kd)
     return np.einsum("h,hn->n", w.astype(np.float64), np.maximum(dots, 0.0))
 

@@ -173,8 +173,54 @@ static double index_score(const double *qd /*[32][128]*/, const float *w,
   return s;
 }
 
-static void decode_index_query(const uint16_t *q, double *qd) {
-  for (int i = 0; i < CSA2REF_HI * CSA2REF_DI; ++i) qd[i] = csa2ref_bf16(q[i]);
+/* The index query in the key's number format.  The NVFP4 article (section
+ * 3.3) runs the indexer on FP4-quantised index queries; the pages do not say
+ * how a query meets a key of another format.  Reading: the query is rounded
+ * to the format of the keys it is scored against -- E4M3 keys: the nearest
+ * E4M3 value; MXFP4 keys: the nearest E2M1 value (unit block scale) -- and
+ * stays bf16 for bf16 keys.  Both roundings are nearest, ties to the even
+ * code, saturating at the largest finite magnitude (448 / 6), the sign taken
+ * from x < 0.  The search runs over every finite code in double. */
+uint8_t csa2ref_round_e4m3(double x) {
+  double a = fabs(x), best_d = INFINITY;
+  uint8_t best = 0;
+  if (isnan(x)) return 0x7F;
+  /* at or past the largest finite value: saturate (for huge |x| the two
+   * largest candidates' distances would round to the same double) */
+  if (a >= 448.0) return (uint8_t)(0x7E | (x < 0.0 ? 0x80 : 0));
+  for (int c = 0; c <= 0x7E; ++c) { /* every finite non-negative code */
+    double d = fabs(csa2ref_e4m3((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = (uint8_t)c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(best | (x < 0.0 ? 0x80 : 0));
+}
+
+uint8_t csa2ref_round_e2m1(double x) {
+  double a = fabs(x), best_d = INFINITY;
+  uint8_t best = 0;
+  if (a >= 6.0) return (uint8_t)(7 | (x < 0.0 ? 8 : 0)); /* saturate, as above */
+  for (int c = 0; c < 8; ++c) { /* the eight magnitudes */
+    double d = fabs(csa2ref_e2m1((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = (uint8_t)c;
+      best_d = d;
+    }
+  }
+  return (uint8_t)(best | (x < 0.0 ? 8 : 0));
+}
+
+static void decode_index_query(const uint16_t *q, int k_fmt, double *qd) {
+  for (int i = 0; i < CSA2REF_HI * CSA2REF_DI; ++i) {
+    double x = csa2ref_bf16(q[i]);
+    if (k_fmt == CSA2REF_E4M3)
+      x = csa2ref_e4m3(csa2ref_round_e4m3(x));
+    else if (k_fmt == CSA2REF_MXFP4)
+      x = csa2ref_e2m1(csa2ref_round_e2m1(x));
+    qd[i] = x;
+  }
 }
 
 /* ===================================================================== */
@@ -196,7 +242,7 @@ void csa2ref_scan(int B, int Tq, const uint16_t *q, const float *w,
     const void *kb = (k_fmt == CSA2REF_BF16)
                          ? (const void *)((const uint16_t *)k + b * k_sb)
                          : (const void *)((const uint8_t *)k + b * k_sb); /* bytes */
-    decode_index_query(q + (int64_t)r * CSA2REF_HI * CSA2REF_DI, qd);
+    decode_index_query(q + (int64_t)r * CSA2REF_HI * CSA2REF_DI, k_fmt, qd);
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < n_cache; ++p) {
       double kd[CSA2REF_DI];
@@ -293,7 +339,7 @@ void csa2ref_cand(int B, int Tq, const uint16_t *q, const float *w,
     const void *kb = (k_fmt == CSA2REF_BF16)
                          ? (const void *)((const uint16_t *)k + b * k_sb)
                          : (const void *)((const uint8_t *)k + b * k_sb); /* bytes */
-    decode_index_query(q + (int64_t)r * CSA2REF_HI * CSA2REF_DI, qd);
+    decode_index_query(q + (int64_t)r * CSA2REF_HI * CSA2REF_DI, k_fmt, qd);
     for (int j = 0; j < K_b; ++j) {
       int32_t blk = blocks[(int64_t)r * K_b + j];
       for (int i = 0; i < CSA2REF_BLK; ++i) {
@@ -473,6 +519,9 @@ uint8_t csa2ref_quant_e2m1(float x, uint8_t scale_code) {
   uint8_t best = 0;
   if (s == 0.0) return 0;
   target = fabs((double)x) / s;
+  /* saturate at 6 first: for a huge quotient the distances to 4 and 6 would
+   * round to the same double and the tie rule would pick 4 */
+  if (target >= 6.0) return (uint8_t)(7 | (x < 0.0f ? 8 : 0));
   for (int c = 0; c < 8; ++c) { /* the eight magnitudes */
     double d = fabs(csa2ref_e2m1((uint8_t)c) - target);
     if (d < best_d || (d == best_d && (c & 1) == 0)) {

@@ -68,6 +68,15 @@ double csa2ref_e2m1(uint8_t nibble); /* low 4 bits used                   */
 double csa2ref_e8m0(uint8_t bits);   /* 2^(bits-127); NaN for 0xFF        */
 uint16_t csa2ref_round_bf16(double x); /* round-to-nearest-even to bf16   */
 
+/* ---- the index query in the key's format ----------------------------- */
+/* Nearest E4M3 code / E2M1 nibble to x, ties to the even code, saturating
+ * at 448 / 6, sign bit from x < 0 (E4M3: NaN gives 0x7F).  The indexer
+ * rounds the bf16 index query this way before scoring it against E4M3 or
+ * MXFP4 keys (reading of the NVFP4 article, section 3.3: FP4 index
+ * queries); bf16 keys meet the bf16 query unrounded.                      */
+uint8_t csa2ref_round_e4m3(double x);
+uint8_t csa2ref_round_e2m1(double x);
+
 /* ---- visibility helpers -------------------------------------------- */
 int64_t csa2ref_n_vis(int64_t t, int64_t n_cache);
 int64_t csa2ref_newest_block(int64_t t, int64_t n_cache); /* -1 if none */
@@ -82,8 +91,8 @@ void csa2ref_compress(int B, int T, const uint16_t *kv, int64_t kv_sb,
                       int64_t out_sb, double *out_f64);
 
 /* ---- a2: index scores over all visible latents + block max ---------- */
-/* q: bf16 [B][Tq][32][128]; w: f32 [B][Tq][32]; k: [B][n_cache][128] in
- * k_fmt (BF16 or E4M3), batch stride k_sb elements; q_pos: [B][Tq].
+/* q: bf16 [B][Tq][32][128], rounded to the key format first (see
+ * csa2ref_round_e4m3 / _e2m1); w: f32 [B][Tq][32]; q_pos: [B][Tq].
  * scores (optional): [B*Tq][s_stride], -inf for invisible positions.
  * block_max (optional): [B*Tq][bm_stride], -inf for invisible blocks.     */
 /* Index keys k: [B][N][128] in k_fmt (CSA2REF_BF16, CSA2REF_E4M3 or
@@ -105,7 +114,8 @@ void csa2ref_select(int R, int64_t n, const double *scores, int64_t s_stride,
                     int64_t o_stride);
 
 /* ---- a4: indexer scores over the candidate blocks -------------------- */
-/* blocks: [B*Tq][K_b] block ids (-1 = none).  Output column j*8+i is the
+/* q, w, k as for csa2ref_scan (the query rounded to the key format).
+ * blocks: [B*Tq][K_b] block ids (-1 = none).  Output column j*8+i is the
  * latent 8*blocks[j]+i when that latent is visible, else id -1 and score
  * -inf.                                                                   */
 void csa2ref_cand(int B, int Tq, const uint16_t *q, const float *w,

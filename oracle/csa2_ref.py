@@ -46,6 +46,10 @@ def lib():
         L.csa2ref_e2m1.argtypes = [ctypes.c_uint8]
         L.csa2ref_e8m0.restype = D_
         L.csa2ref_e8m0.argtypes = [ctypes.c_uint8]
+        L.csa2ref_round_e4m3.restype = ctypes.c_uint8
+        L.csa2ref_round_e4m3.argtypes = [D_]
+        L.csa2ref_round_e2m1.restype = ctypes.c_uint8
+        L.csa2ref_round_e2m1.argtypes = [D_]
         L.csa2ref_round_bf16.restype = ctypes.c_uint16
         L.csa2ref_round_bf16.argtypes = [D_]
         L.csa2ref_n_vis.restype = I64
@@ -132,6 +136,18 @@ def bf16_array(bits: np.ndarray) -> np.ndarray:
     return tab[flat].reshape(u.shape)
 
 
+def round_e4m3(x) -> int:
+    """Nearest E4M3 code to x (ties to even, saturating at 448): the index
+    query's rounding for E4M3 keys."""
+    return lib().csa2ref_round_e4m3(float(x))
+
+
+def round_e2m1(x) -> int:
+    """Nearest E2M1 nibble to x (ties to even, saturating at 6): the index
+    query's rounding for MXFP4 keys."""
+    return lib().csa2ref_round_e2m1(float(x))
+
+
 def n_vis(t, n_cache) -> int:
     return lib().csa2ref_n_vis(int(t), int(n_cache))
 
@@ -156,8 +172,10 @@ def scan(q, w, k, q_pos, want_scores=False):
     """Indexer scores of every visible latent and per-block maxima.
 
     q uint16 [B][Tq][32][128]; w f32 [B][Tq][32]; k [B][N][128] (uint16 bf16 or
-    uint8 E4M3); q_pos int64 [B][Tq].  Returns (scores [B*Tq][N] or None,
-    block_max [B*Tq][ceil(N/8)]), float64 with -inf where invisible."""
+    uint8 E4M3) or an MXFP4 (codes, scales) pair; q_pos int64 [B][Tq].  The
+    query is rounded to the key format first (E4M3 / E2M1, nearest, ties to
+    even, saturating).  Returns (scores [B*Tq][N] or None, block_max
+    [B*Tq][ceil(N/8)]), float64 with -inf where invisible."""
     q, w, q_pos = _c(q, np.uint16), _c(w, np.float32), _c(q_pos, np.int64)
     k, k_fmt, k_sb = _keys(k)
     B, Tq = q.shape[:2]

@@ -121,3 +121,50 @@ def test_fp8_dequant_row_scale():
     ours = ref.dequant_fp8(src, sc)
     exp = brute.dec_e4m3(src) * sc[:, None].astype(np.float64)
     assert np.array_equal(ours, exp)
+
+
+# ---- the index query rounded to the key format (NVFP4 article, section 3.3:
+# FP4 index queries; E4M3 keys meet an E4M3 query, MXFP4 keys an E2M1 one)
+def _all_bf16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    return bits, vals
+
+
+def test_query_round_e4m3_matches_torch_cast():
+    bits, vals = _all_bf16()
+    fin = np.isfinite(vals)
+    inside = fin & (np.abs(vals) < 464.0)
+    want = brute.round_e4m3(vals[inside])
+    got = np.array([ref.e4m3(ref.round_e4m3(v)) for v in vals[inside]])
+    assert np.array_equal(got, want)
+    # beyond torch's saturating range (and infinities) the format's largest
+    # finite magnitude, 448, with the input's sign
+    outside = ~inside & ~np.isnan(vals)
+    got_out = np.array([ref.e4m3(ref.round_e4m3(v)) for v in vals[outside]])
+    assert np.array_equal(got_out, np.where(vals[outside] < 0, -448.0, 448.0))
+    # ties go to the even code: 2^-10 (half the smallest subnormal) -> 0,
+    # 3 * 2^-10 -> 2^-8 (code 2), 1 + 1/16 -> 1, 1 + 3/16 -> 1.25
+    for x, code in ((2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (1 + 1 / 16, 0x38),
+                    (1 + 3 / 16, 0x3A), (-(1 + 3 / 16), 0xBA)):
+        assert ref.round_e4m3(x) == code, (x, ref.round_e4m3(x), code)
+
+
+def test_query_round_e2m1_matches_exact_nearest():
+    from fractions import Fraction
+
+    table = _table("e2m1_values.txt")
+    mags = sorted({abs(v) for _, v in table})
+    code_of = {abs(v): c for c, v in table if c < 8}
+    bits, vals = _all_bf16()
+    sel = np.isfinite(vals) & (np.abs(vals) <= 8.0)
+    for v in vals[sel][::7].tolist() + [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75, 6.0, 7.9]:
+        a = Fraction(abs(v))
+        d = [abs(a - Fraction(m)) for m in mags]
+        best = min(d)
+        ties = [m for m, dd in zip(mags, d) if dd == best]
+        m = ties[0] if len(ties) == 1 else [t for t in ties if code_of[t] % 2 == 0][0]
+        want = code_of[m] | (8 if v < 0 else 0)
+        assert ref.round_e2m1(v) == want, (v, ref.round_e2m1(v), want)
+        assert ref.e2m1(ref.round_e2m1(v)) == brute.round_e2m1(np.array([v]))[0], v
+    assert ref.e2m1(ref.round_e2m1(1e30)) == 6.0 and ref.e2m1(ref.round_e2m1(-7.0)) == -6.0

@@ -103,7 +103,9 @@ def test_e2m1_ties_and_saturation():
     # mantissa bit is 0
     cases = [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6),
              (6.0, 7), (6.5, 7), (100.0, 7), (0.2499, 0), (0.2501, 1), (-0.75, 10),
-             (-5.0001, 15), (-0.1, 8), (0.0, 0)]
+             (-5.0001, 15), (-0.1, 8), (0.0, 0),
+             # quotients far past 6 (the distances to 4 and 6 equal in double)
+             (1e30, 7), (-3e38, 15)]
     for x, want in cases:
         assert ref.quant_e2m1(x, s_code) == want, (x, want)
         if abs(x) <= 6:
