@@ -350,6 +350,19 @@ class DecodePath:
         return graph
 
 
+def stack_route(layer: int, index_sources, kv_sources, window_only):
+    """Which published Sel and which compressed cache a layer reads (NVFP4
+    article, sections 3.3 and 4: index source layers publish their top-K,
+    KV source layers store the cache the other layers share; section 3.2:
+    window-only layers read neither).  A layer reads the most recent source
+    at or before it; None for a window-only layer."""
+    if layer in window_only:
+        return None
+    idx = max((s for s in index_sources if s <= layer), default=-1)
+    kv = max((s for s in kv_sources if s <= layer), default=-1)
+    return idx, kv
+
+
 class LayerStackPath:
     """One decode step through a stack of layers that share index results and
     compressed caches (NVFP4 article, sections 3.3 and 4): the block stage
@@ -387,10 +400,7 @@ class LayerStackPath:
 
     def source_of(self, layer: int):
         """(index source, KV source) read by ``layer``; None for window-only layers."""
-        if layer in self.window_only:
-            return None
-        from .gen import stack_source
-        return stack_source(layer, self.index_sources), stack_source(layer, self.kv_sources)
+        return stack_route(layer, self.index_sources, self.kv_sources, self.window_only)
 
     def run(self, inp: dict, scale: float, stream=None):
         index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], block_max=self.block_max,

@@ -243,15 +243,6 @@ STACK_INDEX_SOURCES = (2, 8, 14, 20, 24, 28, 32, 36)
 STACK_KV_SOURCES = (2, 8, 14, 20)
 
 
-def stack_source(layer: int, sources) -> int:
-    """The most recent source layer at or before ``layer`` (-1 if none)."""
-    best = -1
-    for s in sources:
-        if s <= layer:
-            best = max(best, s)
-    return best
-
-
 def make_stack_inputs(cfg: Config, layers: int = STACK_LAYERS, window_only=STACK_WINDOW_ONLY,
                       index_sources=STACK_INDEX_SOURCES, kv_sources=STACK_KV_SOURCES,
                       device="cpu", seed: Optional[int] = None) -> dict:

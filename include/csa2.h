@@ -25,8 +25,10 @@
  *     keeps no pointer after a call returns and allocates no device memory;
  *     scratch space, where a call needs it, is passed in by the caller.
  *   - Calls enqueue work on the given HIP stream and return without waiting.
- *     The library holds no global state and may be called from several
- *     threads at once on different streams.
+ *     The only state the library keeps is a once-per-device flag recording
+ *     that the attention kernels' dynamic-LDS limit has been raised (set on
+ *     the first csa2_sparse_attn call on a device, atomically); calls may be
+ *     made from several threads at once on different streams.
  *   - Strides are in elements of the tensor's own storage type (bytes for
  *     FP8 / NVFP4 data); the innermost dimension is contiguous.
  *   - Every call returns a csa2_status.  Arguments are validated on the host

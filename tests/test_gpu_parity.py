@@ -424,6 +424,132 @@ def test_attention_rescale(name, kw, tol):
     assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3 * max(1.0, np.abs(lse_ref).max())
 
 
+def _direct_q_pos(R, W_cap, W, seed):
+    """Query positions for the attention stage tests of many queries: a
+    quarter of them before position W - 1 (windows that reach before the
+    first token), the rest spread so that one ring of W_cap slots holds every
+    query's window (spread + W <= W_cap)."""
+    rng = np.random.default_rng(seed)
+    early = np.sort(rng.choice(W - 1, R // 4, replace=False))
+    late = np.sort(rng.choice(np.arange(W - 1, W_cap - W + 1), R - R // 4, replace=False))
+    return np.concatenate([early, late]).astype(np.int64)
+
+
+@pytest.mark.parametrize("B,Tq,K,rescale,seed", [
+    (1, 300, 480, False, 120),   # 15 + 4 = 19 tiles per workgroup: odd
+    (1, 300, 512, False, 121),   # 20 tiles
+    (1, 300, 352, True, 122),    # 11 + 4 = 15 tiles, growing logits: rescales
+    (150, 1, 512, False, 123),   # a decode batch of 150 queries: one workgroup each
+    (1, 160, 480, False, 124),   # 160 queries, 19 tiles
+])
+def test_attention_direct_rows(B, Tq, K, rescale, seed):
+    """bf16 latents and window with 10 or more tiles per workgroup: rows move
+    straight from memory into the two LDS tile buffers.  Covers an odd tile
+    count (the loop leaves after its first half), Sel rows of -1 (zero-filled
+    rows), window positions before 0, and a forced rescale of the
+    accumulators."""
+    W, W_cap = 128, 512
+    N = 2048
+    cfg = gen.shrink(gen.CONFIGS["tiny"], B=B, Tq=Tq, N=N, K=K, W=W, W_cap=W_cap, comp_T=0,
+                     seed=seed)
+    inp = _inputs(cfg)
+    R = cfg.R
+    qp = _direct_q_pos(R, W_cap, W, seed).reshape(B, Tq)
+    inp["q_pos"] = torch.from_numpy(qp).cuda()
+    scale = cfg.scale
+    if rescale:
+        ramp = torch.linspace(0.0, 1.0, N, device="cuda")
+        inp["lat"] = (inp["lat"].float() * (1.0 + 5.0 * ramp)[None, :, None]).bfloat16()
+        scale = 8.0 * cfg.scale
+    host = np_subset(inp)
+    rng = np.random.default_rng(seed)
+    sel = np.full((R, K), -1, np.int32)
+    for r in range(R):
+        # ragged: some rows keep far fewer than K latents; early queries'
+        # latents are drawn from the whole cache (the attention call does not
+        # restrict Sel to the query's visible latents)
+        m = K - int(rng.integers(0, K // 2)) if r % 4 else K
+        pick = np.sort(rng.choice(N, m, replace=False)) if not rescale else \
+            np.unique(np.linspace(0, N - 1, m).astype(np.int64))
+        sel[r, :len(pick)] = pick
+    say(f"  direct rows: R={R}, K={K}, {int((sel < 0).sum())} empty Sel slots, "
+        f"{int((qp < W - 1).sum())} queries with partial windows")
+    out = torch.empty((R, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, 64), dtype=torch.float32, device="cuda")
+    wsb = api.workspace_bytes(2, R, K, W)
+    ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device="cuda")
+    api.sparse_attn(inp["q"], inp["lat"], torch.from_numpy(sel).cuda(), inp["win"], inp["q_pos"],
+                    inp["sink"], W, scale, out, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref.attn(host["q"], host["lat"], sel, host["win"], host["q_pos"], host["sink"],
+                              W, scale)
+    check_close("attention out (direct rows)", bf16_to_np(out).reshape(o_ref.shape), o_ref, BF16_TOL)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3 * max(1.0, np.abs(lse_ref).max())
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("1m_lowp", dict(B=2, N=4096, t_last=8191, Tq=1, K_b=64, seed=130)),   # decode scan, FP8
+    ("1m_lowp", dict(B=2, N=3001, t_last=6001, Tq=3, K_b=64, seed=131)),   # few queries, FP8
+    ("prefill_fp8", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=132)),
+    ("prefill_mxfp4", dict(Tq=100, N=5100, t_last=10099, K_b=64, K=128, comp_T=0, seed=133)),
+])
+def test_index_noninteger_queries(name, kw):
+    """Index queries that are not small integers (N(0,1) * 1.7, bf16): the
+    indexer rounds them to the keys' format (E4M3 for FP8 keys, E2M1 for
+    MXFP4 keys) before scoring, as the oracle does.  Every dot product is then
+    exact in fp32; the weighted head sum of 32 non-negative terms is within
+    64 ulp of the exact value.  Selection on identical scores stays
+    bit-exact."""
+    cfg = gen.shrink(gen.CONFIGS[name], **kw)
+    inp = _inputs(cfg)
+    g = torch.Generator(device="cuda").manual_seed(cfg.seed + 1000)
+    inp["qs"] = (torch.randn(inp["qs"].shape, generator=g, device="cuda") * 1.7).bfloat16()
+    if cfg.shared_indexer:
+        inp["qi"] = inp["qs"]
+    else:
+        inp["qi"] = (torch.randn(inp["qi"].shape, generator=g, device="cuda") * 1.7).bfloat16()
+    host = np_subset(inp)
+    R, nblk = cfg.R, cfg.nblk
+    mx = cfg.key_fmt == "mxfp4"
+    ks_h = (host["ks"], host["ks_scale"]) if mx else host["ks"]
+    scores = torch.empty((R, (cfg.N + 3) // 4 * 4), dtype=torch.float32, device="cuda")[:, :cfg.N]
+    bm = torch.empty((R, nblk), dtype=torch.float32, device="cuda")
+    api.index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], scores=scores, block_max=bm,
+                   k_scale=inp["ks_scale"])
+    torch.cuda.synchronize()
+    sc_ref, bm_ref = ref.scan(host["qs"], host["ws"], ks_h, host["q_pos"], want_scores=True)
+    tol = 64 * 2.0 ** -24
+    got_sc, got_bm = scores.cpu().numpy().astype(np.float64), bm.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(sc_ref)
+    assert np.array_equal(np.isfinite(got_sc), fin)
+    err = np.abs(got_sc[fin] - sc_ref[fin])
+    assert np.all(err <= tol * sc_ref[fin]), err.max()
+    finb = np.isfinite(bm_ref)
+    assert np.array_equal(np.isfinite(got_bm), finb)
+    assert np.all(np.abs(got_bm[finb] - bm_ref[finb]) <= tol * bm_ref[finb])
+    nonint = np.abs(ref.bf16_array(host["qs"]) - np.round(ref.bf16_array(host["qs"]))) > 0
+    say(f"  scan: {R} rows, max rel err {(err / np.maximum(sc_ref[fin], 1e-30)).max():.2e}; "
+        f"{nonint.mean() * 100:.0f}% of query values non-integer")
+    # the block stage on the device's own block maxima: bit-exact
+    blocks = torch.empty((R, cfg.K_b), dtype=torch.int32, device="cuda")
+    api.select_topk(bm, cfg.K_b, blocks, force_last=True)
+    forced = np.array([ref.newest_block(t, cfg.N) for t in host["q_pos"].reshape(-1)], np.int32)
+    blk = ref.select(got_bm, cfg.K_b, forced=forced)
+    assert np.array_equal(blocks.cpu().numpy(), blk)
+    if mx:
+        return  # MXFP4 keys serve the one-indexer prefill: candidates are gathered scan scores
+    csc = torch.empty((R, cfg.K_b * 8), dtype=torch.float32, device="cuda")
+    cid = torch.empty((R, cfg.K_b * 8), dtype=torch.int32, device="cuda")
+    api.index_cand(inp["qi"], inp["wi"], inp["ki"], inp["q_pos"], blocks, csc, cid)
+    torch.cuda.synchronize()
+    csc_ref, cid_ref = ref.cand(host["qi"], host["wi"], host["ki"], host["q_pos"], blk)
+    assert np.array_equal(cid.cpu().numpy(), cid_ref)
+    got_c = csc.cpu().numpy().astype(np.float64)
+    finc = np.isfinite(csc_ref)
+    assert np.array_equal(np.isfinite(got_c), finc)
+    assert np.all(np.abs(got_c[finc] - csc_ref[finc]) <= tol * csc_ref[finc])
+
+
 # ------------------------------------------------------ chained, small
 @pytest.mark.parametrize("name,kw", [
     ("tiny", {}),
@@ -497,35 +623,40 @@ def _check_step_row(cfg, inp, host, seqs):
         check_close("decode-step row", bf16_to_np(inp["lat"][list(seqs), g:g + 1]), y64, BF16_TOL)
 
 
+def _every(step, n, offset=0):
+    """Every step-th index from offset, plus the last one."""
+    return sorted(set(range(offset, n, step)) | {n - 1})
+
+
 def test_full_128k():
-    _full("128k", seqs=[0, 13, 31])
+    _full("128k", seqs=_every(4, 32))
 
 
 def test_full_prefill_sampled_queries():
     Tq = gen.CONFIGS["prefill"].Tq
-    _full("prefill", seqs=[0], queries=[0, 1, 2, 127, 128, 1000, 4095, 4096, 6000, Tq - 2, Tq - 1])
+    _full("prefill", seqs=[0], queries=sorted(set(_every(32, Tq)) | {1, 2, 127, 128, Tq - 2}))
 
 
 def test_full_prefill_fp8_sampled_queries():
     Tq = gen.CONFIGS["prefill_fp8"].Tq
-    _full("prefill_fp8", seqs=[0], queries=[0, 5, 300, 4097, Tq - 1])
+    _full("prefill_fp8", seqs=[0], queries=_every(32, Tq, offset=5))
 
 
 def test_full_prefill_mxfp4_sampled_queries():
     Tq = gen.CONFIGS["prefill_mxfp4"].Tq
-    _full("prefill_mxfp4", seqs=[0], queries=[0, 7, 2048, 4099, Tq - 1])
+    _full("prefill_mxfp4", seqs=[0], queries=_every(32, Tq, offset=7))
 
 
 def test_full_1m():
-    _full("1m", seqs=[0, 7])
+    _full("1m", seqs=list(range(8)))
 
 
 def test_full_1m_verify():
-    _full("1m_verify", seqs=[0, 7])
+    _full("1m_verify", seqs=list(range(8)))
 
 
 def test_full_1m_lowp():
-    _full("1m_lowp", seqs=[0, 31])
+    _full("1m_lowp", seqs=_every(4, 32, offset=1))
 
 
 def test_dequant_all_codes():
