@@ -22,8 +22,9 @@ EXPORTS = (
     "csa2_status_string", "csa2_version", "csa2_compress", "csa2_index_scores",
     "csa2_select_topk", "csa2_sparse_attn", "csa2_dequant_fp8", "csa2_dequant_nvfp4",
     "csa2_workspace_bytes", "csa2_compress_nvfp4", "csa2_compress_step", "csa2_quant_nvfp4",
-    "csa2_gather_scores", "csa2_gather_select",
+    "csa2_gather_scores", "csa2_gather_select", "csa2_sparse_attn_noalloc",
 )
+ATTN_SCRATCH_BYTES = 32 << 20
 
 _lib = None
 
@@ -54,6 +55,8 @@ def lib():
         "csa2_select_topk": (I, [I, I64, P, I64, P, I64, P, I, I, P, I64, P, SZ, P]),
         "csa2_sparse_attn": (I, [I, I, P, I64, P, I, P, I64, I64, P, I, I64, P, I, P, I, I, I64,
                                  P, P, F, P, I64, P, P, SZ, P]),
+        "csa2_sparse_attn_noalloc": (I, [I, I, P, I64, P, I, P, I64, I64, P, I, I64, P, I, P, I,
+                                         I, I64, P, P, F, P, I64, P, P]),
         "csa2_dequant_fp8": (I, [P, P, I64, I, P, I, P]),
         "csa2_dequant_nvfp4": (I, [P, P, I64, I, P, I, P]),
         "csa2_workspace_bytes": (SZ, [I, I64, I64, I64]),

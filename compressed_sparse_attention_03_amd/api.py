@@ -228,6 +228,26 @@ def sparse_attn(q, lat, sel, win, q_pos, sink, W: int, scale: float, out, lat_sc
     return out, lse
 
 
+def sparse_attn_noalloc(q, lat, sel, win, q_pos, sink, W: int, scale: float, out, lat_scale=None,
+                        win_scale=None, lse=None, stream=None):
+    """a6 as sparse_attn, with the split partials in the library's fixed
+    per-device scratch instead of a caller workspace (nothing is allocated;
+    calls that overlap on one GPU race)."""
+    B, Tq = q.shape[:2]
+    N = lat.shape[1]
+    W_cap = win.shape[1]
+    K = sel.shape[1]
+    lat_dt = BF16 if lat.dtype == torch.bfloat16 else NVFP4
+    win_dt = BF16 if win.dtype == torch.bfloat16 else FP8_E4M3
+    assert q.stride(-1) == 1 and q.stride(1) == HQ * D
+    check("csa2_sparse_attn_noalloc", lib().csa2_sparse_attn_noalloc(
+        B, Tq, _p(q), q.stride(0), _p(lat), lat_dt, _p(lat_scale), lat.stride(0) // lat.stride(1), N,
+        _p(sel), K, sel.stride(0), _p(win), win_dt, _p(win_scale), W, W_cap,
+        win.stride(0) // win.stride(1), _p(q_pos), _p(sink), float(scale), _p(out), out.stride(0),
+        _p(lse), _stream(stream)))
+    return out, lse
+
+
 def dequant_fp8(src, row_scale=None, dtype=torch.bfloat16, out=None, stream=None):
     rows, cols = src.shape
     if out is None:

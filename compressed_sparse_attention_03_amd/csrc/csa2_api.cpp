@@ -12,6 +12,8 @@
 namespace {
 
 constexpr int64_t kMaxN = int64_t(1) << 24;
+static_assert(csa2::ATTN_SCRATCH_BYTES == CSA2_ATTN_SCRATCH_BYTES,
+              "the header states the scratch size of csa2_sparse_attn_noalloc");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -268,12 +270,18 @@ int csa2_select_topk(int R, int64_t n, const float* scores, int64_t s_stride, co
                                            force_last ? 1 : 0, k, out, o_stride, ws, stream));
 }
 
-int csa2_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
-                     csa2_dtype lat_dt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,
-                     const int32_t* sel, int K, int64_t sel_sb, const void* win, csa2_dtype win_dt,
-                     const float* win_scale, int W, int W_cap, int64_t win_sb,
-                     const int64_t* q_pos, const float* sink, float scale, void* out,
-                     int64_t out_sb, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Every argument check of the sparse attention calls except the scratch.
+// CSA2_OK with R = 0 means there is nothing to do.
+int check_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
+                      csa2_dtype lat_dt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,
+                      const int32_t* sel, int K, int64_t sel_sb, const void* win,
+                      csa2_dtype win_dt, const float* win_scale, int W, int W_cap, int64_t win_sb,
+                      const int64_t* q_pos, const float* sink, void* out, int64_t out_sb,
+                      float* lse) {
   if (B < 0 || Tq < 0 || K < 0 || W < 1 || W_cap < W || n_cache < 0) return CSA2_EINVAL;
   if (K > 2048) return CSA2_EUNSUPPORTED;
   if (lat_dt != CSA2_BF16 && lat_dt != CSA2_NVFP4) return CSA2_EUNSUPPORTED;
@@ -296,11 +304,56 @@ int csa2_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat
   if (K > 0 && sel_sb < K) return CSA2_EINVAL;
   if (lat_sb < 0 || (B > 1 && lat_sb < n_cache)) return CSA2_EINVAL;
   if (win_sb < 0 || (B > 1 && win_sb < W_cap)) return CSA2_EINVAL;
+  return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa2_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
+                     csa2_dtype lat_dt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,
+                     const int32_t* sel, int K, int64_t sel_sb, const void* win, csa2_dtype win_dt,
+                     const float* win_scale, int W, int W_cap, int64_t win_sb,
+                     const int64_t* q_pos, const float* sink, float scale, void* out,
+                     int64_t out_sb, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const int st = check_sparse_attn(B, Tq, q, q_sb, lat, lat_dt, lat_scale, lat_sb, n_cache, sel,
+                                   K, sel_sb, win, win_dt, win_scale, W, W_cap, win_sb, q_pos,
+                                   sink, out, out_sb, lse);
+  const int64_t R = (int64_t)B * Tq;
+  if (st != CSA2_OK || R == 0) return st;
   const size_t need = csa2::attn_workspace_bytes(R, K, W);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 16))) return CSA2_EWORKSPACE;
   clear_stale_error();
   const int lat_fmt = lat_dt == CSA2_NVFP4 ? 3 : 1;
   const int win_fmt = win_dt == CSA2_FP8_E4M3 ? 2 : 1;
+  return launched(csa2::launch_sparse_attn(B, Tq, q, q_sb, lat, lat_fmt, lat_scale, lat_sb,
+                                           n_cache, sel, K, sel_sb, win, win_fmt, win_scale, W,
+                                           W_cap, win_sb, q_pos, sink, scale, out, out_sb, lse,
+                                           ws, stream));
+}
+
+int csa2_sparse_attn_noalloc(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
+                             csa2_dtype lat_dt, const void* lat_scale, int64_t lat_sb,
+                             int64_t n_cache, const int32_t* sel, int K, int64_t sel_sb,
+                             const void* win, csa2_dtype win_dt, const float* win_scale, int W,
+                             int W_cap, int64_t win_sb, const int64_t* q_pos, const float* sink,
+                             float scale, void* out, int64_t out_sb, float* lse,
+                             hipStream_t stream) {
+  const int st = check_sparse_attn(B, Tq, q, q_sb, lat, lat_dt, lat_scale, lat_sb, n_cache, sel,
+                                   K, sel_sb, win, win_dt, win_scale, W, W_cap, win_sb, q_pos,
+                                   sink, out, out_sb, lse);
+  const int64_t R = (int64_t)B * Tq;
+  if (st != CSA2_OK || R == 0) return st;
+  const int lat_fmt = lat_dt == CSA2_NVFP4 ? 3 : 1;
+  const int win_fmt = win_dt == CSA2_FP8_E4M3 ? 2 : 1;
+  // the same split policy as csa2_sparse_attn, so the results are the same
+  // bits; the partials must fit the library's fixed scratch
+  const size_t need = csa2::attn_workspace_bytes_fmt(R, K, W, lat_fmt);
+  if (need > csa2::ATTN_SCRATCH_BYTES) return CSA2_EWORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && csa2::attn_scratch(&ws) != hipSuccess) return CSA2_ELAUNCH;
+  clear_stale_error();
   return launched(csa2::launch_sparse_attn(B, Tq, q, q_sb, lat, lat_fmt, lat_scale, lat_sb,
                                            n_cache, sel, K, sel_sb, win, win_fmt, win_scale, W,
                                            W_cap, win_sb, q_pos, sink, scale, out, out_sb, lse,

@@ -51,6 +51,11 @@ hipError_t launch_gather_select(int R, const float* all, int64_t a_stride, int64
 
 int attn_splits(int64_t R, int K, int W, int lat_fmt);
 size_t attn_workspace_bytes(int64_t R, int K, int W);
+size_t attn_workspace_bytes_fmt(int64_t R, int K, int W, int lat_fmt);
+// the allocation-free variant's scratch: its size and, for the current
+// device, its device address (looked up on first use, then cached)
+constexpr size_t ATTN_SCRATCH_BYTES = size_t(32) << 20;
+hipError_t attn_scratch(void** out);
 hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,
                               int lat_fmt, const void* lat_scale, int64_t lat_sb, int64_t n_cache,
                               const int32_t* sel, int K, int64_t sel_sb, const void* win,

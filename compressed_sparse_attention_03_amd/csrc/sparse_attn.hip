@@ -589,11 +589,42 @@ int attn_splits(int64_t R, int K, int W, int lat_fmt) {
   return s < 1 ? 1 : s;
 }
 
-// the larger of the two formats' needs: the workspace query has no format
-size_t attn_workspace_bytes(int64_t R, int K, int W) {
-  const int s = std::max(attn_splits(R, K, W, FMT_BF16), attn_splits(R, K, W, FMT_NVFP4));
+// split partials of one call in a given latent format (0 when unsplit)
+size_t attn_workspace_bytes_fmt(int64_t R, int K, int W, int lat_fmt) {
+  const int s = attn_splits(R, K, W, lat_fmt);
   if (s <= 1) return 0;
   return (size_t)R * s * HQ * PART * sizeof(float);
+}
+
+// the larger of the two formats' needs: the workspace query has no format
+size_t attn_workspace_bytes(int64_t R, int K, int W) {
+  return std::max(attn_workspace_bytes_fmt(R, K, W, FMT_BF16),
+                  attn_workspace_bytes_fmt(R, K, W, FMT_NVFP4));
+}
+
+// Scratch of the allocation-free entry point: a fixed array in device
+// memory that every GPU the library runs on holds until the process ends.
+// In host code the array's name is only a stand-in (passing it to a kernel
+// would fault): its device address is looked up once per device with
+// hipGetSymbolAddress and that address is what kernels receive.
+static __device__ __align__(256) unsigned char scratch[ATTN_SCRATCH_BYTES];
+static std::atomic<void*> scratch_addr[kMaxDevices];
+
+hipError_t attn_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // with this device current: each device has its own copy of the array
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 hipError_t launch_sparse_attn(int B, int Tq, const void* q, int64_t q_sb, const void* lat,

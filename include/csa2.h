@@ -23,12 +23,15 @@
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers owned by the caller.  The library
  *     keeps no pointer after a call returns and allocates no device memory;
- *     scratch space, where a call needs it, is passed in by the caller.
+ *     scratch space, where a call needs it, is passed in by the caller
+ *     (csa2_sparse_attn_noalloc instead uses a fixed scratch array the
+ *     library holds on each device).
  *   - Calls enqueue work on the given HIP stream and return without waiting.
- *     The only state the library keeps is a once-per-device flag recording
- *     that the attention kernels' dynamic-LDS limit has been raised (set on
- *     the first csa2_sparse_attn call on a device, atomically); calls may be
- *     made from several threads at once on different streams.
+ *     The only state the library keeps is per device and written once,
+ *     atomically: a flag recording that the attention kernels' dynamic-LDS
+ *     limit has been raised, and the device address of the scratch array of
+ *     csa2_sparse_attn_noalloc.  Calls may be made from several threads at
+ *     once on different streams (csa2_sparse_attn_noalloc: see there).
  *   - Strides are in elements of the tensor's own storage type (bytes for
  *     FP8 / NVFP4 data); the innermost dimension is contiguous.
  *   - Every call returns a csa2_status.  Arguments are validated on the host
@@ -334,6 +337,37 @@ int csa2_sparse_attn(int B, int Tq, const void *q, int64_t q_sb,
                      const float *sink, float scale, void *out,
                      int64_t out_sb, float *lse, void *ws, size_t ws_bytes,
                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * csa2_sparse_attn without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and preconditions are
+ * those of csa2_sparse_attn (the same kernels and the same split of a
+ * query's rows over workgroups, so the same bits).  Where csa2_sparse_attn
+ * would use the caller's workspace, this call uses a scratch array of
+ * CSA2_ATTN_SCRATCH_BYTES that the library holds in the memory of every GPU
+ * it runs on until the process ends; its device address is looked up on the
+ * first call on a device that needs it.  The call allocates nothing.
+ *   - Returns CSA2_EWORKSPACE, having enqueued nothing, when the call's split
+ *     partials would exceed the scratch (csa2_workspace_bytes(
+ *     CSA2_OP_SPARSE_ATTN, B*Tq, K, W) bounds them: e.g. 32 NVFP4 queries of
+ *     512 + 128 rows need 29.6 MB, 40 need 37 MB and are refused).  Calls
+ *     of 192 or more queries, and bf16 calls of 128 to 191, need none.
+ *   - Every call on a GPU shares that GPU's one scratch array and leaves its
+ *     partials there: calls that overlap in time on one GPU (different
+ *     streams, or different threads) race and must be serialised by the
+ *     caller.  Nothing in the scratch needs to start at zero.
+ * ---------------------------------------------------------------------- */
+#define CSA2_ATTN_SCRATCH_BYTES (32u << 20)
+int csa2_sparse_attn_noalloc(int B, int Tq, const void *q, int64_t q_sb,
+                             const void *lat, csa2_dtype lat_dt,
+                             const void *lat_scale, int64_t lat_sb,
+                             int64_t n_cache, const int32_t *sel, int K,
+                             int64_t sel_sb, const void *win,
+                             csa2_dtype win_dt, const float *win_scale, int W,
+                             int W_cap, int64_t win_sb, const int64_t *q_pos,
+                             const float *sink, float scale, void *out,
+                             int64_t out_sb, float *lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * a7. Standalone dequantisation ([NVFP4] sections 3.1, 3.2).

@@ -149,6 +149,33 @@ def test_sparse_attn_validation(L):
     assert _attn(L, ws=ctypes.c_void_p(0x10004), ws_bytes=need) == _lib.EWORKSPACE
 
 
+def _attn_noalloc(L, B=1, Tq=1, q=FAKE, q_sb=0, lat=FAKE, lat_dt=_lib.BF16, lat_scale=NULL,
+                  lat_sb=0, n=1024, sel=FAKE, K=512, sel_sb=512, win=FAKE, win_dt=_lib.BF16,
+                  win_scale=NULL, W=128, W_cap=128, win_sb=0, qp=FAKE, sink=FAKE, out=FAKE,
+                  out_sb=64 * 512, lse=NULL):
+    return L.csa2_sparse_attn_noalloc(B, Tq, q, q_sb, lat, lat_dt, lat_scale, lat_sb, n, sel, K,
+                                      sel_sb, win, win_dt, win_scale, W, W_cap, win_sb, qp, sink,
+                                      0.044, out, out_sb, lse, None)
+
+
+def test_sparse_attn_noalloc_validation(L):
+    """The allocation-free variant checks its arguments as csa2_sparse_attn
+    does and refuses, before touching any device, a call whose split
+    partials would not fit the fixed scratch."""
+    assert _attn_noalloc(L, W=0) == _lib.EINVAL
+    assert _attn_noalloc(L, q=NULL) == _lib.EINVAL
+    assert _attn_noalloc(L, lat_dt=_lib.FP8_E4M3) == _lib.EUNSUPPORTED
+    assert _attn_noalloc(L, B=0) == _lib.OK
+    assert _attn_noalloc(L, out=ctypes.c_void_p(0x10008)) == _lib.EINVAL
+    big = 64 * 512 * 2
+    # 40 NVFP4 queries of 512 + 128 rows: 7 splits each, 37 MB of partials
+    need = 40 * 7 * 64 * 516 * 4
+    assert need > _lib.ATTN_SCRATCH_BYTES
+    assert _attn_noalloc(L, B=40, q_sb=big, lat_dt=_lib.NVFP4, lat_scale=FAKE, lat_sb=1024,
+                         win_sb=128) == _lib.EWORKSPACE
+    assert L.csa2_workspace_bytes(_lib.OP_SPARSE_ATTN, 40, 512, 128) >= need
+
+
 def test_workspace_sizes(L):
     # many query rows (prefill): one workgroup per row, no merge, no scratch
     assert L.csa2_workspace_bytes(_lib.OP_SPARSE_ATTN, 8192, 512, 128) == 0
