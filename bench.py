@@ -226,32 +226,124 @@ def scan_launch_us(torch, api, path, inp, launches):
     return start.elapsed_time(end) / launches * 1e3
 
 
-def cpu_baseline(cfg, inp, gen, budget_s=10.0):
-    """The oracle as it stands, on the sequences of the same workload: each
-    sequence's inputs are copied to the host once, then whole-sequence oracle
-    decodes run round-robin until about budget_s of oracle time (the host
-    copies are not counted)."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_sequence(inp, gen, b, queries=None):
+    """Host copy of sequence b's inputs (optionally only some of its queries)."""
+    per_query = {"q", "qs", "ws", "qi", "wi", "q_pos"}
+    host = {}
+    for k, v in inp.items():
+        if k == "cfg":
+            continue
+        if v is None:
+            host[k] = None
+            continue
+        t = v if k == "sink" else v[b:b + 1]
+        if queries is not None and k in per_query:
+            t = t[:, queries]
+        host[k] = gen.to_numpy(t)
+    host["comp_pos0"] = inp["cfg"].comp_pos0
+    return host
+
+
+def cpu_baseline(cfg, inp, gen, budget_s=10.0, threads=None, max_seqs=8, what=None):
+    """The oracle as it stands, on sequences of the same workload: each
+    sequence's inputs are copied to the host once (at most max_seqs of
+    them), then whole-sequence oracle decodes run round-robin until about
+    budget_s of oracle time (the host copies are not counted).  threads:
+    OpenMP threads for the oracle (default: as the environment sets)."""
     from oracle import csa2_ref as ref
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    hosts = []
-    for b in range(cfg.B):
-        host = {k: (None if v is None else gen.to_numpy(v if k == "sink" else v[b:b + 1]))
-                for k, v in inp.items() if k != "cfg"}
-        host["comp_pos0"] = cfg.comp_pos0
-        hosts.append(host)
+    default = ref.threads()
+    if threads:
+        ref.set_threads(threads)
+    used = ref.threads()
+    hosts = [host_sequence(inp, gen, b) for b in range(min(cfg.B, max_seqs))]
     done, spent = 0, 0.0
+    try:
+        while spent < budget_s:
+            host = hosts[done % len(hosts)]
+            ts = time.perf_counter()
+            ref.decode(host, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=cfg.comp_T > 0)
+            spent += time.perf_counter() - ts
+            done += 1
+    finally:
+        ref.set_threads(default)
+    log(f"[cpu] oracle {cfg.name} ({used} threads): {done} sequence decodes in {spent:.1f} s")
+    what = what or cfg.desc
+    return {"value": round(done * cfg.Tq / spent, 4), "unit": "queries/s", "cores": used,
+            "kind": "oracle",
+            "sample": f"{done} whole-sequence decodes ({cfg.Tq} quer{'y' if cfg.Tq == 1 else 'ies'} "
+                      f"each, round-robin over {len(hosts)} sequences of the {what} workload"
+                      f"{', compressor included' if cfg.comp_T else ''}), {spent:.1f} s of oracle "
+                      f"time on {used} threads; host copies of the inputs excluded"}
+
+
+def cpu_baseline_prefill(cfg, inp, gen, budget_s=5.0):
+    """The oracle on the chunked prefill, in tokens/s: the compressor over the
+    whole chunk once, then groups of 32 queries spread over the chunk (each
+    with its own causal horizon and window) until about budget_s; the rate
+    is Tq / (compressor time + Tq x time per query)."""
+    from oracle import csa2_ref as ref
+
+    used = ref.threads()
+    host = host_sequence(inp, gen, 0, queries=[0])
+    ts = time.perf_counter()
+    ref.compress(host["raw"], host["gate"])
+    t_comp = time.perf_counter() - ts
+    done, spent, g, group = 0, 0.0, 0, 0
     while spent < budget_s:
-        host = hosts[done % cfg.B]
+        qs = list(range(g % 256, cfg.Tq, 256))
+        group = len(qs)
+        h = host_sequence(inp, gen, 0, queries=qs)
         ts = time.perf_counter()
-        ref.decode(host, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=cfg.comp_T > 0)
+        ref.decode(h, cfg.K_b, cfg.K, cfg.W, cfg.scale, compress_first=False)
         spent += time.perf_counter() - ts
-        done += 1
-    log(f"[cpu] oracle: {done} sequence decodes in {spent:.1f} s")
-    return {"value": done * cfg.Tq / spent, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} whole-sequence decodes (round-robin over the {cfg.B} sequences of the "
-                      f"1M-context decode workload, one query each), {spent:.1f} s of oracle time; "
-                      f"host copies of the inputs excluded"}
+        done += len(qs)
+        g += 97
+    per_q = spent / done
+    rate = cfg.Tq / (t_comp + cfg.Tq * per_q)
+    log(f"[cpu] oracle prefill ({used} threads): compressor {t_comp:.2f} s, {done} queries in "
+        f"{spent:.1f} s -> {rate:.1f} tokens/s")
+    return {"value": round(rate, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"compressor over the whole {cfg.comp_T}-token chunk ({t_comp:.2f} s), then "
+                      f"{done} of the chunk's {cfg.Tq} queries in groups of {group} spread over it "
+                      f"({spent:.1f} s; each query scans, selects and attends over its own causal "
+                      f"horizon); rate = {cfg.Tq} / (compressor + {cfg.Tq} x mean query time)"}
+
+
+def time_config_evict(cfg, inp, path, steps, torch, evict_bytes=1 << 30):
+    """The same step with a 1 GiB write between steps (four times the 256 MB
+    last-level cache), so no step finds the previous step's bytes cached.
+    Events around each step alone: the eviction write is not timed."""
+    comp = cfg.comp_T > 0
+    evict = torch.empty(evict_bytes // 4, dtype=torch.float32, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evict.fill_(float(i))
+        ev[i][0].record()
+        path.run(inp, cfg.scale, compress_first=comp)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    mean = sum(t) / len(t)
+    del evict
+    log(f"[bench] {cfg.name} with a 1 GiB eviction write between steps: {mean * 1e3:.1f} us/step "
+        f"(median {t[len(t) // 2] * 1e3:.1f})")
+    return {"workload": f"the headline step with a {evict_bytes >> 20} MiB write between steps "
+                        "(untimed), so every step starts with a cold last-level cache",
+            "ms_per_step_mean": round(mean, 4), "ms_per_step_median": round(t[len(t) // 2], 4),
+            "queries_per_s": round(cfg.R / (mean * 1e-3), 1)}
 
 
 def calib_copy(torch, nbytes=1 << 30):
@@ -298,6 +390,8 @@ def main():
     ap.add_argument("--only", metavar="CONFIG", default=None,
                     help="time only this workload's step (e.g. prefill) and print its stage times "
                          "instead of the benchmark line (for counter runs)")
+    ap.add_argument("--evict", action="store_true",
+                    help="with --only: also time steps with a 1 GiB write between them")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the CSA2 path here is built and timed on a single "
@@ -315,9 +409,12 @@ def main():
         if args.only not in gen.CONFIGS:
             print(f"unknown workload {args.only!r}; one of {sorted(gen.CONFIGS)}", file=sys.stderr)
             sys.exit(2)
-        ocfg, _, _, oms, ost = time_config(args.only, args.steps, args.warmup, torch, gen, api)
-        print(json.dumps({"workload": args.only, "ms_per_step": round(oms, 4),
-                          "stages_us_eager": {k: round(v * 1e3, 2) for k, v in ost.items()}}), flush=True)
+        ocfg, oinp, opath, oms, ost = time_config(args.only, args.steps, args.warmup, torch, gen, api)
+        line = {"workload": args.only, "ms_per_step": round(oms, 4),
+                "stages_us_eager": {k: round(v * 1e3, 2) for k, v in ost.items()}}
+        if args.evict:
+            line["evict"] = time_config_evict(ocfg, oinp, opath, args.steps, torch)
+        print(json.dumps(line), flush=True)
         return
 
     cfg, inp, path, ms, stage_ms = time_config("1m", args.steps, args.warmup, torch, gen, api)
@@ -328,6 +425,7 @@ def main():
     scan_s = scan_us * 1e-6
     scan_gbs = sb["index_scan"] / scan_s / 1e9
     log(f"[bench] 1m: scan kernel {scan_us:.1f} us/launch = {scan_gbs:.0f} GB/s")
+    path_keep = path
     del path
     kernel_src = [os.path.join(ROOT, "compressed_sparse_attention_03_amd", "csrc", f) for f in SCAN_SOURCES]
     workload = "1m"
@@ -380,9 +478,39 @@ def main():
                     "(eager stage times, launch gaps included); secondary",
         "us": round(amort * 1e3, 2), "queries_per_s": round(cfg.R / (amort * 1e-3), 1),
     }
+    extra["evict_1m"] = time_config_evict(cfg, inp, path_keep, args.steps, torch)
+    del path_keep
     extra["hbm_ceiling_context"] = hbm_ceiling(torch)
+    cpu = {}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, gen, budget_s=10.0,
+                                              what="1M-context decode")
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
+        result["cpu_baseline"]["affinity_cores"] = len(os.sched_getaffinity(0))
+    else:
+        result["cpu_baseline"] = None
     if not args.only_main:
         del inp
+        torch.cuda.empty_cache()
+        ccfg, cinp, cpath, cms, cst = time_config("128k", args.steps, args.warmup, torch, gen, api)
+        del cpath
+        csb = step_bytes(ccfg)
+        ct = sum(csb.values())
+        extra["decode_128k"] = {
+            "workload": "128K batched decode: 32 sequences x 131,072 raw tokens (65,536 bf16 "
+                        "latents), 1 query each; the step starts with the compressor pooling "
+                        "each sequence's last 256 raw tokens",
+            "queries_per_s": round(ccfg.R / (cms * 1e-3), 1), "ms_per_step": round(cms, 4),
+            "algorithmic_bytes": ct,
+            "step_hbm_frac": round(ct / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stages_us_eager": {k: round(v * 1e3, 2) for k, v in cst.items()},
+        }
+        if not args.no_cpu_baseline:
+            cpu["128k"] = cpu_baseline(ccfg, cinp, gen, budget_s=4.0, max_seqs=4,
+                                       what="128K batched decode")
+            cpu["128k_1thread"] = cpu_baseline(ccfg, cinp, gen, budget_s=4.0, threads=1,
+                                               max_seqs=2, what="128K batched decode")
+        del cinp
         torch.cuda.empty_cache()
         lcfg, linp, lpath, lms, lst = time_config("1m_lowp", max(3, args.steps // 2), 2, torch, gen,
                                                   api)
@@ -397,6 +525,9 @@ def main():
             "index_scan_GBs_eager_stage": round(lsb["index_scan"] / (lst["index_scan"] * 1e-3) / 1e9, 1),
             "stages_us_eager": {k: round(v * 1e3, 2) for k, v in lst.items()},
         }
+        if not args.no_cpu_baseline:
+            cpu["1m_lowp"] = cpu_baseline(lcfg, linp, gen, budget_s=4.0, max_seqs=4,
+                                          what="low-precision 1M decode")
         del linp
         torch.cuda.empty_cache()
         vcfg, vinp, vpath, vms, vst = time_config("1m_verify", max(3, args.steps // 2), 2, torch, gen,
@@ -428,6 +559,8 @@ def main():
             "tokens_per_s": round(pcfg.R / (pms * 1e-3), 1), "ms_per_step": round(pms, 3),
             "stages_us_eager": {k: round(v * 1e3, 2) for k, v in pst.items()},
         }
+        if not args.no_cpu_baseline:
+            cpu["prefill"] = cpu_baseline_prefill(pcfg, pinp, gen, budget_s=5.0)
         del pinp
         torch.cuda.empty_cache()
         fcfg, finp, fpath, fms, fst = time_config("prefill_fp8", 2, 1, torch, gen, api)
@@ -454,12 +587,14 @@ def main():
         }
         del xinp
         torch.cuda.empty_cache()
-        inp = gen.make_inputs(cfg, device="cuda") if not args.no_cpu_baseline else None
-    result["extra"] = extra
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, gen)
-    else:
-        result["cpu_baseline"] = None
+        tcfg = gen.CONFIGS["tiny"]
+        tinp = gen.make_inputs(tcfg, device="cpu")
+        cpu["tiny_1thread"] = cpu_baseline(tcfg, tinp, gen, budget_s=3.0, threads=1,
+                                           what="tiny decode")
+        extra["cpu_baselines"] = dict(cpu, cpu_model=cpu_model(),
+                                      affinity_cores=len(os.sched_getaffinity(0)))
+    result["extra"] = extra
     print(json.dumps(result), flush=True)
 
 

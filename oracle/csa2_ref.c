@@ -11,8 +11,16 @@
 #include "csa2_ref.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the OpenMP regions below (only independent rows / positions
+ * are spread over them): the count the next region uses, and setting it. */
+int csa2ref_threads(void) { return omp_get_max_threads(); }
+void csa2ref_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
 
 /* ===================================================================== */
 /* Element decoders, written from the format definitions.                */

@@ -61,6 +61,10 @@ extern "C" {
 #define CSA2REF_DI 128  /* index head width                                */
 #define CSA2REF_BLK 8   /* candidate block size (latents)                  */
 
+/* ---- threads: OpenMP spreads independent rows / positions only ------ */
+int csa2ref_threads(void);        /* threads the next parallel region uses */
+void csa2ref_set_threads(int n);  /* n > 0                                 */
+
 /* ---- element decoders (format definitions, no tables) ---------------- */
 double csa2ref_bf16(uint16_t bits);
 double csa2ref_e4m3(uint8_t bits);   /* NaN for S.1111.111                */

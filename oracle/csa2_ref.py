@@ -38,6 +38,10 @@ def lib():
             _b.build()
         L = ctypes.CDLL(_LIB_PATH)
         P, I, I64, D_ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.csa2ref_threads.restype = I
+        L.csa2ref_threads.argtypes = []
+        L.csa2ref_set_threads.restype = None
+        L.csa2ref_set_threads.argtypes = [I]
         L.csa2ref_bf16.restype = D_
         L.csa2ref_bf16.argtypes = [ctypes.c_uint16]
         L.csa2ref_e4m3.restype = D_
@@ -105,6 +109,15 @@ def _keys(k):
         return packed, MXFP4, N * MXFP4_ROW
     k = np.ascontiguousarray(k)
     return k, (BF16 if k.dtype == np.uint16 else E4M3), k.shape[1] * DI
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's next parallel region uses."""
+    return lib().csa2ref_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().csa2ref_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- decoders
