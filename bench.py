@@ -321,16 +321,20 @@ def cpu_baseline_prefill(cfg, inp, gen, budget_s=5.0):
 
 
 def time_config_evict(cfg, inp, path, steps, torch, evict_bytes=1 << 30):
-    """The same step with a 1 GiB write between steps (four times the 256 MB
+    """The same step with a 1 GiB read between steps (four times the 256 MB
     last-level cache), so no step finds the previous step's bytes cached.
-    Events around each step alone: the eviction write is not timed."""
+    A read, not a write: the write-back of a 1 GiB write would still be
+    draining into HBM when the step starts and slow it down (random 2 KiB
+    gathers measured at 2.3 TB/s right after such a write, 4.9 TB/s after a
+    read).  Events around each step alone: the eviction read is not timed."""
     comp = cfg.comp_T > 0
-    evict = torch.empty(evict_bytes // 4, dtype=torch.float32, device="cuda")
+    evict = torch.ones(evict_bytes // 4, dtype=torch.float32, device="cuda")
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    sink = torch.empty((steps,), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     for i in range(steps):
-        evict.fill_(float(i))
+        torch.sum(evict, dim=0, out=sink[i])
         ev[i][0].record()
         path.run(inp, cfg.scale, compress_first=comp)
         ev[i][1].record()
@@ -338,9 +342,9 @@ def time_config_evict(cfg, inp, path, steps, torch, evict_bytes=1 << 30):
     t = sorted(a.elapsed_time(b) for a, b in ev)
     mean = sum(t) / len(t)
     del evict
-    log(f"[bench] {cfg.name} with a 1 GiB eviction write between steps: {mean * 1e3:.1f} us/step "
+    log(f"[bench] {cfg.name} with a 1 GiB eviction read between steps: {mean * 1e3:.1f} us/step "
         f"(median {t[len(t) // 2] * 1e3:.1f})")
-    return {"workload": f"the headline step with a {evict_bytes >> 20} MiB write between steps "
+    return {"workload": f"the headline step with a {evict_bytes >> 20} MiB read between steps "
                         "(untimed), so every step starts with a cold last-level cache",
             "ms_per_step_mean": round(mean, 4), "ms_per_step_median": round(t[len(t) // 2], 4),
             "queries_per_s": round(cfg.R / (mean * 1e-3), 1)}
@@ -391,7 +395,7 @@ def main():
                     help="time only this workload's step (e.g. prefill) and print its stage times "
                          "instead of the benchmark line (for counter runs)")
     ap.add_argument("--evict", action="store_true",
-                    help="with --only: also time steps with a 1 GiB write between them")
+                    help="with --only: also time steps with a 1 GiB read between them")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the CSA2 path here is built and timed on a single "
