@@ -108,6 +108,7 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint16_t* lo, const uint16_t*
 struct Smem {
   float rscale[2][TILE];
   int rvalid[2][TILE];
+  uint32_t vmask[2][4];  // direct rows: per buffer and wave, bit x = row 8w + x exists
   int32_t selc[SEL_CAP];  // sel[lat_beg ..] of this workgroup's latent rows
 };
 
@@ -319,35 +320,43 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // register staging; rows that do not exist are zero-filled by LDS stores.
   // A row's source is the same for the whole wave (scalar registers).
   auto gather_direct = [&](int tt, uint16_t (*kvd)[KV_LD], int buf) {
+    // lane x < 8 finds row 8w + x's source (one LDS read of the Sel cache
+    // for the wave's 8 rows); the offsets reach the scalar unit by
+    // v_readlane, so the row loads go out without a round trip between them
     const bool lat_tile = tt < a.tiles_lat;
+    const int rl0 = (TILE / 4) * wave + (lane & 7);
+    bool okl;
+    int64_t roff;
+    if (lat_tile) {
+      const int i = TILE * tt + rl0;
+      const int32_t gidx = i < a.K ? sm.selc[i - lat_beg] : -1;
+      okl = gidx >= 0 && gidx < a.n_cache;
+      roff = ((int64_t)b * a.lat_sb + (okl ? gidx : 0)) * D;
+    } else {
+      const int jw = TILE * (tt - a.tiles_lat) + rl0;
+      okl = jw < a.W && w0 + jw >= 0;
+      int sl = wslot0 + jw;
+      sl = sl >= a.W_cap ? sl - a.W_cap : sl;
+      roff = ((int64_t)b * a.win_sb + (okl ? sl : 0)) * D;
+    }
+    const uint32_t mask = (uint32_t)__ballot(okl) & 0xffu;
+    const uint16_t* base = static_cast<const uint16_t*>(lat_tile ? a.lat : a.win);
+    const uint32_t off_lo = (uint32_t)roff, off_hi = (uint32_t)((uint64_t)roff >> 32);
 #pragma unroll
     for (int x = 0; x < TILE / 4; ++x) {
       const int rl = (TILE / 4) * wave + x;
-      const uint16_t* src;
-      bool ok;
-      if (lat_tile) {
-        const int i = TILE * tt + rl;
-        const int32_t gidx = __builtin_amdgcn_readfirstlane(i < a.K ? sm.selc[i - lat_beg] : -1);
-        ok = gidx >= 0 && gidx < a.n_cache;
-        src = static_cast<const uint16_t*>(a.lat) + ((int64_t)b * a.lat_sb + (ok ? gidx : 0)) * D;
-      } else {
-        const int jw = TILE * (tt - a.tiles_lat) + rl;
-        ok = jw < a.W && w0 + jw >= 0;
-        int sl = wslot0 + jw;
-        sl = sl >= a.W_cap ? sl - a.W_cap : sl;
-        src = static_cast<const uint16_t*>(a.win) + ((int64_t)b * a.win_sb + (ok ? sl : 0)) * D;
-      }
+      const bool ok = (mask >> x) & 1u;
       uint16_t* dst = &kvd[rl][0];
-      if (ok)
-        __builtin_amdgcn_global_load_lds(src + 8 * lane, (__attribute__((address_space(3))) void*)dst,
-                                         16, 0, 0);
-      else
+      if (ok) {
+        const uint64_t o64 = (uint64_t)__builtin_amdgcn_readlane(off_lo, x) |
+                             ((uint64_t)__builtin_amdgcn_readlane(off_hi, x) << 32);
+        __builtin_amdgcn_global_load_lds(base + o64 + 8 * lane,
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      } else {
         *reinterpret_cast<u32x4*>(dst + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
-      if (lane == 0) {
-        sm.rvalid[buf][rl] = ok;
-        sm.rscale[buf][rl] = 1.0f;
       }
     }
+    if (lane == 0) sm.vmask[buf][wave] = mask;
   };
 
   // PV operand addresses: ds_read_b64_tr_b16 works on 16-lane groups, lane
@@ -358,7 +367,13 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   const int trj = (lane & 15) >> 2, tra = lane & 3;
 
   // one tile from LDS (kv, and its rows' scales and validity)
-  auto tile_body = [&](const uint16_t (*kv)[KV_LD], const float* rscale, const int* rvalid) {
+  auto tile_body = [&](const uint16_t (*kv)[KV_LD], const float* rscale, const int* rvalid,
+                       int buf) {
+    // direct rows (bf16, unit row scales): one validity word per tile
+    uint32_t vm = 0;
+    if constexpr (DIRECT)
+      vm = sm.vmask[buf][0] | (sm.vmask[buf][1] << 8) | (sm.vmask[buf][2] << 16) |
+           (sm.vmask[buf][3] << 24);
     const uint16_t* tr_lo = &kv[4 * g + trj][4 * tra];
     const uint16_t* tr_hi = &kv[16 + 4 * g + trj][4 * tra];
 
@@ -387,19 +402,28 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * st + 4 * g + i;
-        rs[st][i] = rscale[row];
-        lg[st][i] = rvalid[row] ? s[st][i] * scale2 * rs[st][i] : -INFINITY;
+        if constexpr (DIRECT) {
+          rs[st][i] = 1.0f;
+          lg[st][i] = (vm >> row) & 1u ? s[st][i] * scale2 : -INFINITY;
+        } else {
+          rs[st][i] = rscale[row];
+          lg[st][i] = rvalid[row] ? s[st][i] * scale2 * rs[st][i] : -INFINITY;
+        }
         mt = fmaxf(mt, lg[st][i]);
       }
     mt = max_across_rows(mt);
     // row validity does not depend on the head, and the 64 lanes together
     // hold all 32 rows: the ballot is the same answer for the whole wave
-    bool mine = false;
+    if constexpr (DIRECT) {
+      seen |= vm != 0u;
+    } else {
+      bool mine = false;
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mine |= rvalid[16 * st + 4 * g + i] != 0;
-    seen |= __ballot(mine) != 0;
+        for (int i = 0; i < 4; ++i) mine |= rvalid[16 * st + 4 * g + i] != 0;
+      seen |= __ballot(mine) != 0;
+    }
     if (!seen) return;
     // Lazy rescaling: m_run is a reference point, not necessarily the
     // running max; it moves only when a logit exceeds it by more than
@@ -449,12 +473,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of tile tt are in
       __syncthreads();  // every wave's rows are in; kvB's readers (tile tt-1) are done
       if (tt + 1 < tile_end) gather_direct(tt + 1, kvB, 1);
-      tile_body(kvA, sm.rscale[0], sm.rvalid[0]);
+      tile_body(kvA, sm.rscale[0], sm.rvalid[0], 0);
       if (tt + 1 >= tile_end) break;
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();  // tile tt+1 is in; kvA's readers (tile tt) are done
       if (tt + 2 < tile_end) gather_direct(tt + 2, kvA, 0);
-      tile_body(kvB, sm.rscale[1], sm.rvalid[1]);
+      tile_body(kvB, sm.rscale[1], sm.rvalid[1], 1);
     }
   } else {
     if (tile_beg < tile_end) gather(tile_beg, nxt);
@@ -463,7 +487,7 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       stage(nxt);
       __syncthreads();
       if (tt + 1 < tile_end) gather(tt + 1, nxt);
-      tile_body(kvA, sm.rscale[0], sm.rvalid[0]);
+      tile_body(kvA, sm.rscale[0], sm.rvalid[0], 0);
     }
   }
 

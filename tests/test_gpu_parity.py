@@ -435,19 +435,24 @@ def _direct_q_pos(R, W_cap, W, seed):
     return np.concatenate([early, late]).astype(np.int64)
 
 
-@pytest.mark.parametrize("B,Tq,K,rescale,seed", [
-    (1, 300, 480, False, 120),   # 15 + 4 = 19 tiles per workgroup: odd
-    (1, 300, 512, False, 121),   # 20 tiles
-    (1, 300, 352, True, 122),    # 11 + 4 = 15 tiles, growing logits: rescales
-    (150, 1, 512, False, 123),   # a decode batch of 150 queries: one workgroup each
-    (1, 160, 480, False, 124),   # 160 queries, 19 tiles
+@pytest.mark.parametrize("B,Tq,K,growth,seed", [
+    (1, 300, 480, 0, 120),     # 15 + 4 = 19 tiles per workgroup: odd
+    (1, 300, 512, 0, 121),     # 20 tiles
+    (1, 300, 352, 5, 122),     # 11 + 4 = 15 tiles, growing logits
+    (150, 1, 512, 0, 123),     # a decode batch of 150 queries: one workgroup each
+    (1, 160, 480, 0, 124),     # 160 queries, 19 tiles
+    (1, 200, 416, 300, 125),   # logits far above every earlier tile's: a second pass
 ])
-def test_attention_direct_rows(B, Tq, K, rescale, seed):
-    """bf16 latents and window with 10 or more tiles per workgroup: rows move
-    straight from memory into the two LDS tile buffers.  Covers an odd tile
-    count (the loop leaves after its first half), Sel rows of -1 (zero-filled
-    rows), window positions before 0, and a forced rescale of the
-    accumulators."""
+def test_attention_direct_rows(B, Tq, K, growth, seed):
+    """bf16 latents and window, one workgroup walking 10 or more tiles per
+    query (the chunked prefill's attention): rows move straight from memory
+    into the two LDS tile buffers.  Covers an odd tile count (the loop leaves
+    after its first half), Sel rows of -1 (zero-filled rows) and queries with
+    no selected latent at all, window positions before 0, logits that grow
+    from tile to tile (latent rows scaled up with their position, an 8x
+    softmax scale), and logits so much larger than the first tile's that the
+    softmax reference must be redone (rows scaled up to 301x)."""
+    rescale = growth > 0
     W, W_cap = 128, 512
     N = 2048
     cfg = gen.shrink(gen.CONFIGS["tiny"], B=B, Tq=Tq, N=N, K=K, W=W, W_cap=W_cap, comp_T=0,
@@ -459,7 +464,7 @@ def test_attention_direct_rows(B, Tq, K, rescale, seed):
     scale = cfg.scale
     if rescale:
         ramp = torch.linspace(0.0, 1.0, N, device="cuda")
-        inp["lat"] = (inp["lat"].float() * (1.0 + 5.0 * ramp)[None, :, None]).bfloat16()
+        inp["lat"] = (inp["lat"].float() * (1.0 + growth * ramp)[None, :, None]).bfloat16()
         scale = 8.0 * cfg.scale
     host = np_subset(inp)
     rng = np.random.default_rng(seed)
@@ -469,6 +474,8 @@ def test_attention_direct_rows(B, Tq, K, rescale, seed):
         # latents are drawn from the whole cache (the attention call does not
         # restrict Sel to the query's visible latents)
         m = K - int(rng.integers(0, K // 2)) if r % 4 else K
+        if r % 11 == 5:
+            continue  # no selected latent: the window alone
         pick = np.sort(rng.choice(N, m, replace=False)) if not rescale else \
             np.unique(np.linspace(0, N - 1, m).astype(np.int64))
         sel[r, :len(pick)] = pick
