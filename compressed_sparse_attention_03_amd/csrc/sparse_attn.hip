@@ -103,6 +103,11 @@ __device__ __forceinline__ bf16x8 pv_operand(const uint16_t* lo, const uint16_t*
   return __builtin_bit_cast(bf16x8, (u32x4){a2[0], a2[1], b2[0], b2[1]});
 }
 
+// One 1 KiB row of zeros in device memory (zero-initialised, never
+// written): the direct row loads read it for rows that do not exist, so that
+// each row is one load without a branch.
+__device__ __align__(1024) uint16_t zero_row[D];
+
 // The tile buffers themselves are two static LDS arrays of the kernel (see
 // the direct row loads); these are the per-tile row data and the Sel cache.
 struct Smem {
@@ -171,6 +176,13 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // other; the register path uses the first only.
   __shared__ __align__(16) uint16_t kvA[TILE][KV_LD];
   __shared__ __align__(16) uint16_t kvB[TILE][KV_LD];
+  // direct path only: each wave's PV weights (its PV B operand as the lanes
+  // hold it), the per-head rescale factors and flags of the last tile, and
+  // the per-head output factors
+  __shared__ __align__(16) bf16x8 pxch[4][64];
+  __shared__ float alpha_x[HQ];
+  __shared__ __align__(16) int resc_x[4];
+  __shared__ float fin_x[HQ];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane & 15, g = lane >> 4;
@@ -213,6 +225,11 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // the window follow it, wrapping once at most since W <= W_cap)
   const int64_t w0 = t - (a.W - 1);
   const int wslot0 = (int)(((w0 % a.W_cap) + a.W_cap) % a.W_cap);
+  // direct rows: source base addresses, and the zero row that rows which do
+  // not exist are loaded from (their weights are masked to 0 as well)
+  const uint64_t lat_base = (uint64_t)(uintptr_t)a.lat;
+  const uint64_t win_base = (uint64_t)(uintptr_t)a.win;
+  const uint64_t zero_base = (uint64_t)(uintptr_t)zero_row;
 
   f32x4 o[32];
 #pragma unroll
@@ -317,44 +334,42 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // bf16 caches: wave w moves rows 8w .. 8w+7 of tile tt straight from
   // memory into LDS buffer buf, one global_load_lds_dwordx4 per row (lane l
   // carries bytes 16l .. 16l+15 of the 1 KiB row, measured), with no
-  // register staging; rows that do not exist are zero-filled by LDS stores.
+  // register staging; rows that do not exist are read from a row of zeros.
   // A row's source is the same for the whole wave (scalar registers).
   auto gather_direct = [&](int tt, uint16_t (*kvd)[KV_LD], int buf) {
     // lane x < 8 finds row 8w + x's source (one LDS read of the Sel cache
-    // for the wave's 8 rows); the offsets reach the scalar unit by
-    // v_readlane, so the row loads go out without a round trip between them
+    // for the wave's 8 rows) and its full address -- the zero row when the
+    // row does not exist, so every row is one load with no branch; the
+    // addresses reach the scalar unit by v_readlane, so the row loads go
+    // out back to back
     const bool lat_tile = tt < a.tiles_lat;
     const int rl0 = (TILE / 4) * wave + (lane & 7);
     bool okl;
-    int64_t roff;
+    uint64_t raddr;
     if (lat_tile) {
       const int i = TILE * tt + rl0;
       const int32_t gidx = i < a.K ? sm.selc[i - lat_beg] : -1;
       okl = gidx >= 0 && gidx < a.n_cache;
-      roff = ((int64_t)b * a.lat_sb + (okl ? gidx : 0)) * D;
+      raddr = lat_base + (uint64_t)(b * a.lat_sb + (okl ? gidx : 0)) * (D * 2);
     } else {
       const int jw = TILE * (tt - a.tiles_lat) + rl0;
       okl = jw < a.W && w0 + jw >= 0;
       int sl = wslot0 + jw;
       sl = sl >= a.W_cap ? sl - a.W_cap : sl;
-      roff = ((int64_t)b * a.win_sb + (okl ? sl : 0)) * D;
+      raddr = win_base + (uint64_t)(b * a.win_sb + (okl ? sl : 0)) * (D * 2);
     }
+    raddr = okl ? raddr : zero_base;
     const uint32_t mask = (uint32_t)__ballot(okl) & 0xffu;
-    const uint16_t* base = static_cast<const uint16_t*>(lat_tile ? a.lat : a.win);
-    const uint32_t off_lo = (uint32_t)roff, off_hi = (uint32_t)((uint64_t)roff >> 32);
+    const uint32_t a_lo = (uint32_t)raddr, a_hi = (uint32_t)(raddr >> 32);
 #pragma unroll
     for (int x = 0; x < TILE / 4; ++x) {
-      const int rl = (TILE / 4) * wave + x;
-      const bool ok = (mask >> x) & 1u;
-      uint16_t* dst = &kvd[rl][0];
-      if (ok) {
-        const uint64_t o64 = (uint64_t)__builtin_amdgcn_readlane(off_lo, x) |
-                             ((uint64_t)__builtin_amdgcn_readlane(off_hi, x) << 32);
-        __builtin_amdgcn_global_load_lds(base + o64 + 8 * lane,
-                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-      } else {
-        *reinterpret_cast<u32x4*>(dst + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
-      }
+      // readlane returns a signed int: both halves go through uint32_t so
+      // that the low half is zero-extended, not sign-extended into the high
+      const uint64_t ra = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)a_lo, x) |
+                          ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)a_hi, x) << 32);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ra) + 8 * lane,
+                                       (__attribute__((address_space(3))) void*)&kvd[(TILE / 4) * wave + x][0],
+                                       16, 0, 0);
     }
     if (lane == 0) sm.vmask[buf][wave] = mask;
   };
@@ -465,6 +480,107 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
     }
   };
 
+  // Direct path, PV split by dims: wave w still forms S^T and the softmax
+  // weights of its 16 heads, publishes the weights (its PV B operand) in
+  // LDS, and after one barrier computes O^T for dims 128w .. 128w+127 of all
+  // 64 heads.  Each wave then reads a quarter of the tile through the
+  // transpose reads instead of all of it: a workgroup reads 176 KB of LDS
+  // per tile instead of 256.  o[4T + hb] is dims 128w + 16T + (rows of the
+  // C layout) of heads 16hb + l%16.  The barrier only waits for LDS: the
+  // next tile's row loads stay in flight across it.
+  auto tile_body_ds = [&](const uint16_t (*kv)[KV_LD], int buf) {
+    const uint32_t vm = sm.vmask[buf][0] | (sm.vmask[buf][1] << 8) |
+                        (sm.vmask[buf][2] << 16) | (sm.vmask[buf][3] << 24);
+    // vm is the same word in every wave, so this exit is workgroup-uniform
+    seen |= vm != 0u;
+    if (!seen) return;
+    f32x4 s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // operands of chunk c + 1 are read before the MFMAs of chunk c
+    bf16x8 kop[2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+      kop[0][st] = *reinterpret_cast<const bf16x8*>(&kv[16 * st + hl][8 * g]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      if (c + 1 < 16) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          kop[(c + 1) & 1][st] =
+              *reinterpret_cast<const bf16x8*>(&kv[16 * st + hl][32 * (c + 1) + 8 * g]);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[c & 1][st], qreg[c], s[st], 0, 0, 0);
+    }
+    float lg[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * st + 4 * g + i;
+        lg[st][i] = (vm >> row) & 1u ? s[st][i] * scale2 : -INFINITY;
+        mt = fmaxf(mt, lg[st][i]);
+      }
+    mt = max_across_rows(mt);
+    // lazy reference point as in the register path; the factor reaches the
+    // other waves (which hold these heads' other dims) through LDS
+    const bool grow = mt > m_run + RESCALE_TAU;
+    const bool scale_acc = grow && m_run != -INFINITY;
+    const float alpha = scale_acc ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+    const bool any = __ballot(scale_acc) != 0;
+    if (any) l_run *= alpha;
+    if (grow) m_run = mt;
+    float psum = 0.f;
+    bf16x8 pop;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pw = __builtin_amdgcn_exp2f(lg[st][i] - m_run);
+        psum += pw;
+        pop[4 * st + i] = (__bf16)pw;
+      }
+    l_run += psum;
+    pxch[wave][lane] = pop;
+    if (lane < 16) alpha_x[16 * wave + lane] = alpha;
+    if (lane == 0) resc_x[wave] = any ? 1 : 0;
+    // LDS-only barrier: wait for this wave's LDS writes, not for its
+    // in-flight row loads (a __syncthreads would wait for those too)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const int4 rf = *reinterpret_cast<const int4*>(resc_x);
+    if ((rf.x | rf.y | rf.z | rf.w) != 0) {
+      const int rfa[4] = {rf.x, rf.y, rf.z, rf.w};
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        if (rfa[hb]) {
+          const float f = alpha_x[16 * hb + hl];
+#pragma unroll
+          for (int T = 0; T < 8; ++T) o[4 * T + hb] *= f;
+        }
+    }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) pb[hb] = pxch[hb][lane];
+    const uint16_t* tr_lo = &kv[4 * g + trj][4 * tra + 128 * wave];
+    const uint16_t* tr_hi = &kv[16 + 4 * g + trj][4 * tra + 128 * wave];
+#pragma unroll
+    for (int T0 = 0; T0 < 8; T0 += 2) {
+      bf16x8 vop[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) vop[u] = pv_operand(tr_lo + 16 * (T0 + u), tr_hi + 16 * (T0 + u));
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[4 * (T0 + u) + hb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop[u], pb[hb], o[4 * (T0 + u) + hb], 0, 0, 0);
+    }
+  };
+
   if constexpr (DIRECT) {
     // two tiles per trip, one per buffer: each half reads a buffer that is
     // known at compile time while the next tile's rows load into the other
@@ -473,12 +589,12 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows of tile tt are in
       __syncthreads();  // every wave's rows are in; kvB's readers (tile tt-1) are done
       if (tt + 1 < tile_end) gather_direct(tt + 1, kvB, 1);
-      tile_body(kvA, sm.rscale[0], sm.rvalid[0], 0);
+      tile_body_ds(kvA, 0);
       if (tt + 1 >= tile_end) break;
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();  // tile tt+1 is in; kvA's readers (tile tt) are done
       if (tt + 2 < tile_end) gather_direct(tt + 2, kvA, 0);
-      tile_body(kvB, sm.rscale[1], sm.rvalid[1], 1);
+      tile_body_ds(kvB, 1);
     }
   } else {
     if (tile_beg < tile_end) gather(tile_beg, nxt);
@@ -494,6 +610,44 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
   // full row sum for this head (each lane group held a quarter of the rows)
   l_run = sum_across_rows(l_run);
   const int h = 16 * wave + hl;
+  if constexpr (DIRECT) {
+    // this wave holds dims 128w .. 128w+127 of every head; the reference
+    // and sum of heads 16w .. 16w+15
+    if (a.splits > 1) {
+      float* pq = a.part + (r * a.splits + split) * HQ * PART;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int T = 0; T < 8; ++T)
+          *reinterpret_cast<f32x4*>(pq + (16 * hb + hl) * PART + 128 * wave + 16 * T + 4 * g) =
+              o[4 * T + hb];
+      if (g == 0) {
+        pq[h * PART + D] = m_run;
+        pq[h * PART + D + 1] = l_run;
+      }
+      return;
+    }
+    const float sk = a.sink[h] * LOG2E;
+    const float M = fmaxf(m_run, sk);
+    const float em = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    const float Z = l_run * em + __builtin_amdgcn_exp2f(sk - M);
+    if (g == 0) fin_x[h] = em / Z;
+    if (a.lse && g == 0) a.lse[r * HQ + h] = (M + __log2f(Z)) * LN2;
+    __syncthreads();
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      const float f = fin_x[16 * hb + hl];
+      uint16_t* orow = a.out + r * a.out_sb + (int64_t)(16 * hb + hl) * D + 128 * wave;
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[4 * T + hb][0] * f, o[4 * T + hb][1] * f);
+        pk[1] = pack_bf16x2(o[4 * T + hb][2] * f, o[4 * T + hb][3] * f);
+        *reinterpret_cast<u32x2*>(orow + 16 * T + 4 * g) = pk;
+      }
+    }
+    return;
+  }
   if (a.splits > 1) {
     float* pp = a.part + ((r * a.splits + split) * HQ + h) * PART;
 #pragma unroll

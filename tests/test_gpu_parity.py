@@ -441,7 +441,9 @@ def _direct_q_pos(R, W_cap, W, seed):
     (1, 300, 352, 5, 122),     # 11 + 4 = 15 tiles, growing logits
     (150, 1, 512, 0, 123),     # a decode batch of 150 queries: one workgroup each
     (1, 160, 480, 0, 124),     # 160 queries, 19 tiles
-    (1, 200, 416, 300, 125),   # logits far above every earlier tile's: a second pass
+    (1, 200, 416, 300, 125),   # logits far above every earlier tile's: repeated rescales
+    (1, 40, 2048, 0, 126),     # 40 queries, 68 tiles: 4 splits of 17, merged
+    (1, 40, 1536, 5, 127),     # 4 splits of 13 with growing logits, merged
 ])
 def test_attention_direct_rows(B, Tq, K, growth, seed):
     """bf16 latents and window, one workgroup walking 10 or more tiles per
@@ -491,6 +493,48 @@ def test_attention_direct_rows(B, Tq, K, growth, seed):
     o_ref, lse_ref = ref.attn(host["q"], host["lat"], sel, host["win"], host["q_pos"], host["sink"],
                               W, scale)
     check_close("attention out (direct rows)", bf16_to_np(out).reshape(o_ref.shape), o_ref, BF16_TOL)
+    assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3 * max(1.0, np.abs(lse_ref).max())
+
+
+def test_attention_direct_far_rows():
+    """Direct row loads of latents far into a large cache: rows at byte
+    offsets past 2 GiB and past 4 GiB of a 4.4 GB bf16 cache, so that row
+    addresses need all 64 bits (the low word's top bit set, a non-zero high
+    word).  Only the selected rows are written on the GPU; the oracle gets
+    those rows alone, with Sel renumbered to them, which is the same
+    computation."""
+    B, Tq, K, W, W_cap, n_small = 1, 192, 320, 128, 512, 2048
+    cfg = gen.shrink(gen.CONFIGS["tiny"], B=B, Tq=Tq, N=n_small, K=K, W=W, W_cap=W_cap,
+                     comp_T=0, seed=128)
+    inp = _inputs(cfg)
+    R = cfg.R
+    qp = _direct_q_pos(R, W_cap, W, 128).reshape(B, Tq)
+    inp["q_pos"] = torch.from_numpy(qp).cuda()
+    host = np_subset(inp)
+    # small row i -> cache row: i (near), 2^21 + i (past 2 GiB), 2^22 + 64 i (past 4 GiB)
+    i = np.arange(n_small, dtype=np.int64)
+    far = np.where(i % 3 == 0, i, np.where(i % 3 == 1, (1 << 21) + i, (1 << 22) + 64 * i))
+    n_big = (1 << 22) + 64 * n_small
+    big = torch.empty((1, n_big, 512), dtype=torch.bfloat16, device="cuda")
+    big[0, torch.from_numpy(far).cuda()] = inp["lat"][0]
+    rng = np.random.default_rng(128)
+    sel = np.full((R, K), -1, np.int32)
+    for r in range(R):
+        m = K - int(rng.integers(0, K // 4)) if r % 5 else K
+        sel[r, :m] = np.sort(rng.choice(n_small, m, replace=False))
+    sel_big = np.where(sel >= 0, far[np.maximum(sel, 0)], -1).astype(np.int32)
+    say(f"  far rows: cache {n_big} rows ({n_big * 1024 / 2**30:.2f} GiB), R={R}, K={K}")
+    out = torch.empty((R, 64, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((R, 64), dtype=torch.float32, device="cuda")
+    wsb = api.workspace_bytes(2, R, K, W)
+    ws = torch.empty((max(wsb, 16) // 4,), dtype=torch.float32, device="cuda")
+    api.sparse_attn(inp["q"], big, torch.from_numpy(sel_big).cuda(), inp["win"], inp["q_pos"],
+                    inp["sink"], W, cfg.scale, out, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    del big
+    o_ref, lse_ref = ref.attn(host["q"], host["lat"], sel, host["win"], host["q_pos"], host["sink"],
+                              W, cfg.scale)
+    check_close("attention out (far rows)", bf16_to_np(out).reshape(o_ref.shape), o_ref, BF16_TOL)
     assert np.abs(lse.cpu().numpy() - lse_ref).max() < 2e-3 * max(1.0, np.abs(lse_ref).max())
 
 
