@@ -28,6 +28,10 @@
 //     so the softmax statistics stay per lane; then
 //       O^T += V^T . P^T (dims x heads, K = 32 rows)
 //     whose B operand is exactly the P values the lane already holds.
+//   * with rows loaded straight into LDS (bf16 caches, many tiles per
+//     workgroup) PV is split by dims instead: each wave publishes its P^T
+//     operand in LDS and computes O^T for dims 128w .. 128w+127 of all 64
+//     heads, so each wave reads a quarter of the tile for PV.
 // FP8 window rows keep their per-token scale out of the MFMA: it multiplies
 // the logit of that row and its P weight.
 #include <algorithm>
