@@ -392,8 +392,11 @@ __device__ __forceinline__ f32x16 tile_mfma(const i32x8 (&qa)[2], const i32x8 (&
   return acc;
 }
 
+// The second launch bound is the minimum number of waves per SIMD: a block
+// of fewer than 8 waves must still leave room for two of them per SIMD
+// (without it a 4-wave bf16 block took 270 registers, one wave per SIMD).
 template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
-__global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
   using TK = TileKeys<KT>;
   constexpr bool MX = std::is_same<KT, KMx4>::value;
   constexpr int NT = NW * 64;
@@ -611,6 +614,16 @@ __global__ __launch_bounds__(NW * 64, 1) void tile_scan_kernel(ScanArgs a, int64
     masked(tt);
 }
 
+// one launch of the tile scan: NW waves of QW queries per block
+template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
+hipError_t launch_tile_scan(const ScanArgs& a, int64_t kpc, unsigned nchunks, int Tq, int B,
+                            hipStream_t s) {
+  constexpr int NQ = NW * QW;
+  dim3 grid(nchunks, (unsigned)((Tq + NQ - 1) / NQ), (unsigned)B);
+  hipLaunchKernelGGL((tile_scan_kernel<NW, QW, DEPTH, PIPE, KT>), grid, dim3(NW * 64), 0, s, a, kpc);
+  return hipGetLastError();
+}
+
 template <int QPB, bool FP8>
 hipError_t launch_scan_t(const ScanArgs& a, int B, dim3 grid, hipStream_t s) {
   if (FP8)
@@ -635,14 +648,17 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
     int64_t kpc = (n_cache + CH - 1) / CH;
     kpc = (kpc + TS_TILE - 1) / TS_TILE * TS_TILE;
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
-    dim3 grid(nchunks, (unsigned)((Tq + 15) / 16), (unsigned)B);
+    // 4-wave blocks of 2 queries per wave: two or more blocks per CU, so one
+    // block's tile barrier is covered by another's work (8-wave blocks, one
+    // per CU: bf16 2118-2145 -> 2079 us, FP8 1694-1708 -> 1639-1647).  The
+    // MXFP4 scan, whose MFMAs are shortest, goes unpipelined: 128 VGPRs, four
+    // waves per SIMD (1584-1592 -> 1105-1108 us; pipelined, three waves:
+    // 1197-1200).  One query per wave doubles the LDS operand reads per MFMA
+    // and loses (bf16 2425-2452).
     if (k_fmt == KEYS_MXFP4)
-      hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KMx4>), grid, dim3(512), 0, s, a, kpc);
-    else if (k_fp8)
-      hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KFp8>), grid, dim3(512), 0, s, a, kpc);
-    else
-      hipLaunchKernelGGL((tile_scan_kernel<8, 2, 2, true, KBf16>), grid, dim3(512), 0, s, a, kpc);
-    return hipGetLastError();
+      return launch_tile_scan<4, 2, 2, false, KMx4>(a, kpc, nchunks, Tq, B, s);
+    if (k_fp8) return launch_tile_scan<4, 2, 2, true, KFp8>(a, kpc, nchunks, Tq, B, s);
+    return launch_tile_scan<4, 2, 2, true, KBf16>(a, kpc, nchunks, Tq, B, s);
   }
   if (k_fmt == KEYS_MXFP4) return hipErrorInvalidValue;  // rejected before launch
   if (!k_fp8 && Tq >= 2) {
