@@ -371,9 +371,20 @@ __global__ __launch_bounds__(256, 1) void sparse_attn_kernel(AttnArgs a) {
       // that the low half is zero-extended, not sign-extended into the high
       const uint64_t ra = (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)a_lo, x) |
                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)a_hi, x) << 32);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint16_t*>(ra) + 8 * lane,
-                                       (__attribute__((address_space(3))) void*)&kvd[(TILE / 4) * wave + x][0],
-                                       16, 0, 0);
+      // Issued from asm: the compiler models this load as a pending flat LDS
+      // access and would then force every LDS wait of the tile's QK^T to
+      // zero; the loop waits for it explicitly (vmcnt(0), then a barrier).
+      // The row address was just written to scalar registers by v_readlane,
+      // and a memory instruction that reads them needs 5 wait states after
+      // that write: s_mov + s_nop 4 give 6.
+      const uint32_t ldsa = (uint32_t)(uintptr_t)&kvd[(TILE / 4) * wave + x][0];
+      asm volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "s_nop 4\n\t"
+          "global_load_lds_dwordx4 %1, %2"
+          :
+          : "s"(ldsa), "v"(16u * (uint32_t)lane), "s"(ra)
+          : "memory", "m0");
     }
     if (lane == 0) sm.vmask[buf][wave] = mask;
   };
