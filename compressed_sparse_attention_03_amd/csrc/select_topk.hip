@@ -319,17 +319,21 @@ struct CandStats {
 // out[0..2], the bin, the count in higher bins and the bin's count.  Only
 // wave 0 may call this; nothing is written if want exceeds the total.  Kept
 // out of line: inlined into the 1024-thread kernels it made the register
-// allocator spill.
+// allocator spill.  Its pointers are typed as LDS pointers, so that the
+// out-of-line body reads the histogram with LDS instructions rather than
+// generic (flat) loads.
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
 template <int NB>
-__device__ __noinline__ void wave_find_bin(const uint32_t* hist, uint32_t want, uint32_t* out) {
+__device__ __noinline__ void wave_find_bin_lds(lds_cu32* hist, uint32_t want, lds_u32* out) {
   constexpr int PL = NB / 64, NG = PL / 4;  // bins per lane, groups of 4 per lane
   const int lane = threadIdx.x & 63;
-  const uint32_t* mine = hist + NB - PL * (lane + 1);  // this lane's bins, ascending
+  lds_cu32* mine = hist + NB - PL * (lane + 1);  // this lane's bins, ascending
   uint32_t gsum[NG];
   uint32_t tot = 0;
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(mine + 4 * gi);
+    const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(mine + 4 * gi);
     gsum[gi] = x[0] + x[1] + x[2] + x[3];
     tot += gsum[gi];
   }
@@ -346,7 +350,7 @@ __device__ __noinline__ void wave_find_bin(const uint32_t* hist, uint32_t want, 
       }
       above += gsum[gi];
     }
-    const u32x4 x = *reinterpret_cast<const u32x4*>(mine + 4 * gsel);
+    const u32x4 x = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(mine + 4 * gsel);
     above = gabove;
 #pragma unroll
     for (int j = 3; j >= 0; --j) {
@@ -358,6 +362,12 @@ __device__ __noinline__ void wave_find_bin(const uint32_t* hist, uint32_t want, 
       above += x[j];
     }
   }
+}
+
+// Call sites pass their (LDS) histogram and result arrays through this.
+template <int NB>
+__device__ __forceinline__ void wave_find_bin(const uint32_t* hist, uint32_t want, uint32_t* out) {
+  wave_find_bin_lds<NB>((lds_cu32*)hist, want, (lds_u32*)out);
 }
 
 struct FinishSmem {
