@@ -492,13 +492,14 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void tile_scan_kernel(Sca
   };
   // the epilogue of one tile: ReLU . w . head sum, causal mask, block max
   auto epi = [&](int t0, const Accs& A) {
-    const int p = t0 + kn;  // this lane's key
+    const int p = t0 + kn;  // this lane's key (non-negative: 32-bit unsigned offsets)
+    const uint32_t pu = (uint32_t)p;
     auto finish = [&](float s, int nv_l, bool ok_l, int64_t row_l, float* bm_l) {
       s = p < nv_l ? s : -INFINITY;
-      if (a.scores && ok_l && p < k1) a.scores[row_l * a.s_stride + p] = s;
+      if (a.scores && ok_l && p < k1) a.scores[row_l * a.s_stride + pu] = s;
       if (a.block_max) {
         const float m = max_of_8_lanes(s);
-        if (ok_l && (kn & 7) == 0 && p < k1) bm_l[p >> 3] = m;
+        if (ok_l && (kn & 7) == 0 && p < k1) bm_l[pu >> 3] = m;
       }
     };
     if constexpr (QW % 2 == 0) {

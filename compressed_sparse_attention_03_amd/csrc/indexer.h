@@ -170,10 +170,15 @@ __device__ __forceinline__ constexpr int64_t key_elem_bytes() {
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Max over each group of 8 consecutive lanes, by DPP within the lanes' row.
+// Each moved value goes through "+ 0.0f" (exact for every score: finite,
+// -inf; -0 becomes +0, which no maximum tells apart): the result of an add
+// is known to be canonical, so IEEE-mode fmaxf needs no canonicalising
+// v_max_f32 of its own for it (two instead of four instructions a step,
+// the DPP folding into the add).
 __device__ __forceinline__ float max_of_8_lanes(float m) {
-  m = fmaxf(m, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(m))));   // quad_perm [1,0,3,2]
-  m = fmaxf(m, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(m))));   // quad_perm [2,3,0,1]
-  return fmaxf(m, __uint_as_float(dpp_mov<0x141>(__float_as_uint(m))));  // row_half_mirror
+  m = fmaxf(m, __uint_as_float(dpp_perm<0xB1>(__float_as_uint(m))) + 0.0f);   // quad_perm [1,0,3,2]
+  m = fmaxf(m, __uint_as_float(dpp_perm<0x4E>(__float_as_uint(m))) + 0.0f);   // quad_perm [2,3,0,1]
+  return fmaxf(m, __uint_as_float(dpp_perm<0x141>(__float_as_uint(m))) + 0.0f);  // row_half_mirror
 }
 
 // ---- the fused contraction + epilogue -------------------------------------
