@@ -111,15 +111,6 @@ __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
-// The same for a control that gives every lane a source lane inside its
-// row (quad_perm, row_half_mirror, row_mirror): no lane keeps its old value,
-// so none is supplied, which lets the compiler fold the move into the
-// instruction that uses it.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_perm(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-
 template <typename F>
 __device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, F op) {
   v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]

@@ -392,11 +392,19 @@ __device__ __forceinline__ f32x16 tile_mfma(const i32x8 (&qa)[2], const i32x8 (&
   return acc;
 }
 
-// The second launch bound is the minimum number of waves per SIMD: a block
-// of fewer than 8 waves must still leave room for two of them per SIMD
-// (without it a 4-wave bf16 block took 270 registers, one wave per SIMD).
+// The second launch bound is the minimum number of waves per SIMD.  An
+// 8-wave block runs one per CU.  A smaller block must leave room for at
+// least two waves per SIMD (without it a 4-wave bf16 block took 270
+// registers, one wave per SIMD); FP8 keys take three (168 registers, the
+// tile loop free of spills: 1.66 -> 1.37 ms on an 8192-query prefill against
+// two), MXFP4 keys four (128 registers; a fifth wave spills in the loop).
+template <int NW, typename KT>
+constexpr int tile_scan_min_waves() {
+  return NW >= 8 ? 1 : std::is_same<KT, KFp8>::value ? 3 : std::is_same<KT, KMx4>::value ? 4 : 2;
+}
+
 template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
+__global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
   using TK = TileKeys<KT>;
   constexpr bool MX = std::is_same<KT, KMx4>::value;
   constexpr int NT = NW * 64;

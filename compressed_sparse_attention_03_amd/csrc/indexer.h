@@ -169,16 +169,23 @@ __device__ __forceinline__ constexpr int64_t key_elem_bytes() {
 // v_max_f32 per input in IEEE mode.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Max over each group of 8 consecutive lanes, by DPP within the lanes' row.
-// Each moved value goes through "+ 0.0f" (exact for every score: finite,
-// -inf; -0 becomes +0, which no maximum tells apart): the result of an add
-// is known to be canonical, so IEEE-mode fmaxf needs no canonicalising
-// v_max_f32 of its own for it (two instead of four instructions a step,
-// the DPP folding into the add).
+// Max over each group of 8 consecutive lanes, by DPP within the lanes' row:
+// three v_max_f32 whose first operand is the DPP-moved value (quad_perm
+// [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror).  Written as asm because
+// in IEEE mode the compiler does not fold a DPP move into fmaxf: it needs
+// the moved value canonical and adds an instruction per step to make it so
+// (three per step instead of one).  Each DPP read follows its source's VALU
+// write by two wait states (s_nop 1).  Requires every lane of the wave
+// active and no NaN inputs (scores are finite or -inf); max(-0, +0) = +0,
+// which no maximum tells apart.
 __device__ __forceinline__ float max_of_8_lanes(float m) {
-  m = fmaxf(m, __uint_as_float(dpp_perm<0xB1>(__float_as_uint(m))) + 0.0f);   // quad_perm [1,0,3,2]
-  m = fmaxf(m, __uint_as_float(dpp_perm<0x4E>(__float_as_uint(m))) + 0.0f);   // quad_perm [2,3,0,1]
-  return fmaxf(m, __uint_as_float(dpp_perm<0x141>(__float_as_uint(m))) + 0.0f);  // row_half_mirror
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
+      : "=&v"(r)
+      : "v"(m));
+  return r;
 }
 
 // ---- the fused contraction + epilogue -------------------------------------
