@@ -188,8 +188,16 @@ __device__ __forceinline__ float across_rows(float v, F op) {
 __device__ __forceinline__ float sum_across_rows(float v) {
   return across_rows(v, [](float x, float y) { return x + y; });
 }
+// max of two floats as one v_max_f32: in IEEE mode fmaxf first makes each
+// operand that is not known to be canonical (a value moved between lanes)
+// canonical, one more instruction each.  Not for NaN operands.
+__device__ __forceinline__ float fmax_nc(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
 __device__ __forceinline__ float max_across_rows(float v) {
-  return across_rows(v, [](float x, float y) { return fmaxf(x, y); });
+  return across_rows(v, [](float x, float y) { return fmax_nc(x, y); });
 }
 
 }  // namespace csa2
