@@ -1322,8 +1322,18 @@ struct ManySmem {
   int32_t blk[GATHER ? E * MT / BLK : 1];  // the row's block list (gather mode)
 };
 
+// Minimum waves per SIMD (the launch bound's second argument): the gather
+// of 16K candidates per row (E = 32, 512 threads) asks for three
+// workgroups per CU (80 registers, a 16-byte spill) instead of the two its
+// 98 registers allowed -- more rows' score loads in flight: 296 -> 272 us
+// on an 8192-row prefill stage.  The other shapes already fit.
+template <int MT, int E, bool GATHER>
+constexpr int many_min_waves() {
+  return (GATHER && MT == 512 && E >= 32) ? 6 : 1;
+}
+
 template <int MT, int E, bool GATHER, bool IDS>
-__global__ __launch_bounds__(MT) void select_many_kernel(SelArgs a, GatherSrc gs) {
+__global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_many_kernel(SelArgs a, GatherSrc gs) {
   __shared__ ManySmem<MT, E, GATHER> sm;
   constexpr int NW = MT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
