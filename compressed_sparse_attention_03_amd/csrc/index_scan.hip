@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 // (v_permlane32_swap; with two queries one swap serves both, each half of
 // the wave then finishing one query), causal mask, max over each 8-key block
 // by three DPP steps.
-// Prefill (thousands of queries, MFMA-bound): 8 waves x 2 queries, 8 key
+// Prefill (thousands of queries, MFMA-bound): 4 waves x 2 queries, 8 key
 // ranges with the range as the block id's low index, so that each XCD keeps
 // "its" range resident in L2 while all query groups stream through it.
 // Verification decode (a few queries per sequence, HBM-bound): 8 waves x 1

@@ -1,0 +1,160 @@
+"""GPU parity at the largest cache the indexer accepts: 2^27 latents of one
+sequence (32 GiB of bf16 index keys, 2^24 blocks of 8), the limit that
+csa2_index_scores, csa2_select_topk and csa2_gather_select check.  Key byte
+offsets pass 2^32 here and key positions reach 2^27 - 1, so every 64-bit
+offset computation of the scan, candidate and top-k kernels runs at its
+maximum.
+
+One cache serves three passes over it:
+- the decode chain for one query (t = 2^28 - 1, everything visible): the
+  scan's block maxima, the block top-2048 over the 2^24 maxima with the
+  newest block kept, the candidate indexer over the chosen blocks and the
+  position top-512;
+- the verification scan (5 draft queries) and the prefill scan (64
+  consecutive queries whose horizons end inside the last four blocks).
+
+The oracle scores compact copies of the rows it needs: sampled blocks
+spread over the whole cache (first, last, around 2^21, 2^23 and 2^24 - 1,
+and seeded random ones) plus the cache's last 64 rows, with each query's
+horizon mapped into the compact array.  The block top-k is checked on the
+full row of block maxima, the candidate scores bit-exactly over all 16,384
+candidates.  Inputs are the integer-valued index queries and keys in
+[-3, 3] and head weights k/16 of the other configs; skipped when the GPU
+has less than 40 GiB free.
+"""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_attention_03_amd import api, gen
+from oracle import csa2_ref as ref
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+N = 1 << 27          # latents: the indexer's limit (2^24 blocks of 8)
+NB = N // 8
+HI, DI = 32, 128
+K_B, K = 2048, 512
+TAIL = 64            # the cache's last rows, copied whole to the oracle
+CHUNK_ROWS = 1 << 21
+
+
+def _keys(g):
+    k = torch.empty((1, N, DI), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, N, CHUNK_ROWS):
+        k[0, r0:r0 + CHUNK_ROWS] = torch.randint(-3, 4, (CHUNK_ROWS, DI), generator=g, device="cuda",
+                                                 dtype=torch.int32).to(torch.bfloat16)
+    return k
+
+
+def _queries(g, tq):
+    q = torch.randint(-3, 4, (1, tq, HI, DI), generator=g, device="cuda",
+                      dtype=torch.int32).to(torch.bfloat16)
+    w = torch.randint(1, 17, (1, tq, HI), generator=g, device="cuda",
+                      dtype=torch.int32).to(torch.float32) / 16.0
+    return q, w
+
+
+def _sample_blocks(rng, count):
+    fixed = [0, 1, 2, (1 << 21) - 1, 1 << 21, (1 << 23) + 5, (1 << 24) - 9, NB - TAIL // 8 - 1]
+    rnd = rng.choice(NB - TAIL // 8, size=count - len(fixed), replace=False)
+    return np.unique(np.concatenate([np.array(fixed, np.int64), rnd.astype(np.int64)]))
+
+
+def _compact(keys, blocks):
+    """Host bit patterns of the rows of `blocks`, then the cache's last TAIL rows."""
+    rows = (torch.from_numpy(blocks).cuda()[:, None] * 8 + torch.arange(8, device="cuda")).reshape(-1)
+    inner = keys[0].index_select(0, rows)
+    tail = keys[0, N - TAIL:]
+    return gen.to_numpy(torch.cat([inner, tail]))[None]   # [1][8*len(blocks)+TAIL][128] uint16
+
+
+def _check_block_max(name, keys, q, w, q_pos, bm, blocks):
+    """Block maxima of sampled blocks and of the last TAIL/8 blocks against
+    the oracle on the compact rows; each query's horizon is mapped so that
+    the same rows of the tail stay visible."""
+    kc = _compact(keys, blocks)
+    n_in = 8 * len(blocks)
+    n_vis = np.minimum(N, (q_pos.cpu().numpy() + 1) // 2)      # [1][Tq]
+    assert np.all(n_vis >= N - TAIL)
+    qp_c = 2 * (n_in + TAIL - (N - n_vis)) - 1                   # the same rows visible
+    _, bm_ref = ref.scan(gen.to_numpy(q), gen.to_numpy(w), kc, qp_c)
+    want = np.concatenate([blocks, np.arange(NB - TAIL // 8, NB)])
+    got = bm[:, torch.from_numpy(want).cuda()].cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, bm_ref), f"{name}: block maxima"
+    say(f"  {name}: block maxima of {len(want)} blocks x {bm.shape[0]} queries bit-exact")
+
+
+@pytest.fixture(scope="module")
+def cache():
+    free, _ = torch.cuda.mem_get_info()
+    if free < (40 << 30):
+        pytest.skip(f"needs 40 GiB of free GPU memory, {free >> 30} GiB free")
+    say(f"[gen] max-size cache: 1 sequence x {N} bf16 index keys ({N * DI * 2 >> 30} GiB)")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2027)
+    keys = _keys(g)
+    torch.cuda.synchronize()
+    yield g, keys
+    del keys
+    torch.cuda.empty_cache()
+
+
+def test_max_cache_decode_chain(cache):
+    g, keys = cache
+    rng = np.random.default_rng(7)
+    q, w = _queries(g, 1)
+    t = 2 * N - 1
+    q_pos = torch.full((1, 1), t, dtype=torch.int64, device="cuda")
+    bm = torch.empty((1, NB), dtype=torch.float32, device="cuda")
+    say("[run] scan, block top-2048, candidate indexer, position top-512 at 2^27 latents")
+    api.index_scan(q, w, keys, q_pos, block_max=bm)
+    blocks = torch.empty((1, K_B), dtype=torch.int32, device="cuda")
+    api.select_topk(bm, K_B, blocks, force_last=True)
+    csc = torch.empty((1, K_B * 8), dtype=torch.float32, device="cuda")
+    cid = torch.empty((1, K_B * 8), dtype=torch.int32, device="cuda")
+    api.index_cand(q, w, keys, q_pos, blocks, csc, cid)
+    sel = torch.empty((1, K), dtype=torch.int32, device="cuda")
+    api.select_topk(csc, K, sel, ids=cid)
+    torch.cuda.synchronize()
+
+    _check_block_max("decode scan", keys, q, w, q_pos, bm, _sample_blocks(rng, 512))
+
+    # the block stage over the whole row of 2^24 maxima
+    bm_h = bm.cpu().numpy().astype(np.float64)
+    blk_ref = ref.select(bm_h, K_B, forced=np.array([ref.newest_block(t, N)], np.int32))
+    blk = blocks.cpu().numpy()
+    assert np.array_equal(blk, blk_ref), "block selection"
+    assert blk[0, -1] == NB - 1
+    say(f"  block top-{K_B} of {NB} bit-exact (largest ids {blk[0, -3:].tolist()})")
+
+    # the candidates: the chosen blocks' rows in their order, all visible
+    kc = _compact(keys, blk[0].astype(np.int64))[:, :K_B * 8]
+    qp_c = np.array([[2 * K_B * 8 - 1]], np.int64)
+    csc_ref, cid_c = ref.cand(gen.to_numpy(q), gen.to_numpy(w), kc, qp_c,
+                              np.arange(K_B, dtype=np.int32)[None])
+    cid_ref = np.where(cid_c >= 0, blk[0][cid_c // 8].astype(np.int64) * 8 + cid_c % 8, -1)
+    assert np.array_equal(cid.cpu().numpy().astype(np.int64), cid_ref), "candidate ids"
+    assert np.array_equal(csc.cpu().numpy().astype(np.float64), csc_ref), "candidate scores"
+
+    sel_ref = ref.select(csc.cpu().numpy().astype(np.float64), K, ids=cid.cpu().numpy())
+    assert np.array_equal(sel.cpu().numpy(), sel_ref), "position selection"
+    say(f"  {K_B * 8} candidate scores and the top-{K} positions bit-exact "
+        f"(largest {sel_ref[0, -2:].tolist()})")
+
+
+@pytest.mark.parametrize("tq", [5, 64])
+def test_max_cache_multi_query_scan(cache, tq):
+    """tq = 5: the verification scan; tq = 64: the prefill scan (4-wave
+    blocks, 8 key ranges of 2^24 keys)."""
+    g, keys = cache
+    rng = np.random.default_rng(100 + tq)
+    q, w = _queries(g, tq)
+    # horizons N - 32 + (j + 1) // 2: the last four blocks partly visible
+    q_pos = torch.arange(2 * N - 64, 2 * N - 64 + tq, dtype=torch.int64, device="cuda")[None]
+    bm = torch.empty((tq, NB), dtype=torch.float32, device="cuda")
+    say(f"[run] scan of {tq} queries at 2^27 latents")
+    api.index_scan(q, w, keys, q_pos, block_max=bm)
+    torch.cuda.synchronize()
+    _check_block_max(f"scan, {tq} queries", keys, q, w, q_pos, bm, _sample_blocks(rng, 256))
