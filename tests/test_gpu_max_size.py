@@ -21,6 +21,11 @@ full row of block maxima, the candidate scores bit-exactly over all 16,384
 candidates.  Inputs are the integer-valued index queries and keys in
 [-3, 3] and head weights k/16 of the other configs; skipped when the GPU
 has less than 40 GiB free.
+
+The compressor (bf16 and NVFP4 rows) runs once over 2^23 + 2 raw tokens of
+one sequence (8 GiB each of tokens and gate logits, byte offsets past 2^33),
+checked at sampled latents and the last one against the oracle's pooling of
+the same token pairs.
 """
 import numpy as np
 import pytest
@@ -28,7 +33,7 @@ import torch
 
 from compressed_sparse_attention_03_amd import api, gen
 from oracle import csa2_ref as ref
-from tests.gpu_util import say
+from tests.gpu_util import BF16_TOL, check_close, check_fp4_pooling, say
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +163,52 @@ def test_max_cache_multi_query_scan(cache, tq):
     api.index_scan(q, w, keys, q_pos, block_max=bm)
     torch.cuda.synchronize()
     _check_block_max(f"scan, {tq} queries", keys, q, w, q_pos, bm, _sample_blocks(rng, 256))
+
+
+T_BIG = (1 << 23) + 2   # raw tokens: 2^22 + 1 latents
+
+
+def _normal_rows(g, rows):
+    x = torch.empty((1, rows, 512), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, rows, CHUNK_ROWS):
+        r1 = min(rows, r0 + CHUNK_ROWS)
+        x[0, r0:r1] = torch.randn((r1 - r0, 512), generator=g, device="cuda").to(torch.bfloat16)
+    return x
+
+
+def test_large_compress():
+    free, _ = torch.cuda.mem_get_info()
+    if free < (30 << 30):
+        pytest.skip(f"needs 30 GiB of free GPU memory, {free >> 30} GiB free")
+    G = T_BIG // 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2029)
+    say(f"[gen] compressor input: 1 sequence x {T_BIG} raw tokens (2 x {T_BIG * 1024 >> 30} GiB)")
+    raw, gate = _normal_rows(g, T_BIG), _normal_rows(g, T_BIG)
+    out = torch.empty((1, G, 512), dtype=torch.bfloat16, device="cuda")
+    codes = torch.empty((1, G, 256), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, G, 32), dtype=torch.uint8, device="cuda")
+    say("[run] compress (bf16 rows) and compress_nvfp4 over 2^22 + 1 latents")
+    api.compress(raw, gate, out)
+    api.compress_nvfp4(raw, gate, codes, scales)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(11)
+    lat = np.unique(np.concatenate([[0, 1, (1 << 21) + 3, (1 << 22) - 1, G - 1],
+                                    rng.choice(G, 507, replace=False)])).astype(np.int64)
+    li = torch.from_numpy(lat).cuda()
+    pairs = (li[:, None] * 2 + torch.arange(2, device="cuda")).reshape(-1)
+    raw_h = gen.to_numpy(raw[0].index_select(0, pairs))[None]
+    gate_h = gen.to_numpy(gate[0].index_select(0, pairs))[None]
+    del raw, gate
+    bits, y64 = ref.compress(raw_h, gate_h)
+    got = out[0].index_select(0, li).float().cpu().numpy().astype(np.float64)[None]
+    check_close("compress at 2^22 + 1 latents", got, y64, BF16_TOL)
+    x = ref.bf16_array(raw_h).reshape(1, len(lat), 2, 512)
+    slack = 1e-6 * (np.abs(x[:, :, 0]) + np.abs(x[:, :, 1]))
+    assert np.all(np.abs(got - y64) <= np.abs(y64) * 2 ** -8 + slack)
+    nd = check_fp4_pooling("compress_nvfp4 at 2^22 + 1 latents",
+                           codes[0].index_select(0, li).cpu().numpy()[None],
+                           scales[0].index_select(0, li).cpu().numpy()[None], raw_h, gate_h)
+    assert sum(nd) <= max(1, len(lat) * 512 // 100000)
+    say(f"  {len(lat)} sampled latents (last {int(lat[-1])}) within one bf16 rounding; NVFP4 rows as the oracle's")
