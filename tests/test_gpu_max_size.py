@@ -22,6 +22,10 @@ candidates.  Inputs are the integer-valued index queries and keys in
 [-3, 3] and head weights k/16 of the other configs; skipped when the GPU
 has less than 40 GiB free.
 
+FP8 E4M3 and MXFP4 index keys get the same size: the FP8 decode scan (1
+and 5 queries) and the prefill scans of both formats (64 queries), checked
+at sampled blocks and the last blocks.
+
 The compressor (bf16 and NVFP4 rows) runs once over 2^23 + 2 raw tokens of
 one sequence (8 GiB each of tokens and gate logits, byte offsets past 2^33),
 checked at sampled latents and the last one against the oracle's pooling of
@@ -68,11 +72,14 @@ def _sample_blocks(rng, count):
 
 
 def _compact(keys, blocks):
-    """Host bit patterns of the rows of `blocks`, then the cache's last TAIL rows."""
+    """Host copies of the rows of `blocks`, then the cache's last TAIL rows
+    ([1][8*len(blocks)+TAIL][...]); an MXFP4 (codes, scales) pair gives a pair."""
+    if isinstance(keys, tuple):
+        return tuple(_compact(k, blocks) for k in keys)
     rows = (torch.from_numpy(blocks).cuda()[:, None] * 8 + torch.arange(8, device="cuda")).reshape(-1)
     inner = keys[0].index_select(0, rows)
     tail = keys[0, N - TAIL:]
-    return gen.to_numpy(torch.cat([inner, tail]))[None]   # [1][8*len(blocks)+TAIL][128] uint16
+    return gen.to_numpy(torch.cat([inner, tail]))[None]
 
 
 def _check_block_max(name, keys, q, w, q_pos, bm, blocks):
@@ -135,7 +142,7 @@ def test_max_cache_decode_chain(cache):
     say(f"  block top-{K_B} of {NB} bit-exact (largest ids {blk[0, -3:].tolist()})")
 
     # the candidates: the chosen blocks' rows in their order, all visible
-    kc = _compact(keys, blk[0].astype(np.int64))[:, :K_B * 8]
+    kc = _compact(keys, blk[0].astype(np.int64))[:, :K_B * 8]  # the tail rows dropped
     qp_c = np.array([[2 * K_B * 8 - 1]], np.int64)
     csc_ref, cid_c = ref.cand(gen.to_numpy(q), gen.to_numpy(w), kc, qp_c,
                               np.arange(K_B, dtype=np.int32)[None])
@@ -212,3 +219,46 @@ def test_large_compress():
                            scales[0].index_select(0, li).cpu().numpy()[None], raw_h, gate_h)
     assert sum(nd) <= max(1, len(lat) * 512 // 100000)
     say(f"  {len(lat)} sampled latents (last {int(lat[-1])}) within one bf16 rounding; NVFP4 rows as the oracle's")
+
+
+def _lowp_keys(g, fmt):
+    if fmt == "fp8":
+        k = torch.empty((1, N, DI), dtype=torch.uint8, device="cuda")
+        for r0 in range(0, N, CHUNK_ROWS):
+            x = torch.randint(-3, 4, (CHUNK_ROWS, DI), generator=g, device="cuda", dtype=torch.int32)
+            k[0, r0:r0 + CHUNK_ROWS] = x.to(torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+        return k, None
+    codes = torch.empty((1, N, DI // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((1, N, DI // 32), dtype=torch.uint8, device="cuda")
+    for r0 in range(0, N, CHUNK_ROWS):
+        codes[0, r0:r0 + CHUNK_ROWS] = torch.randint(0, 256, (CHUNK_ROWS, DI // 2), generator=g,
+                                                     device="cuda", dtype=torch.int32).to(torch.uint8)
+        scales[0, r0:r0 + CHUNK_ROWS] = torch.randint(126, 128, (CHUNK_ROWS, DI // 32), generator=g,
+                                                      device="cuda", dtype=torch.int32).to(torch.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("fmt,tqs", [("fp8", (1, 5, 64)), ("mxfp4", (64,))])
+def test_max_cache_lowp_scan(fmt, tqs):
+    """FP8 keys (E4M3 codes, the decode scan for 1 and 5 queries and the
+    prefill scan) and MXFP4 keys (E2M1 codes with E8M0 scales 2^-1 / 2^0,
+    the prefill scan) over 2^27 latents."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < (24 << 30):
+        pytest.skip(f"needs 24 GiB of free GPU memory, {free >> 30} GiB free")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(2031 if fmt == "fp8" else 2033)
+    say(f"[gen] max-size cache: 1 sequence x {N} {fmt} index keys")
+    k, k_scale = _lowp_keys(g, fmt)
+    keys = k if k_scale is None else (k, k_scale)
+    rng = np.random.default_rng(300)
+    for tq in tqs:
+        q, w = _queries(g, tq)
+        q_pos = torch.arange(2 * N - 64, 2 * N - 64 + tq, dtype=torch.int64, device="cuda")[None]
+        bm = torch.empty((tq, NB), dtype=torch.float32, device="cuda")
+        say(f"[run] {fmt} scan of {tq} queries at 2^27 latents")
+        api.index_scan(q, w, k, q_pos, block_max=bm, k_scale=k_scale)
+        torch.cuda.synchronize()
+        _check_block_max(f"{fmt} scan, {tq} queries", keys, q, w, q_pos, bm, _sample_blocks(rng, 256))
+    del k, k_scale, keys
+    torch.cuda.empty_cache()
