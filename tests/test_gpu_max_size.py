@@ -26,6 +26,11 @@ FP8 E4M3 and MXFP4 index keys get the same size: the FP8 decode scan (1
 and 5 queries) and the prefill scans of both formats (64 queries), checked
 at sampled blocks and the last blocks.
 
+The prefill's fused candidate gather + position top-512 reads a score
+matrix of 2 rows x 2^27 latents (few rows: one workgroup per row) and of
+1100 rows x 2^22 latents (the many-rows kernel, row offsets past 16 GiB),
+block ids spread up to the last block and past the cache.
+
 The compressor (bf16 and NVFP4 rows) runs once over 2^23 + 2 raw tokens of
 one sequence (8 GiB each of tokens and gate logits, byte offsets past 2^33),
 checked at sampled latents and the last one against the oracle's pooling of
@@ -261,4 +266,58 @@ def test_max_cache_lowp_scan(fmt, tqs):
         torch.cuda.synchronize()
         _check_block_max(f"{fmt} scan, {tq} queries", keys, q, w, q_pos, bm, _sample_blocks(rng, 256))
     del k, k_scale, keys
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("R,n,seed", [(2, N, 80), (1100, 1 << 22, 81)])
+def test_max_gather_select(R, n, seed):
+    """The one-pass gather + position top-k over a large score matrix equals
+    gather_scores + select_topk and the oracle's selection over the same
+    candidates (gathered on the host from the same scores)."""
+    free, _ = torch.cuda.mem_get_info()
+    if free < R * n * 4 + (4 << 30):
+        pytest.skip(f"needs {(R * n * 4 >> 30) + 4} GiB of free GPU memory, {free >> 30} GiB free")
+    rng = np.random.default_rng(seed)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    say(f"[gen] score matrix {R} x {n} ({R * n * 4 >> 30} GiB)")
+    all_s = torch.empty((R, n), dtype=torch.float32, device="cuda")
+    step = max(1, (1 << 26) // n)
+    for r0 in range(0, R, step):
+        r1 = min(R, r0 + step)
+        all_s[r0:r1] = torch.randint(0, 60, (r1 - r0, n), generator=g, device="cuda",
+                                     dtype=torch.int32).to(torch.float32) / 16.0
+    nblk = n // 8
+    kb, k = 2048, 512
+    blocks = np.full((R, kb), -1, np.int32)
+    for r in range(R):
+        m = int(rng.integers(kb // 2, kb + 1)) - 4
+        pick = np.unique(np.concatenate([rng.integers(0, nblk, m), [0, nblk - 1]]))
+        blocks[r, :len(pick)] = pick
+        blocks[r, len(pick):len(pick) + 3] = [1 << 28, 1 << 30, 2**31 - 1]  # past the cache
+    # horizons: most rows see everything, some end inside the last blocks
+    q_pos = np.where(rng.random(R) < 0.7, 2 * n - 1, 2 * n - 1 - rng.integers(0, 200, R)).astype(np.int64)
+    qp = torch.from_numpy(q_pos[None]).cuda()
+    b_t = torch.from_numpy(blocks).cuda()
+    say(f"[run] gather + top-{k} of {kb} blocks per row over {R} x {n} scores")
+    fused = torch.full((R, k), -7, dtype=torch.int32, device="cuda")
+    api.gather_select(all_s, qp, b_t, k, fused, n_cache=n)
+    sc = torch.empty((R, kb * 8), dtype=torch.float32, device="cuda")
+    ids = torch.empty((R, kb * 8), dtype=torch.int32, device="cuda")
+    api.gather_scores(all_s, qp, b_t, sc, ids, n_cache=n)
+    two = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    api.select_topk(sc, k, two, ids=ids)
+    torch.cuda.synchronize()
+    got = fused.cpu().numpy()
+    assert np.array_equal(got, two.cpu().numpy()), "fused != gather + select"
+    # oracle: the candidates gathered on the host side of the same scores
+    nv = np.minimum((q_pos + 1) // 2, n)
+    pos = blocks[:, :, None].astype(np.int64) * 8 + np.arange(8)
+    ok = (blocks[:, :, None] >= 0) & (pos < nv[:, None, None])
+    vals = torch.gather(all_s, 1, torch.from_numpy(np.clip(pos, 0, n - 1).reshape(R, -1)).cuda())
+    cs = np.where(ok.reshape(R, -1), vals.cpu().numpy().astype(np.float64), -np.inf)
+    cid = np.where(ok, pos, -1).reshape(R, -1).astype(np.int32)
+    assert np.array_equal(got, ref.select(cs, k, ids=cid)), "fused != oracle selection"
+    say(f"  gather+select fused at {R} x {n}: bit-exact (largest kept id {int(got.max())})")
+    del all_s
     torch.cuda.empty_cache()
