@@ -460,17 +460,41 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
   }
   // staging: piece u*NT + tid of a tile -> row / PPR, 16-byte piece % PPR
   const int kend = min(k1, max(k0, nv_blk));  // keys that need computing
-  // rows past kend repeat row kend - 1: every query of the block masks them
-  // (p >= kend means p >= k1 or p >= every query's horizon)
+  // bf16 and MXFP4 keys: the block's key range [k0, k1) (and the MXFP4
+  // scale words) as buffer resources, a load's offset a per-lane constant
+  // plus the tile's offset in a scalar register, so the loop computes no
+  // addresses (the launcher keeps a range below 2^31 bytes); rows past k1
+  // read as zeros.  FP8 keys keep 64-bit addresses, rows past kend
+  // repeating row kend - 1: measured faster for them (1.36-1.37 against
+  // 1.40 ms on an 8192-query prefill), where the buffer loads gave bf16
+  // 2.08-2.10 -> 2.05 ms, MXFP4 1.09 -> 1.08 ms and the verification scan
+  // 300 -> 284-288 us.  Whatever a row past kend holds, every query of the
+  // block masks it (p >= kend means p >= k1 or p >= every query's horizon).
+  constexpr bool BUF = !std::is_same<KT, KFp8>::value;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kb + (int64_t)k0 * TK::ROWB), (short)0, (k1 - k0) * TK::ROWB, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      MX ? const_cast<uint32_t*>(ksb + k0) : nullptr, (short)0, MX ? (k1 - k0) * 4 : 0, BUF_DWORD3);
+  uint32_t voff[LPT];
+#pragma unroll
+  for (int u = 0; u < LPT; ++u) {
+    const int pc = u * NT + tid;
+    voff[u] = pc < PIECES ? (uint32_t)((pc / PPR) * TK::ROWB + 16 * (pc % PPR))
+                          : (uint32_t)(4 * (pc - PIECES));
+  }
   auto load_tile = [&](int t0, u32x4 (&v)[LPT]) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int pc = u * NT + tid;
-      const int row = min(t0 + pc / PPR, kend - 1);
-      if (pc < PIECES)
+      if constexpr (BUF) {
+        if (pc < PIECES)
+          v[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, voff[u], (uint32_t)(t0 - k0) * TK::ROWB, 0);
+        else if (MX && pc < PIECES + TS_TILE)  // one key's scale word
+          v[u][0] = __builtin_amdgcn_raw_buffer_load_b32(srs, voff[u], (uint32_t)(t0 - k0) * 4u, 0);
+      } else if (pc < PIECES) {
+        const int row = min(t0 + pc / PPR, kend - 1);
         v[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)row * TK::ROWB + 16 * (pc % PPR));
-      else if (MX && pc < PIECES + TS_TILE)  // one key's scale word
-        v[u][0] = ksb[min(t0 + pc - PIECES, kend - 1)];
+      }
     }
   };
   auto store_tile = [&](uint8_t* tile, const u32x4 (&v)[LPT]) {
@@ -623,6 +647,13 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
     masked(tt);
 }
 
+// Longest key range of one tile-scan block: its bytes stay below 2^31, the
+// reach of the block's buffer resource (bf16 keys: 2^23 - 32 keys).
+int64_t tile_scan_max_keys(int k_fmt) {
+  const int64_t row = k_fmt == KEYS_MXFP4 ? 64 : k_fmt == KEYS_FP8 ? 128 : 256;
+  return (INT32_MAX / row) / TS_TILE * TS_TILE;
+}
+
 // one launch of the tile scan: NW waves of QW queries per block
 template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
 hipError_t launch_tile_scan(const ScanArgs& a, int64_t kpc, unsigned nchunks, int Tq, int B,
@@ -656,6 +687,7 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
     constexpr int CH = 8;
     int64_t kpc = (n_cache + CH - 1) / CH;
     kpc = (kpc + TS_TILE - 1) / TS_TILE * TS_TILE;
+    kpc = min(kpc, tile_scan_max_keys(k_fmt));
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
     // 4-wave blocks of 2 queries per wave: two or more blocks per CU, so one
     // block's tile barrier is covered by another's work (8-wave blocks, one
@@ -678,7 +710,7 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
     int64_t ch = (1024 + B * groups - 1) / (B * groups);
     if (ch > n_tiles32) ch = n_tiles32;
     if (ch < 1) ch = 1;
-    const int64_t kpc = (n_tiles32 + ch - 1) / ch * TS_TILE;
+    const int64_t kpc = min((n_tiles32 + ch - 1) / ch * TS_TILE, tile_scan_max_keys(k_fmt));
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
     dim3 grid(nchunks, (unsigned)groups, (unsigned)B);
     hipLaunchKernelGGL((tile_scan_kernel<8, 1, 6, false, KBf16>), grid, dim3(512), 0, s, a, kpc);
