@@ -233,16 +233,19 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 // l % 32 and heads 8(i/4) + 4(l/32) + i%4 of accumulator element i.  Lane
 // half h = l / 32 supplies the same dims of A and B (the dot product does not
 // care which dims a k-slot carries).
-// Each wave issues the MFMAs of all its queries before their epilogues, so
-// the epilogue of one query runs on the vector ALU while the matrix core
-// works on the next.  Epilogue per query and 32 keys: ReLU x w_h over the
+// Each wave issues the MFMAs of all its queries before their epilogues (the
+// pipelined loop also issues the next tile's before this tile's epilogue),
+// so no epilogue waits on the MFMA chain it follows; on one SIMD the MFMAs
+// and the vector epilogue still mostly take turns.  Epilogue per query and
+// 32 keys: ReLU x w_h over the
 // lane's 16 heads, the other 16 from the partner half by one lane swap
 // (v_permlane32_swap; with two queries one swap serves both, each half of
 // the wave then finishing one query), causal mask, max over each 8-key block
 // by three DPP steps.
 // Prefill (thousands of queries, MFMA-bound): 4 waves x 2 queries, 8 key
-// ranges with the range as the block id's low index, so that each XCD keeps
-// "its" range resident in L2 while all query groups stream through it.
+// ranges (more when a range would reach 2^31 bytes) with the range as the
+// block id's low index, so that each XCD keeps "its" range resident in L2
+// while all query groups stream through it.
 // Verification decode (a few queries per sequence, HBM-bound): 8 waves x 1
 // query, 6 tiles in flight, enough key ranges to fill the chip.
 constexpr int TS_TILE = 32;  // keys per tile

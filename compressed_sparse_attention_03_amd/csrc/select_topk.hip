@@ -4,9 +4,10 @@
 // of the candidate blocks).  Ranking key: (score descending, id ascending).
 //
 // Scores become order-preserving uint32 keys (larger score -> larger key;
-// invalid entries -> 0).  One workgroup of 1024 threads owns a row.
+// invalid entries -> 0).  A row is owned by one workgroup, except on the
+// split sampled path below.
 //
-// Sampled path (8192 <= n <= 2^18, k <= 2048: both decode stages).  A
+// Sampled path (8192 <= n <= 2^17, k <= 2048: the decode block stage).  A
 // histogram of 2048 keys spread evenly over the row brackets the k-th key
 // with a wide margin (4 sigma of the sample rank + 16).  ONE coalesced pass
 // over the row then splits it into "certainly in" (key above the bracket,

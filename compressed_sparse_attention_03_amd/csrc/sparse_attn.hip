@@ -12,8 +12,9 @@
 // split over several workgroups and a second kernel merges the partial (max,
 // sum, numerator) triples; many queries (prefill) -> one workgroup per query,
 // no merge.  Rows that do not exist (sel id < 0 or past the cache, a window
-// position before 0, the padding of a partial tile) load row 0 of their
-// source and are zeroed and masked.
+// position before 0, the padding of a partial tile) are masked: the
+// register path loads row 0 of their source and zeroes it, the direct path
+// loads a row of zeros kept in device memory.
 //
 // Per tile of 32 rows:
 //   * every row is gathered from HBM once (1 KiB bf16, or 256 B NVFP4 codes +
