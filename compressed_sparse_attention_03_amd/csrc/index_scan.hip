@@ -500,23 +500,27 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
       }
     }
   };
-  auto store_tile = [&](uint8_t* tile, const u32x4 (&v)[LPT]) {
+  // bi: the LDS tile buffer, a constant at every call site (stage i of the
+  // pipelined loop and tile d of a trip of the other always use buffer i,
+  // resp. d % 2), so no tile address is chosen at run time
+  auto store_tile = [&](int bi, const u32x4 (&v)[LPT]) {
 #pragma unroll
     for (int u = 0; u < LPT; ++u) {
       const int pc = u * NT + tid;
-      if (pc < PIECES) *reinterpret_cast<u32x4*>(tile + (pc / PPR) * TK::LD + 16 * (pc % PPR)) = v[u];
-      else if (MX && pc < PIECES + TS_TILE) kts[tile == kt[0] ? 0 : 1][pc - PIECES] = v[u][0];
+      if (pc < PIECES) *reinterpret_cast<u32x4*>(kt[bi] + (pc / PPR) * TK::LD + 16 * (pc % PPR)) = v[u];
+      else if (MX && pc < PIECES + TS_TILE) kts[bi][pc - PIECES] = v[u][0];
     }
   };
   struct Accs {
     f32x16 v[QW];
   };
   // the MFMAs of all queries of the wave on one tile
-  auto mma = [&](const uint8_t* tile, Accs& A) {
+  auto mma = [&](int bi, Accs& A) {
+    const uint8_t* tile = kt[bi];
     typename TK::QOp kop;
     if constexpr (MX) {
       int ks[2];
-      tile_key_mx(tile, kts[tile == kt[0] ? 0 : 1], kn, half, kop, ks);
+      tile_key_mx(tile, kts[bi], kn, half, kop, ks);
 #pragma unroll
       for (int qi = 0; qi < QW; ++qi) A.v[qi] = tile_mfma_mx(qa[qi], kop, ks);
     } else {
@@ -569,9 +573,9 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
       }
     }
   };
-  auto compute = [&](int t0, const uint8_t* tile) {
+  auto compute = [&](int t0, int bi) {
     Accs A;
-    mma(tile, A);
+    mma(bi, A);
     epi(t0, A);
   };
   // keys past every query's horizon: masked scores and block maxima only
@@ -593,31 +597,29 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
     u32x4 stage[2][LPT];
     if (k0 < kend) load_tile(k0, stage[0]);
     if (k0 + TS_TILE < kend) load_tile(k0 + TS_TILE, stage[1]);
-    int buf = 0;
-    auto step = [&](int tt, u32x4 (&st)[LPT], Accs& A) {
-      store_tile(kt[buf], st);
+    auto step = [&](int tt, int bi, u32x4 (&st)[LPT], Accs& A) {
+      store_tile(bi, st);
       __syncthreads();
       if (tt + 2 * TS_TILE < kend) load_tile(tt + 2 * TS_TILE, st);
-      mma(kt[buf], A);
-      buf ^= 1;
+      mma(bi, A);
     };
     Accs A0, A1;
     int tt = k0;
     if (tt < kend) {
-      step(tt, stage[0], A0);
+      step(tt, 0, stage[0], A0);
       for (;;) {  // block-uniform trip count
         if (tt + TS_TILE >= kend) {
           epi(tt, A0);
           break;
         }
-        step(tt + TS_TILE, stage[1], A1);
+        step(tt + TS_TILE, 1, stage[1], A1);
         epi(tt, A0);
         tt += TS_TILE;
         if (tt + TS_TILE >= kend) {
           epi(tt, A1);
           break;
         }
-        step(tt + TS_TILE, stage[0], A0);
+        step(tt + TS_TILE, 0, stage[0], A0);
         epi(tt, A1);
         tt += TS_TILE;
       }
@@ -629,18 +631,17 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
       if (k0 + d * TS_TILE < kend) load_tile(k0 + d * TS_TILE, stage[d]);
-    int buf = 0;
+    static_assert(DEPTH % 2 == 0, "tile d of a trip uses LDS buffer d % 2");
     int t0 = k0;
     for (; t0 < kend; t0 += DEPTH * TS_TILE) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
         const int tt = t0 + d * TS_TILE;
         if (tt < kend) {  // block-uniform
-          store_tile(kt[buf], stage[d]);
+          store_tile(d % 2, stage[d]);
           __syncthreads();
           if (tt + DEPTH * TS_TILE < kend) load_tile(tt + DEPTH * TS_TILE, stage[d]);
-          compute(tt, kt[buf]);
-          buf ^= 1;
+          compute(tt, d % 2);
         }
       }
     }
