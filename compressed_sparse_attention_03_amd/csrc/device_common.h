@@ -67,22 +67,36 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t n) {
   return __uint_as_float(s | ((e + 126u) << 23) | (m << 22));
 }
 
-// bf16 bits -> E4M3FN code, round to nearest even, saturating to +-448
-// (infinities included); NaN -> 0x7f.  Integer work on the bit fields.
-__device__ __forceinline__ uint32_t bf16_to_e4m3(uint32_t h) {
-  const uint32_t s = (h >> 8) & 0x80u;
-  const uint32_t a = h & 0x7fffu;
-  if (a > 0x7f80u) return 0x7fu;
-  const int e = (int)(a >> 7) - 120;  // E4M3 biased exponent of the value
-  if (e >= 1) {
-    const uint32_t m = a & 0x7fu;     // 7 mantissa bits, keep the top 3
-    uint32_t code = ((uint32_t)(e > 16 ? 16 : e) << 3) | (m >> 4);
-    const uint32_t rem = m & 15u;
-    if (rem > 8u || (rem == 8u && (code & 1u))) ++code;
-    return s | (code > 0x7eu ? 0x7eu : code);
-  }
-  // below 2^-6: multiples of 2^-9 (8 rounds up to 2^-6, code 0x08)
-  return s | (uint32_t)rintf(bf16_to_f32(a) * 512.0f);
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+
+// The two bf16 values of w (low half first) -> two E4M3FN codes (bits 0-7
+// and 8-15): nearest, ties to even, saturating to +-448 (infinities
+// included).  The conversion instruction rounds exactly so for every
+// magnitude up to 464 and makes larger ones NaN, so magnitudes above 448 are
+// clamped to 448 first; NaN stays NaN.  (Checked against the format's
+// definition over all 65,536 bf16 values.)
+__device__ __forceinline__ uint32_t bf16x2_to_e4m3x2(uint32_t w) {
+  float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+  lo = fabsf(lo) > 448.0f ? copysignf(448.0f, lo) : lo;
+  hi = fabsf(hi) > 448.0f ? copysignf(448.0f, hi) : hi;
+  const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((s16x2){0, 0}, lo, hi, 1.0f, false);
+  return (uint32_t)(uint16_t)r[0];
+}
+
+// Eight bf16 values (the four words of x, low half first) -> eight E2M1
+// codes, value 2i in the low nibble of byte i: nearest, ties to even,
+// saturating to +-6, by the conversion instruction, which gives the format's
+// definition for every finite bf16 value (checked over all of them) but
+// keeps the sign of -0 (code 8; its products are zeros either way).
+// (Each word is copied to a scalar before the bit cast: a bit cast of a
+// vector element reads the vector's first element.)
+__device__ __forceinline__ uint32_t bf16x8_to_e2m1x8(const u32x4& x) {
+  const uint32_t x0 = x[0], x1 = x[1], x2 = x[2], x3 = x[3];
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, x0), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, x1), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, x2), 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(w, __builtin_bit_cast(bf16x2, x3), 1.0f, 3);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

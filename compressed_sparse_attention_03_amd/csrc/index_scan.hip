@@ -297,10 +297,8 @@ __device__ __forceinline__ void tile_query(const uint16_t* q, int kn, int half, 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const u32x4 x = p[v];  // 8 bf16 -> 8 E4M3 codes = operand words 2v, 2v+1
-      qa[c][2 * v] = (int)(bf16_to_e4m3(x[0] & 0xffffu) | (bf16_to_e4m3(x[0] >> 16) << 8) |
-                           (bf16_to_e4m3(x[1] & 0xffffu) << 16) | (bf16_to_e4m3(x[1] >> 16) << 24));
-      qa[c][2 * v + 1] = (int)(bf16_to_e4m3(x[2] & 0xffffu) | (bf16_to_e4m3(x[2] >> 16) << 8) |
-                               (bf16_to_e4m3(x[3] & 0xffffu) << 16) | (bf16_to_e4m3(x[3] >> 16) << 24));
+      qa[c][2 * v] = (int)(bf16x2_to_e4m3x2(x[0]) | (bf16x2_to_e4m3x2(x[1]) << 16));
+      qa[c][2 * v + 1] = (int)(bf16x2_to_e4m3x2(x[2]) | (bf16x2_to_e4m3x2(x[3]) << 16));
     }
   }
 }
@@ -325,17 +323,6 @@ __device__ __forceinline__ void tile_key(const uint8_t* tile, int kn, int half, 
   }
 }
 
-// bf16 -> E2M1 code, nearest with ties to the even code, saturating at +-6
-// (midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; ties at 0.75, 1.75 and 3.5
-// round up, the others down), sign from x < 0
-__device__ __forceinline__ uint32_t bf16_to_e2m1(uint32_t h) {
-  const float x = bf16_to_f32(h), a = fabsf(x);
-  const uint32_t mag = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                       (uint32_t)(a > 5.0f);
-  return mag | (x < 0.0f ? 8u : 0u);
-}
-
 // this lane's A operands for MXFP4 keys: dims 32(2c+h) .. +31 as E2M1 codes
 __device__ __forceinline__ void tile_query_mx(const uint16_t* q, int kn, int half, i32x8 (&qa)[2]) {
 #pragma unroll
@@ -343,12 +330,7 @@ __device__ __forceinline__ void tile_query_mx(const uint16_t* q, int kn, int hal
     const u32x4* p = reinterpret_cast<const u32x4*>(q + kn * DI + 32 * (2 * c + half));
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const u32x4 x = p[v];  // 8 bf16 -> 8 codes = one operand word
-      uint32_t wd = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wd |= (bf16_to_e2m1(x[i] & 0xffffu) | (bf16_to_e2m1(x[i] >> 16) << 4)) << (8 * i);
-      qa[c][v] = (int)wd;
+      qa[c][v] = (int)bf16x8_to_e2m1x8(p[v]);  // 8 bf16 -> 8 codes = one operand word
       qa[c][4 + v] = 0;
     }
   }

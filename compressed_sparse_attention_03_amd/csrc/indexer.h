@@ -93,8 +93,7 @@ __device__ __forceinline__ void load_query(const uint16_t* q, const float* w, QF
     for (int i = 0; i < 4; ++i) {
       const uint32_t lo = i < 2 ? x0[2 * i] : x1[2 * i - 4];
       const uint32_t hi = i < 2 ? x0[2 * i + 1] : x1[2 * i - 3];
-      o[i] = bf16_to_e4m3(lo & 0xffffu) | (bf16_to_e4m3(lo >> 16) << 8) |
-             (bf16_to_e4m3(hi & 0xffffu) << 16) | (bf16_to_e4m3(hi >> 16) << 24);
+      o[i] = bf16x2_to_e4m3x2(lo) | (bf16x2_to_e4m3x2(hi) << 16);
     }
     __syncthreads();  // a previous user of the staging row is done
     *reinterpret_cast<u32x4*>(stage + h * DI + d0) = o;
