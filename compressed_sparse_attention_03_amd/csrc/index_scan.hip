@@ -433,7 +433,9 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
 #pragma unroll
     for (int i = 0; i < 16; ++i) wl[qi][i] = a.w[r * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
     nv[qi] = qok[qi] ? (int)n_visible(a.q_pos[r], a.n_cache) : 0;
-    bm_row[qi] = a.block_max ? a.block_max + r * a.bm_stride : nullptr;
+    // this lane's block maximum of a tile starting at key t0 (a multiple of
+    // 32) is entry (t0 + kn) / 8 = t0 / 8 + kn / 8: the lane part is folded in
+    bm_row[qi] = a.block_max ? a.block_max + r * a.bm_stride + (kn >> 3) : nullptr;
   }
   // visible range of the whole block (queries are consecutive)
   int nv_blk;
@@ -520,7 +522,7 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
       if (a.scores && ok_l && p < k1) a.scores[row_l * a.s_stride + pu] = s;
       if (a.block_max) {
         const float m = max_of_8_lanes(s);
-        if (ok_l && (kn & 7) == 0 && p < k1) bm_l[pu >> 3] = m;
+        if (ok_l && (kn & 7) == 0 && p < k1) bm_l[(uint32_t)t0 >> 3] = m;
       }
     };
     if constexpr (QW % 2 == 0) {
@@ -567,7 +569,7 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
     for (int qi = 0; qi < QW; ++qi) {
       if (!qok[qi]) continue;
       if (a.scores && half == 0 && p < k1) a.scores[rows[qi] * a.s_stride + p] = -INFINITY;
-      if (a.block_max && half == 0 && (kn & 7) == 0 && p < k1) bm_row[qi][p >> 3] = -INFINITY;
+      if (a.block_max && half == 0 && (kn & 7) == 0 && p < k1) bm_row[qi][(uint32_t)t0 >> 3] = -INFINITY;
     }
   };
 
