@@ -245,9 +245,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 // Prefill (thousands of queries, MFMA-bound): 4 waves x 2 queries, 8 key
 // ranges (more when a range would reach 2^31 bytes) with the range as the
 // block id's low index, so that each XCD keeps "its" range resident in L2
-// while all query groups stream through it.
-// Verification decode (a few queries per sequence, HBM-bound): 8 waves x 1
-// query, 6 tiles in flight, enough key ranges to fill the chip.
+// while all query groups stream through it.  A few queries per sequence
+// (speculative verification): verify_scan_kernel below.
 constexpr int TS_TILE = 32;  // keys per tile
 
 // MXFP4 index keys: E2M1 codes (dim 2i in the low nibble of byte i) and one
@@ -377,15 +376,16 @@ __device__ __forceinline__ f32x16 tile_mfma(const i32x8 (&qa)[2], const i32x8 (&
   return acc;
 }
 
-// The second launch bound is the minimum number of waves per SIMD.  An
-// 8-wave block runs one per CU.  A smaller block must leave room for at
-// least two waves per SIMD (without it a 4-wave bf16 block took 270
-// registers, one wave per SIMD); FP8 keys take three (168 registers, the
-// tile loop free of spills: 1.66 -> 1.37 ms on an 8192-query prefill against
-// two), MXFP4 keys four (128 registers; a fifth wave spills in the loop).
+// The second launch bound is the minimum number of waves per SIMD.  A
+// 4-wave block must leave room for at least two waves per SIMD (without it
+// a bf16 block took 270 registers, one wave per SIMD); FP8 keys take three
+// (168 registers, the tile loop free of spills: 1.66 -> 1.37 ms on an
+// 8192-query prefill against two), MXFP4 keys four (128 registers; a fifth
+// wave spills in the loop).
 template <int NW, typename KT>
 constexpr int tile_scan_min_waves() {
-  return NW >= 8 ? 1 : std::is_same<KT, KFp8>::value ? 3 : std::is_same<KT, KMx4>::value ? 4 : 2;
+  static_assert(NW == 4, "4-wave blocks");
+  return std::is_same<KT, KFp8>::value ? 3 : std::is_same<KT, KMx4>::value ? 4 : 2;
 }
 
 template <int NW, int QW, int DEPTH, bool PIPE, typename KT>
@@ -635,6 +635,150 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
     masked(tt);
 }
 
+// ---- speculative verification: (query, tile) units dealt over the waves ----
+// A few queries per sequence (2-63 draft tokens), bf16 keys.  A block = 4
+// waves over one key range and a group of up to 8 consecutive queries of one
+// sequence.  Keys come in groups of VG_TILES = 4 tiles (128 keys, 32 KiB),
+// fetched VERIFY_DEPTH groups ahead into registers (non-temporal raw buffer
+// loads over the block's range, rows past it reading as zeros) and stored to
+// one of two LDS group buffers: one barrier per group.  The 4n (query, tile) units of a group of
+// n queries are dealt out evenly: wave w takes units wn .. wn + n - 1 in
+// query-major order (unit u = query u / 4, tile u % 4), so every SIMD does n
+// MFMA tiles and epilogues per group whatever n is (one wave per query slot,
+// 8 slots, computes 3 empty slots for 5 queries).  Wave w meets queries
+// floor(wn / 4) .. floor((wn + n - 1) / 4), at most two when n != 7: their
+// operands and weights stay in registers.  Seven queries run as eight with
+// the last slot empty.  MFMA and epilogue per unit as in tile_scan_kernel.
+constexpr int VG_TILES = 4;
+constexpr int VG_KEYS = VG_TILES * TS_TILE;  // keys per group
+// Measured on the 1M verification workload (8 sequences x 5 queries, 1 GiB
+// of keys): 2 groups in flight and ~512 blocks (two per CU, one round),
+// 207-211 us; with cached instead of non-temporal loads 228-230 us (1 group
+// in flight 232, 3 groups 229-234, 1024 / 2048 blocks 229-232 / 238); the
+// 8-query-slot tile scan 275-285 us.  Not kept: the next unit's MFMAs issued
+// before this unit's epilogue (242-245 us), two MFMA accumulation chains per
+// unit (232-234), one LDS group buffer with three blocks per CU (232).
+constexpr int VERIFY_DEPTH = 2;               // groups in flight per block
+
+struct VerifyQuery {
+  bf16x8 op[8];  // A operands: 32 heads x 128 dims
+  float w[16];   // weights of this lane's 16 heads
+  int nv;        // visible keys
+  bool ok;       // a real query (not an empty slot)
+  int64_t row;   // its row of the score and block-max outputs
+};
+
+__global__ __launch_bounds__(256, 2) void verify_scan_kernel(ScanArgs a, int64_t keys_per_chunk) {
+  using TK = TileKeys<KBf16>;
+  constexpr int NT = 256;
+  constexpr int PPR = TK::ROWB / 16;                     // 16-byte pieces per key row
+  constexpr int LPT = VG_KEYS * TK::ROWB / 16 / NT;      // pieces per thread and group
+  static_assert(LPT * NT * 16 == VG_KEYS * TK::ROWB, "a group is whole pieces per thread");
+  __shared__ __align__(16) uint8_t kt[2][VG_KEYS * TK::LD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, kn = lane & 31;
+  const int b = blockIdx.z;
+  const int jg = blockIdx.y * 8;               // the group's first query
+  const int nq = min(8, a.Tq - jg);            // its queries
+  const int n = nq == 7 ? 8 : nq;              // its query slots
+  const int u0 = wave * n;                     // this wave's first unit
+  const int qa = u0 >> 2, qb = (u0 + n - 1) >> 2;
+  const int na = min(n, 4 * (qa + 1) - u0);    // units of query slot qa
+  const int k0 = (int)(blockIdx.x * keys_per_chunk);
+  const int k1 = (int)min(a.n_cache, (int64_t)k0 + keys_per_chunk);
+  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + b * a.k_sb * TK::ESZ;
+
+  auto setup = [&](int slot, VerifyQuery& Q) {
+    Q.ok = slot < nq;
+    const int64_t r = (int64_t)b * a.Tq + (Q.ok ? jg + slot : a.Tq - 1);
+    Q.row = r;
+    tile_query(a.q + r * (HI * DI), kn, half, Q.op);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Q.w[i] = a.w[r * HI + 8 * (i >> 2) + 4 * half + (i & 3)];
+    Q.nv = Q.ok ? (int)n_visible(a.q_pos[r], a.n_cache) : 0;
+  };
+  VerifyQuery QA, QB;
+  setup(qa, QA);
+  setup(qb, QB);
+  // keys that need computing: the group's queries are consecutive, so the
+  // widest horizon is the first's or the last's
+  const int nv_blk = (int)max(n_visible(a.q_pos[(int64_t)b * a.Tq + jg], a.n_cache),
+                              n_visible(a.q_pos[(int64_t)b * a.Tq + jg + nq - 1], a.n_cache));
+  const int kend = min(k1, max(k0, nv_blk));
+
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kb + (int64_t)k0 * TK::ROWB), (short)0, (k1 - k0) * TK::ROWB, BUF_DWORD3);
+  // piece u * NT + tid of a group is bytes 16 (u NT + tid) of its 128 rows
+  auto load_group = [&](int g0, u32x4 (&v)[LPT]) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, 16u * (uint32_t)tid,
+                                                   (uint32_t)(g0 - k0) * TK::ROWB + 16u * NT * u,
+                                                   2 /* nt: the keys are read once */);
+  };
+  auto store_group = [&](int bi, const u32x4 (&v)[LPT]) {
+#pragma unroll
+    for (int u = 0; u < LPT; ++u) {
+      const int pc = u * NT + tid;
+      *reinterpret_cast<u32x4*>(kt[bi] + (pc / PPR) * TK::LD + 16 * (pc % PPR)) = v[u];
+    }
+  };
+  // one unit: tile t of the group at g0 for query Q
+  auto unit = [&](int bi, int g0, int t, const VerifyQuery& Q) {
+    bf16x8 kop[8];
+    tile_key(kt[bi] + t * TS_TILE * TK::LD, kn, half, kop);
+    const f32x16 acc = tile_mfma(Q.op, kop);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum = fmaf(Q.w[i], relu(acc[i]), sum);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+    sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // both halves' heads
+    const int t0 = g0 + TS_TILE * t;
+    const int p = t0 + kn;
+    const float s = p < Q.nv ? sum : -INFINITY;
+    const bool st = Q.ok && half == 0 && p < k1;
+    if (a.scores && st) a.scores[Q.row * a.s_stride + (uint32_t)p] = s;
+    if (a.block_max) {
+      const float m = max_of_8_lanes(s);
+      if (st && (kn & 7) == 0) a.block_max[Q.row * a.bm_stride + ((uint32_t)p >> 3)] = m;
+    }
+  };
+  auto group = [&](int bi, int g0) {
+    for (int i = 0; i < na; ++i) unit(bi, g0, (u0 + i) & 3, QA);  // wave-uniform trip counts
+    for (int i = na; i < n; ++i) unit(bi, g0, (u0 + i) & 3, QB);
+  };
+
+  // VERIFY_DEPTH groups in flight, staged in registers; the loop body is
+  // unrolled so that every staging set and LDS buffer index is a constant
+  constexpr int SD = VERIFY_DEPTH, UNR = SD % 2 ? 2 * SD : SD;
+  u32x4 stage[SD][LPT];
+#pragma unroll
+  for (int d = 0; d < SD; ++d)
+    if (k0 + d * VG_KEYS < kend) load_group(k0 + d * VG_KEYS, stage[d]);
+  for (int g0 = k0; g0 < kend; g0 += UNR * VG_KEYS) {  // block-uniform
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int g = g0 + k * VG_KEYS;
+      if (g >= kend) break;
+      store_group(k % 2, stage[k % SD]);
+      __syncthreads();
+      if (g + SD * VG_KEYS < kend) load_group(g + SD * VG_KEYS, stage[k % SD]);
+      group(k % 2, g);
+    }
+  }
+  // the keys of the range that no query of the group sees
+  const int mstart = kend > k0 ? k0 + (kend - k0 + VG_KEYS - 1) / VG_KEYS * VG_KEYS : k0;
+  for (int slot = wave; slot < nq; slot += 4) {  // wave-uniform
+    const int64_t r = (int64_t)b * a.Tq + jg + slot;
+    if (a.scores)
+      for (int p = mstart + lane; p < k1; p += 64) a.scores[r * a.s_stride + p] = -INFINITY;
+    if (a.block_max)
+      for (int blk = (mstart >> 3) + lane; blk < (k1 + 7) >> 3; blk += 64)
+        a.block_max[r * a.bm_stride + blk] = -INFINITY;
+  }
+}
+
 // Longest key range of one tile-scan block: its bytes stay below 2^31, the
 // reach of the block's buffer resource (bf16 keys: 2^23 - 32 keys).
 int64_t tile_scan_max_keys(int k_fmt) {
@@ -662,6 +806,8 @@ hipError_t launch_scan_t(const ScanArgs& a, int B, dim3 grid, hipStream_t s) {
 }
 
 }  // namespace
+
+constexpr int VERIFY_BLOCKS = 512;  // target blocks of a verification scan (two per CU)
 
 hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const void* k,
                              int k_fmt, const uint8_t* k_scale, int64_t k_sb, int64_t n_cache,
@@ -692,16 +838,18 @@ hipError_t launch_index_scan(int B, int Tq, const void* q, const float* w, const
   if (k_fmt == KEYS_MXFP4) return hipErrorInvalidValue;  // rejected before launch
   if (!k_fp8 && Tq >= 2) {
     // a few queries per sequence (speculative verification): HBM-bound, the
-    // keys are read once per 8 queries; ranges of whole tiles, ~1024 blocks
+    // keys are read once per 8 queries; ranges of whole 128-key groups,
+    // ~VERIFY_BLOCKS blocks
     const int64_t groups = (Tq + 7) / 8;
-    const int64_t n_tiles32 = (n_cache + TS_TILE - 1) / TS_TILE;
-    int64_t ch = (1024 + B * groups - 1) / (B * groups);
-    if (ch > n_tiles32) ch = n_tiles32;
+    const int64_t n_groups = (n_cache + VG_KEYS - 1) / VG_KEYS;
+    int64_t ch = (VERIFY_BLOCKS + B * groups - 1) / (B * groups);
+    if (ch > n_groups) ch = n_groups;
     if (ch < 1) ch = 1;
-    const int64_t kpc = min((n_tiles32 + ch - 1) / ch * TS_TILE, tile_scan_max_keys(k_fmt));
+    const int64_t kmax = (INT32_MAX / (DI * 2)) / VG_KEYS * VG_KEYS;  // range bytes < 2^31
+    const int64_t kpc = min((n_groups + ch - 1) / ch * VG_KEYS, kmax);
     const unsigned nchunks = (unsigned)((n_cache + kpc - 1) / kpc);
     dim3 grid(nchunks, (unsigned)groups, (unsigned)B);
-    hipLaunchKernelGGL((tile_scan_kernel<8, 1, 6, false, KBf16>), grid, dim3(512), 0, s, a, kpc);
+    hipLaunchKernelGGL(verify_scan_kernel, grid, dim3(256), 0, s, a, kpc);
     return hipGetLastError();
   }
 

@@ -69,6 +69,11 @@ def test_compress_stage_tiny():
     ("1m_verify", dict(B=3, N=20000, t_last=39999, K_b=256, win_pos0=39999 - 131, seed=64)),
     ("1m_verify", dict(B=2, Tq=9, N=9000, t_last=18003, K_b=128, win_pos0=18003 - 135, seed=65)),
     ("1m_verify", dict(B=2, Tq=2, N=4103, t_last=8205, K_b=64, win_pos0=8205 - 128, seed=66)),
+    # verification scan query groups: 7 queries (run as 8, one slot empty),
+    # 8 + 5, and 3 queries whose horizons end before the cache does
+    ("1m_verify", dict(B=2, Tq=7, N=5003, t_last=10005, K_b=64, win_pos0=10005 - 133, seed=67)),
+    ("1m_verify", dict(B=1, Tq=13, N=3001, t_last=6001, K_b=64, win_pos0=6001 - 139, seed=68)),
+    ("1m_verify", dict(B=3, Tq=3, N=1000, t_last=1900, K_b=64, win_pos0=1900 - 129, seed=69)),
     ("prefill", dict(B=2, Tq=64, N=4096, t_last=8191, K_b=32, K=64, comp_T=0,
                      shared_indexer=False, seed=41)),
     # FP8 keys, many queries: the FP8 tile scan (v_mfma 32x32x64 on E4M3)
