@@ -1053,6 +1053,7 @@ __device__ __forceinline__ void load_row_keys(const SelArgs& a, int64_t row, int
   const int32_t* irow = IDS ? a.ids + row * a.id_stride : nullptr;
   // with ids, 16 entries at a time so that ids and scores are not all live
   constexpr int G = (IDS && E > 16) ? 16 : E;
+  static_assert(E % G == 0, "whole batches");
   int32_t lv = -1, ff = 0x7fffffff;
   uint32_t nv = 0;
 #pragma unroll
@@ -1096,6 +1097,7 @@ __device__ __forceinline__ void load_row_keys_gather(const SelArgs& a, const Gat
   const int32_t* brow = gs.blocks + row * gs.K_b;
   const float* srow = gs.all + row * gs.a_stride;
   constexpr int G = E > 16 ? 16 : E;
+  static_assert(E % G == 0, "whole batches");
   int32_t lv = -1;
   uint32_t nv = 0;
 #pragma unroll
@@ -1389,6 +1391,7 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
     const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
         IDS ? (void*)const_cast<int32_t*>(irow) : (void*)const_cast<float*>(srow), (short)0, n * 4,
         SEL_BUF_DWORD3);
+    // entries in batches of G (the last batch may be partial: E % G != 0)
     constexpr int G = (IDS && E > 16) ? 16 : E;
 #pragma unroll
     for (int g = 0; g < E; g += G) {
@@ -1396,6 +1399,7 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
       int32_t id[G];
 #pragma unroll
       for (int u = 0; u < G; ++u) {
+        if (g + u >= E) break;  // compile-time after unrolling
         const int c = (g + u) * MT + tid;
         const uint32_t off = (uint32_t)c << 2;  // past the row: reads as 0, masked here
         const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
@@ -1409,6 +1413,7 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
       }
 #pragma unroll
       for (int u = 0; u < G; ++u) {
+        if (g + u >= E) break;
         const int c = (g + u) * MT + tid;
         const bool ok = id[u] >= 0 && !(sc[u] != sc[u]) && sc[u] != -INFINITY;
         key[g + u] = ok ? order_key(sc[u]) : 0u;
@@ -1558,11 +1563,16 @@ void launch_many_cfg(int R, const SelArgs& a, const GatherSrc& gs, hipStream_t s
 
 // (threads, entries per thread) by row length on the many-rows path.  Measured
 // on the 8192-row prefill stages: 512 threads beat 256 (fewer entries per
-// thread, 4 workgroups per CU at n = 4608, 2 at n = 16,384) and 1024.
+// thread, 4 workgroups per CU at n = 4608, 2 at n = 16,384) and 1024.  The
+// kernel is vector-instruction bound there and its per-entry work runs for
+// every slot, so a row fills its slots exactly where it can: the 4608-entry
+// block stage takes 512 x 9 (128.6-129.1 -> 114-117 us against 512 x 12;
+// 256 x 18: 125-126 us).
 template <bool GATHER, bool IDS>
 void launch_many(int R, int64_t n, const SelArgs& a, const GatherSrc& gs, hipStream_t s) {
   if (n <= 2048) launch_many_cfg<256, 8, GATHER, IDS>(R, a, gs, s);
   else if (n <= 4096) launch_many_cfg<256, 16, GATHER, IDS>(R, a, gs, s);
+  else if (n <= 4608) launch_many_cfg<512, 9, GATHER, IDS>(R, a, gs, s);
   else if (n <= 6144) launch_many_cfg<512, 12, GATHER, IDS>(R, a, gs, s);
   else if (n <= 8192) launch_many_cfg<512, 16, GATHER, IDS>(R, a, gs, s);
   else if (n <= 12288) launch_many_cfg<512, 24, GATHER, IDS>(R, a, gs, s);

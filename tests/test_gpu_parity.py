@@ -281,14 +281,15 @@ def test_select_edge_cases(seed, R, n, k, mode):
 
 
 @pytest.mark.parametrize("seed,n,k,mode", [
-    # 1024+ rows take the 256-thread many-rows kernel (8 to 64 entries per
-    # thread): integer ties, signed scores, continuous scores, all keys equal,
+    # 1024+ rows take the many-rows kernel (256 or 512 threads, 8 to 32
+    # entries per thread): integer ties, signed scores, continuous scores, all keys equal,
     # forced ids (k = 1 keeps only the forced one), the last valid entry kept,
     # fewer valid entries than k, ids
     (80, 4608, 2048, "last"), (81, 16384, 512, "ties"), (82, 16384, 512, "ids"),
     (83, 2000, 64, "signed"), (84, 3000, 1, "forced"), (85, 6000, 700, "cont_forced"),
     (86, 12000, 2048, "allequal"), (87, 700, 900, "plain"), (88, 1, 1, "plain"),
     (89, 257, 256, "last"), (90, 8192, 2048, "cont"), (91, 5000, 4999, "signed"),
+    (92, 4500, 1000, "ids"), (93, 10000, 900, "ids"),
 ])
 def test_select_many_rows(seed, n, k, mode):
     """Thousands of rows (the chunked prefill's shape) against the oracle's
