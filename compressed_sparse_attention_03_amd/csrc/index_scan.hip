@@ -437,14 +437,14 @@ __global__ __launch_bounds__(NW * 64, (tile_scan_min_waves<NW, KT>())) void tile
     // 32) is entry (t0 + kn) / 8 = t0 / 8 + kn / 8: the lane part is folded in
     bm_row[qi] = a.block_max ? a.block_max + r * a.bm_stride + (kn >> 3) : nullptr;
   }
-  // visible range of the whole block (queries are consecutive)
-  int nv_blk;
-  {
-    const int jl = min(a.Tq - 1, (int)blockIdx.y * NQ + NQ - 1);
-    const int jf = min(a.Tq - 1, (int)blockIdx.y * NQ);
-    nv_blk = (int)max(n_visible(a.q_pos[(int64_t)b * a.Tq + jl], a.n_cache),
-                      n_visible(a.q_pos[(int64_t)b * a.Tq + jf], a.n_cache));
-  }
+  // visible range of the whole block: the widest of its queries' (any
+  // order of positions)
+  int64_t qp[NQ];  // NQ unconditional loads first, then their maximum
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) qp[i] = a.q_pos[(int64_t)b * a.Tq + min((int)blockIdx.y * NQ + i, a.Tq - 1)];
+  int nv_blk = 0;
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) nv_blk = max(nv_blk, (int)n_visible(qp[i], a.n_cache));
   // staging: piece u*NT + tid of a tile -> row / PPR, 16-byte piece % PPR
   const int kend = min(k1, max(k0, nv_blk));  // keys that need computing
   // bf16 and MXFP4 keys: the block's key range [k0, k1) (and the MXFP4
@@ -701,10 +701,14 @@ __global__ __launch_bounds__(256, 2) void verify_scan_kernel(ScanArgs a, int64_t
   VerifyQuery QA, QB;
   setup(qa, QA);
   setup(qb, QB);
-  // keys that need computing: the group's queries are consecutive, so the
-  // widest horizon is the first's or the last's
-  const int nv_blk = (int)max(n_visible(a.q_pos[(int64_t)b * a.Tq + jg], a.n_cache),
-                              n_visible(a.q_pos[(int64_t)b * a.Tq + jg + nq - 1], a.n_cache));
+  // keys that need computing: up to the widest horizon of the group's
+  // queries (any order of positions)
+  int64_t qp[8];  // 8 unconditional loads first, then their maximum
+#pragma unroll
+  for (int s = 0; s < 8; ++s) qp[s] = a.q_pos[(int64_t)b * a.Tq + jg + min(s, nq - 1)];
+  int nv_blk = 0;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) nv_blk = max(nv_blk, (int)n_visible(qp[s], a.n_cache));
   const int kend = min(k1, max(k0, nv_blk));
 
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(

@@ -141,6 +141,48 @@ def test_scan_cand_select_stages(name, kw):
     say(f"  blocks, candidates and Sel bit-exact ({(sel_ref >= 0).sum(1).tolist()[:4]} selected)")
 
 
+@pytest.mark.parametrize("name,B,Tq,N,pos,seed", [
+    ("1m", 2, 1, 1, "any", 140),             # decode scan: a single latent
+    ("1m", 3, 1, 37, "any", 141),
+    ("1m_verify", 2, 2, 1, "any", 142),      # verification scan
+    ("1m_verify", 2, 3, 5, "any", 143),
+    ("1m_verify", 1, 7, 129, "any", 144),
+    ("1m_verify", 2, 63, 200, "any", 145),
+    ("1m_verify", 1, 5, 300, "none", 146),
+    ("prefill", 1, 64, 33, "any", 147),      # many-query tile scan
+    ("prefill", 1, 70, 700, "any", 148),
+    ("1m_lowp", 2, 1, 3, "any", 149),        # FP8 decode scan
+    ("1m_lowp", 2, 3, 70, "any", 150),
+    ("prefill_fp8", 1, 64, 45, "any", 151),
+    ("prefill_mxfp4", 1, 64, 45, "any", 152),
+])
+def test_index_scan_edge_cases(name, B, Tq, N, pos, seed):
+    """Tiny caches (one latent, a partial block, one 128-key group and one
+    more) and query positions in any order -- some before the cache starts
+    (nothing visible), some past its end -- through every scan kernel; every
+    score and block maximum bit-exact against the oracle."""
+    cfg = gen.shrink(gen.CONFIGS[name], B=B, Tq=Tq, N=N, t_last=2 * N + Tq, comp_T=0,
+                     comp_step=False, seed=seed)
+    inp = _inputs(cfg)
+    rng = np.random.default_rng(seed)
+    qp = rng.integers(-40, 0, (B, Tq)) if pos == "none" else rng.integers(-3, 2 * N + 6, (B, Tq))
+    inp["q_pos"] = torch.from_numpy(qp.astype(np.int64)).cuda()
+    host = np_subset(inp)
+    R, nblk = B * Tq, (N + 7) // 8
+    mx = cfg.key_fmt == "mxfp4"
+    ks_h = (host["ks"], host["ks_scale"]) if mx else host["ks"]
+    scores = torch.empty((R, (N + 3) // 4 * 4), dtype=torch.float32, device="cuda")[:, :N]
+    bm = torch.empty((R, nblk), dtype=torch.float32, device="cuda")
+    say(f"[run] {name} scan: B={B} Tq={Tq} N={N} positions {qp.reshape(-1)[:8].tolist()}")
+    api.index_scan(inp["qs"], inp["ws"], inp["ks"], inp["q_pos"], scores=scores, block_max=bm,
+                   k_scale=inp["ks_scale"])
+    torch.cuda.synchronize()
+    sc_ref, bm_ref = ref.scan(host["qs"], host["ws"], ks_h, host["q_pos"], want_scores=True)
+    assert np.array_equal(scores.cpu().numpy().astype(np.float64), sc_ref), "scan scores"
+    assert np.array_equal(bm.cpu().numpy().astype(np.float64), bm_ref), "block max"
+    say(f"  {R} rows x {N} scores and {nblk} block maxima bit-exact")
+
+
 def test_gather_edge_cases():
     """Candidate gather from stored scores, and the candidate indexer, on the
     cases the selection rarely produces: block ids of -1, ids past the cache
