@@ -1356,32 +1356,45 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
     const int32_t* brow = gs.blocks + row * gs.K_b;
     const float* srow = gs.all + row * gs.a_stride;
     const int nb = (n + BLK - 1) / BLK;  // <= K_b
-    for (int i = tid; i < nb; i += MT) sm.blk[i] = brow[i];
+    // padded with -1 to the slot count, so that every slot reads its block
+    // id unconditionally (the reads then go out together)
+    for (int i = tid; i < E * MT / BLK; i += MT) sm.blk[i] = i < nb ? brow[i] : -1;
     __syncthreads();
     // the row's visible scores as one buffer resource: 32-bit lane offsets
     // (one register per load instead of a 64-bit address), clipped to n_vis
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(srow), (short)0, (int)(nvis * 4), SEL_BUF_DWORD3);
-    uint64_t okm = 0ull;  // entry e visible: bit e (one register pair, not E flags)
+    static_assert(E <= 32, "one 32-bit mask of the thread's entries");
+    uint32_t okm = 0u;  // entry e visible: bit e (one register, not E flags)
+    // any caller block id is safe: an id above nvis / 8 (negative ones
+    // included, as unsigned) fails the first test, and below it the
+    // position fits 32 bits
+    const uint32_t nvb = (uint32_t)nvis >> 3;
+    static_assert(MT % BLK == 0, "slot c = e * MT + tid: block e * MT / BLK + tid / BLK");
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int c = e * MT + tid;
-      const int32_t blk = c < n ? sm.blk[c >> 3] : -1;
-      const bool ok = blk >= 0 && (int64_t)blk * BLK + (c & 7) < nvis;  // any caller block id is safe
-      const uint32_t off = ok ? ((uint32_t)blk * (uint32_t)BLK + (uint32_t)(c & 7)) << 2 : 0u;
-      key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-      okm |= (uint64_t)ok << e;
+      // slot c = e * MT + tid (c >= n reads a padding -1): one LDS address
+      // per thread, the entry in the immediate offset
+      const uint32_t blk = (uint32_t)sm.blk[e * (MT / BLK) + (tid >> 3)];
+      const uint32_t pos = blk * (uint32_t)BLK + (uint32_t)(tid & 7);
+      const bool ok = blk <= nvb && pos < (uint32_t)nvis;
+      key[e] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? pos << 2 : 0u, 0, 0);
+      okm |= (uint32_t)ok << e;
     }
     // branch-free (a branch per entry made the compiler copy the whole key
-    // array around each one)
+    // array around each one): a select per entry for the key (the order key
+    // as sign-dependent bit flips), the valid entries as one mask whose top
+    // bit and popcount give the last valid column and the count
+    uint32_t vm = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const uint32_t u = key[e];
-      const bool ok = ((okm >> e) & 1ull) && u != 0xff800000u && (u & 0x7fffffffu) <= 0x7f800000u;
-      key[e] = ok ? order_key(__uint_as_float(u)) : 0u;
-      lv = ok ? e * MT + tid : lv;
-      nv += ok ? 1u : 0u;
+      const bool ok = ((okm >> e) & 1u) && u != 0xff800000u && (u & 0x7fffffffu) <= 0x7f800000u;
+      key[e] = ok ? u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u) : 0u;
+      vm |= (uint32_t)ok << e;
     }
+    lv = vm ? (31 - __clz((int)vm)) * MT + tid : -1;  // columns grow with e
+    nv = (uint32_t)__popc(vm);
   } else {
     const float* srow = a.scores + row * a.s_stride;
     const int32_t* irow = IDS ? a.ids + row * a.id_stride : nullptr;
@@ -1442,9 +1455,12 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
   int32_t fcol = -1;
   if (a.force_last) fcol = lv;
   else if (fid >= 0 && ff != 0x7fffffff) fcol = ff;
-  // the forced entry leaves the ranking and comes back as an "above" bit
+  // the forced entry leaves the ranking and comes back as an "above" bit;
+  // it is entry f_e (the same for the whole block) of lane f_lane
+  const int f_e = fcol >= 0 ? fcol / MT : -1;
+  const bool f_lane = fcol >= 0 && fcol % MT == tid;
 #pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (e * MT + tid == fcol) ? 0u : key[e];
+  for (int e = 0; e < E; ++e) key[e] = (e == f_e && f_lane) ? 0u : key[e];
   const uint32_t k_rem = (uint32_t)a.k - (fcol >= 0 ? 1u : 0u);
   const uint32_t n_rest = nv - (fcol >= 0 ? 1u : 0u);
 
@@ -1508,7 +1524,7 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
   // ---- 3: column bitmaps, ordered output -------------------------------------
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool up = key[e] > T || e * MT + tid == fcol;
+    const bool up = key[e] > T || (e == f_e && f_lane);
     const bool tie = need > 0u && key[e] == T;
     const uint64_t mu = __ballot(up), mt = __ballot(tie);
     if (lane == 0) {
