@@ -1406,6 +1406,8 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
         SEL_BUF_DWORD3);
     // entries in batches of G (the last batch may be partial: E % G != 0)
     constexpr int G = (IDS && E > 16) ? 16 : E;
+    static_assert(E <= 32, "one 32-bit mask of the thread's entries");
+    uint32_t vm = 0u;  // entry e valid: bit e
 #pragma unroll
     for (int g = 0; g < E; g += G) {
       float sc[G];
@@ -1429,12 +1431,22 @@ __global__ __launch_bounds__(MT, (many_min_waves<MT, E, GATHER>())) void select_
         if (g + u >= E) break;
         const int c = (g + u) * MT + tid;
         const bool ok = id[u] >= 0 && !(sc[u] != sc[u]) && sc[u] != -INFINITY;
-        key[g + u] = ok ? order_key(sc[u]) : 0u;
-        lv = ok ? c : lv;  // c grows with g + u
-        nv += ok ? 1u : 0u;
-        ff = (ok && fid >= 0 && id[u] == fid && c < ff) ? c : ff;
+        const uint32_t su = __float_as_uint(sc[u]);
+        key[g + u] = ok ? su ^ ((uint32_t)((int32_t)su >> 31) | 0x80000000u) : 0u;  // order_key
+        vm |= (uint32_t)ok << (g + u);
+        // the forced id's first column, under a block-uniform branch (with
+        // ids while the batch's ids are live)
+        if (IDS && fid >= 0) ff = (ok && id[u] == fid && c < ff) ? c : ff;
       }
     }
+    // without ids the forced id is its own column
+    if (!IDS && fid >= 0) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e * MT + tid == fid && ((vm >> e) & 1u)) ff = fid;
+    }
+    lv = vm ? (31 - __clz((int)vm)) * MT + tid : -1;  // columns grow with the entry
+    nv = (uint32_t)__popc(vm);
   }
   lv = wave_max_i(lv);
   ff = wave_min_i(ff);
