@@ -287,6 +287,8 @@ def test_gather_select_fused(seed, R, N, K_b, k, cont):
     # longer rows: few rows take the split path, else one workgroup per row from memory
     (60, 2, 100000, 2048, "allequal"), (61, 3, 131072, 2048, "forced"),
     (62, 2, 140000, 300, "last"), (63, 2, 100000, 1500, "ids"),
+    # the split path's 2048-entry blocks (more than 16 rows; fewer take 1024)
+    (68, 20, 70000, 2048, "last"), (69, 17, 65536, 1000, "ids"),
     # continuous scores (few ties): rows of 8K-16K entries take the compacted
     # candidate list; k from 64 to 2048, with and without a forced id
     (64, 9, 16384, 512, "cont"), (65, 4, 12000, 1500, "cont"), (66, 5, 16384, 64, "cont_forced"),
