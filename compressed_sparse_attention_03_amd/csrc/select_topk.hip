@@ -1617,12 +1617,13 @@ void launch_many(int R, int64_t n, const SelArgs& a, const GatherSrc& gs, hipStr
 // Rows enough to give every CU several workgroups of the many-rows kernel.
 constexpr int MANY_ROWS = 1024;
 bool many_path(int64_t R, int64_t n) { return R >= MANY_ROWS && n <= 16384; }
-// Few rows of 8K-16K entries (the decode's position stage, 16,384
-// candidates per query): the same kernel with 1024 threads per row, one row
-// per CU, beats the register-row kernel's sampled bracket (8 rows: 19.0 ->
-// 16.4 us); at 65,536 entries (the block stage) it loses to the split
-// classify / finish pair (39.5 vs 24.8 us).
-bool wide_path(int64_t R, int64_t n) { return R < MANY_ROWS && n > 8192 && n <= 16384; }
+// Few rows of 4K-16K entries (the decode's position stage, 16,384
+// candidates per query; the 128K decode's block stage, 8192 blocks): the
+// same kernel with 1024 threads per row, one row per CU, beats the
+// register-row kernel's sampled bracket (8 rows of 16,384: 19.0 -> 16.4 us;
+// 32 rows of 8192: 13.4 -> 9.4 us); at 65,536 entries (the 1M block stage)
+// it loses to the split classify / finish pair (39.5 vs 24.8 us).
+bool wide_path(int64_t R, int64_t n) { return R < MANY_ROWS && n > 4096 && n <= 16384; }
 
 // Path choice.  One CU works through a register-held row at a few entries
 // per lane-cycle, so a row of more than 16K entries is faster spread over
@@ -1669,8 +1670,13 @@ hipError_t launch_select_topk(int R, int64_t n, const float* scores, int64_t s_s
   SelArgs a{scores, s_stride, ids, id_stride, forced, force_last, n, k, out, o_stride};
   if (wide_path(R, n)) {
     const GatherSrc none{};
-    if (ids) launch_many_cfg<1024, 16, false, true>(R, a, none, s);
-    else launch_many_cfg<1024, 16, false, false>(R, a, none, s);
+    if (n <= 8192) {
+      if (ids) launch_many_cfg<1024, 8, false, true>(R, a, none, s);
+      else launch_many_cfg<1024, 8, false, false>(R, a, none, s);
+    } else {
+      if (ids) launch_many_cfg<1024, 16, false, true>(R, a, none, s);
+      else launch_many_cfg<1024, 16, false, false>(R, a, none, s);
+    }
     return hipGetLastError();
   }
   if (many_path(R, n)) {
